@@ -1,0 +1,211 @@
+"""Benchmark of the MoE expert layer, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config small] [--mode router]
+                    [--no-cpu-baseline]
+
+One step = the whole hot path over one batch of synthetic input, through the C
+ABI: router logits, routing (softmax / top-k, histogram, offsets, positions),
+rowwise dispatch, grouped SwiGLU GEMMs, combine, and the full backward
+(combine backward, dgrad / wgrad grouped GEMMs, unpermute-sum, router
+backward).  Inputs are generated once and stay resident in HBM; identical
+values are used for every step.
+
+Prints ONE JSON line.  The default workload is the 8-expert top-4 layer
+(T=8192 tokens, d_model 2048, SwiGLU hidden 1024, bf16).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd tokens/s and grouped-GEMM TFLOP/s (% of MFMA peak), 1 GPU"
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+GEMM_KERNELS = {
+    # name: flops per launch as a multiple of R*d*h
+    "ggemm_up_swiglu": 4, "ggemm_down": 2, "ggemm_dgrad_down_swiglu": 2, "ggemm_wgrad_down": 2,
+    "ggemm_dgrad_up": 4, "ggemm_wgrad_up": 4,
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def cpu_baseline(cfg, mode, sample_T, min_seconds=10.0):
+    """The oracle as it stands, timed on the host on the first sample_T tokens
+    of the same workload (all experts, full d and h)."""
+    import numpy as np
+
+    from oracle import moe_ref as ref
+    from token_routing_grouped_amd import inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    inp = inputs.layer_inputs(cfg, T=sample_T)
+    forced = None
+    if mode != "router":
+        forced = inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)[:sample_T]
+    args = (inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"])
+    times = []
+    while True:  # repeat the same sample until ~10 s of CPU work (at most 20 runs)
+        t0 = time.perf_counter()
+        f = ref.layer_forward(*args, cfg.k, forced_idx=forced)
+        ref.layer_backward(f, inp["dy"], *args)
+        times.append(time.perf_counter() - t0)
+        if sum(times) >= min_seconds or len(times) >= 20:
+            break
+    el = float(np.median(times))
+    return {"value": sample_T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {sample_T} of {cfg.T} tokens, all {cfg.E} experts, full d={cfg.d} h={cfg.h}; "
+                      f"float64 numpy fwd+bwd, median of {len(times)} runs ({sum(times):.1f} s total) "
+                      f"on {cpu_model()}",
+            "seconds_per_run": el}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="small")
+    ap.add_argument("--mode", default=None, help="router | uniform | zipf (default: the config's first mode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported by this build "
+              f"(the layer is measured on one GPU's share).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from token_routing_grouped_amd import _abi, configs, inputs
+    from token_routing_grouped_amd.layer import MoELayerGPU
+
+    cfg = configs.get(a.config)
+    mode = a.mode or cfg.modes[0]
+    if cfg.mx:
+        raise SystemExit("the MXFP8 path is not built yet")
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    log(f"bench: {cfg.slug} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} h={cfg.h} {cfg.dtype} mode={mode}")
+    inp = inputs.layer_inputs(cfg)
+    t = {n: torch.from_numpy(v).to(dev).to(dt) for n, v in inp.items()}
+    forced = None
+    if mode != "router":
+        forced = torch.from_numpy(inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)).to(dev)
+    del inp
+    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, dev)
+    args = (t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])
+
+    for _ in range(a.warmup):
+        layer.step(*args, forced_idx=forced)
+    torch.cuda.synchronize()
+    log("bench: warmup done")
+
+    # timed region: exactly `steps` steps, per-kernel HIP events recorded on
+    # the launch stream
+    _abi.prof_reset()
+    _abi.prof_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        layer.step(*args, forced_idx=forced)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _abi.prof_enable(False)
+    log("bench: timed steps done")
+
+    kern = {}
+    for name in _abi.prof_names():
+        n, ms = _abi.prof_query(name)
+        kern[name] = {"launches": n, "avg_us": 1000.0 * ms / max(n, 1)}
+    _abi.prof_reset()
+
+    # one clean step without events (events add a little host/GPU overhead)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(a.steps):
+        layer.step(*args, forced_idx=forced)
+    torch.cuda.synchronize()
+    elapsed_clean = time.perf_counter() - t1
+
+    ms_step = 1000.0 * elapsed / a.steps
+    tokens_per_s = cfg.T * a.steps / elapsed
+    rdh = cfg.R * cfg.d * cfg.h
+    gemm_flops = cfg.gemm_flops()
+    layer_flops = gemm_flops + cfg.router_flops()
+    gemm_us = 0.0
+    for name, mult in GEMM_KERNELS.items():
+        if name in kern:
+            kern[name]["tflops"] = mult * rdh / (kern[name]["avg_us"] * 1e-6) / 1e12
+            gemm_us += kern[name]["avg_us"]
+    dom = max((n for n in GEMM_KERNELS if n in kern), key=lambda n: kern[n]["avg_us"])
+    dom_flops = GEMM_KERNELS[dom] * rdh
+    achieved = dom_flops / (kern[dom]["avg_us"] * 1e-6) / 1e12
+
+    counts = layer.counts.cpu().numpy()
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded: x~N(0,1), weights~N(0,0.02^2), dy~N(0,1); values fixed across steps)",
+        "config": {"workload": f"{cfg.slug}: MoE expert layer fwd+bwd, T={cfg.T} d_model={cfg.d} experts={cfg.E} "
+                               f"top-{cfg.k} SwiGLU hidden={cfg.h} {cfg.dtype}, routing={mode}",
+                   "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "h": cfg.h, "routing": mode,
+                   "parallelism": "single GPU"},
+        "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
+        "layer_frac_bf16_peak": layer_flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "ggemm_tflops": gemm_flops / (gemm_us * 1e-6) / 1e12,
+        "ggemm_frac_bf16_peak": gemm_flops / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+        "ms_per_step_no_events": 1000.0 * elapsed_clean / a.steps,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_per_launch": f"{GEMM_KERNELS[dom]}*R*d*h = {dom_flops:.4g} flop"},
+        "kernels_avg_us": {n: round(v["avg_us"], 2) for n, v in sorted(kern.items())},
+        "expert_load": {"max": int(counts.max()), "mean": float(counts.mean()), "min": int(counts.min())},
+        "peak_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
+    }
+    if not a.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(cfg, mode, min(a.cpu_sample_tokens, cfg.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE expert-layer library.
+ *
+ * One GPU's share of an Olmo-core 3 style mixture-of-experts layer, forward and
+ * backward:
+ *
+ *   router logits -> softmax / top-k with all routing metadata kept on the GPU
+ *   -> rowwise dispatch of every routed token row straight into per-expert
+ *   contiguous input buffers -> one grouped GEMM over all experts' SwiGLU FFNs
+ *   -> gate-weighted combine; and the matching backward.
+ *
+ * Sources: "Olmo-core 3 open mixture-of-experts training infrastructure"
+ * (agentlenshq.com), section "Routing and compute optimisation": routed tokens
+ * are written directly into the experts' input buffers, routing metadata stays
+ * on the GPU so the CPU is not a bottleneck, and many small per-expert matrix
+ * products are batched into one larger grouped GEMM call.  The Thai
+ * announcement (ai4bro.com, "Scaling and optimising MoE training") adds that
+ * the CPU can queue work without waiting for data copies.  The same page set
+ * names MXFP8 as the low-precision option ("Precision optimisation with
+ * MXFP8").  The pages define no interface; the calls below are this library's.
+ *
+ * Conventions for every call
+ * ---------------------------
+ *  - All pointers are DEVICE pointers unless stated; the caller owns every
+ *    buffer.  The library never allocates device memory: scratch comes from a
+ *    caller workspace sized by the matching *_workspace_size() call.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns.  No call copies device data to the host and none
+ *    synchronises a stream or the device.  Buffer sizes depend only on
+ *    T, d, E, k, h (dropless: R = T*k routed rows).
+ *  - Tensors are contiguous and row-major.  Shapes:
+ *      x, y, dx [T,d]; wr, dwr [E,d]; logits, probs [T,E] f32;
+ *      topk_idx, pos [T,k] i32; topk_w, dgate [T,k] f32;
+ *      counts [E], offsets [E+1], off32 [E+1], src [R] i32;
+ *      xp, yp, dyp, dxp [R,d]; g, u, hbuf [R,h]; dgu [R,2h] (dG | dU);
+ *      w1, w3, dw1, dw3 [E,h,d]; w2, dw2 [E,d,h]   (output-major, K last).
+ *  - dt selects the storage type of activations, weights and gradients:
+ *    MOE_F32 or MOE_BF16.  Accumulation is always fp32.
+ *  - Data pointers must be 16-byte aligned; row widths in bytes (d or h times
+ *    the element size) must be multiples of 16.
+ *  - Errors: a non-zero moe_status_t; moe_last_error_string() holds a message
+ *    (thread-local).  Nothing throws across the ABI and nothing aborts.  After
+ *    an error no work has been enqueued by that call, except MOE_ERR_HIP which
+ *    reports a failed launch.
+ *  - Results are bitwise reproducible run to run (no order-dependent float
+ *    atomics) and independent of grid sizes.
+ *  - Only gfx950 is supported (MOE_ERR_UNSUPPORTED otherwise).
+ */
+#ifndef TRG_MOE_H
+#define TRG_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* bad size, null pointer, k > E, ...            */
+  MOE_ERR_UNSUPPORTED = 2,  /* device is not gfx950, or dtype combination    */
+  MOE_ERR_ALIGNMENT = 3,    /* pointer or row width not 16-byte aligned      */
+  MOE_ERR_WORKSPACE = 4,    /* workspace null or smaller than required       */
+  MOE_ERR_HIP = 5           /* a HIP launch or runtime call failed           */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2, MOE_E8M0 = 3 } moe_dtype_t;
+
+/* Device-side data errors OR-ed into *err_flag by moe_route (forced routing). */
+#define MOE_FLAG_INDEX_RANGE 1  /* a forced expert index outside [0, E)      */
+#define MOE_FLAG_DUPLICATE 2    /* a token lists the same expert twice       */
+
+/* Limits: 1 <= k <= min(E, 32); E <= 1024; T*k < 2^31. */
+
+const char* moe_version(void);
+const char* moe_last_error_string(void);
+
+/*
+ * Optional per-kernel timing for benchmarks (not part of the layer's math).
+ * moe_prof_enable(1): every grouped-GEMM kernel and every other entry point
+ * afterwards is bracketed by two HIP events recorded on its launch stream.
+ * moe_prof_query(name): waits for the recorded events of launches called
+ * `name` and returns their count and summed milliseconds (this call does
+ * block the host).  moe_prof_names(): newline-separated names seen so far;
+ * returns the size needed (including the NUL).  moe_prof_reset() frees all
+ * recorded events.
+ */
+moe_status_t moe_prof_enable(int on);
+moe_status_t moe_prof_reset(void);
+moe_status_t moe_prof_query(const char* name, int* count, float* total_ms);
+size_t moe_prof_names(char* buf, size_t n);
+
+/*
+ * moe_router_logits: logits[t,e] = sum_c x[t,c] * wr[e,c], fp32 accumulate,
+ * fp32 output.  The router of the MoE block (the pages call the step routing;
+ * its form -- a linear router followed by softmax / top-k -- is this
+ * library's reading).  x [T,d], wr [E,d] of type dt; logits [T,E] f32.
+ */
+moe_status_t moe_router_logits(const void* x, int dt, const void* wr, int T, int d, int E,
+                               float* logits, void* stream);
+
+/*
+ * moe_route: softmax + top-k + GPU-resident routing metadata ("Routing and
+ * compute optimisation": routing metadata stays on the GPU).
+ *   probs[t,:]  = softmax(logits[t,:]) (max-subtracted, fp32)
+ *   topk_idx[t,j] = the j-th largest logit's expert; ties go to the lower
+ *                 index.  If forced_idx [T,k] is non-null it is used instead
+ *                 (random-routing stress modes); entries outside [0,E) are
+ *                 clamped and flagged, duplicates flagged.
+ *   topk_w[t,j] = probs[t, topk_idx[t,j]]  (not renormalised)
+ *   counts[e]   = number of (t,j) routed to e; offsets = exclusive prefix sum
+ *                 (offsets[E] = T*k); off32 (nullable) = prefix sum of counts
+ *                 rounded up to multiples of 32 (MX column blocks).
+ *   pos[t,j]    = row of (t,j) in the expert-contiguous buffer: offsets[e]
+ *                 plus the number of entries (t',j') < (t,j) in (token, slot)
+ *                 order routed to the same e.  src[pos[t,j]] = t*k + j.
+ *   err_flag    = nullable int32; MOE_FLAG_* bits are OR-ed in on the device.
+ * ws: moe_route_workspace_size(T,E,k) bytes.  Bit-exact for identical logits.
+ */
+size_t moe_route_workspace_size(int T, int E, int k);
+moe_status_t moe_route(const float* logits, int T, int E, int k, const int32_t* forced_idx,
+                       float* probs, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                       int32_t* offsets, int32_t* pos, int32_t* src, int32_t* off32,
+                       int32_t* err_flag, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute: rowwise dispatch ("Routing and compute optimisation": routed
+ * tokens are written directly into the experts' input buffers).  Token-major:
+ * each x[t] row is read once and written to its k rows xp[pos[t,j]].
+ */
+moe_status_t moe_permute(const void* x, int dt, int T, int d, int k, const int32_t* pos,
+                         void* xp, void* stream);
+
+/*
+ * moe_combine: y[t] = sum_j topk_w[t,j] * yp[pos[t,j]], fp32 accumulation in
+ * slot order, one rounding to dt.  The inverse of the dispatch.
+ */
+moe_status_t moe_combine(const void* yp, const float* topk_w, const int32_t* pos, int T, int d,
+                         int k, int dt, void* y, void* stream);
+
+/*
+ * moe_combine_bwd: dyp[pos[t,j]] = topk_w[t,j] * dy[t] (rounded to dt) and
+ * dgate[t,j] = <dy[t], yp[pos[t,j]]> (fp32).
+ */
+moe_status_t moe_combine_bwd(const void* dy, const void* yp, const float* topk_w,
+                             const int32_t* pos, int T, int d, int k, int dt, void* dyp,
+                             float* dgate, void* stream);
+
+/*
+ * moe_unpermute_sum: dx[t] = sum_j dxp[pos[t,j]] (fp32 accumulation, one
+ * rounding).  Adjoint of moe_permute.
+ */
+moe_status_t moe_unpermute_sum(const void* dxp, const int32_t* pos, int T, int d, int k, int dt,
+                               void* dx, void* stream);
+
+/*
+ * moe_grouped_gemm_fwd: all experts' SwiGLU FFNs as grouped GEMMs over the
+ * ragged expert segments [offsets[e], offsets[e+1]) of xp ("Routing and
+ * compute optimisation": many small per-expert products batched into one
+ * grouped GEMM).  One launch computes, for every expert at once,
+ *   g = xp w1[e]^T, u = xp w3[e]^T, hbuf = silu(g) * u   (SwiGLU fused in the
+ *   epilogue; g, u, hbuf stored in dt for the backward),
+ * and a second launch yp = hbuf w2[e]^T.  The tile map is derived on the
+ * device from offsets.  ws: moe_grouped_gemm_workspace_size() bytes.
+ */
+size_t moe_grouped_gemm_workspace_size(int E, int R, int d, int h);
+moe_status_t moe_grouped_gemm_fwd(const void* xp, const void* w1, const void* w3, const void* w2,
+                                  const int32_t* offsets, int E, int R, int d, int h, int dt,
+                                  void* g, void* u, void* hbuf, void* yp, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_gemm_bwd: backward of moe_grouped_gemm_fwd given dyp.
+ *   dgrad down + SwiGLU backward (fused):  dH = dyp w2[e];  s = sigmoid(g);
+ *     dU = dH * silu(g);  dG = dH * u * s * (1 + g (1 - s))  -> dgu [R,2h]
+ *   wgrad down: dw2[e] = dyp_e^T hbuf_e   (K = the expert's rows)
+ *   dgrad up:   dxp = dG w1[e] + dU w3[e]
+ *   wgrad up:   dw1[e] = dG_e^T xp_e,  dw3[e] = dU_e^T xp_e
+ * Weight gradients are accumulated in fp32 over the whole segment and rounded
+ * once; an expert with no rows gets zero gradients.
+ */
+moe_status_t moe_grouped_gemm_bwd(const void* dyp, const void* xp, const void* g, const void* u,
+                                  const void* hbuf, const void* w1, const void* w3,
+                                  const void* w2, const int32_t* offsets, int E, int R, int d,
+                                  int h, int dt, void* dgu, void* dxp, void* dw1, void* dw3,
+                                  void* dw2, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_router_bwd: gradient through the gates into the logits, wr and x.
+ *   gh[t,e] = dgate[t,j] where e = topk_idx[t,j], else 0
+ *   dlogits = probs * (gh - sum_e probs*gh)      (softmax backward)
+ *   dwr = dlogits^T x;   dx += dlogits wr        (dx holds the expert-path
+ *                                                 gradient on entry)
+ * ws: moe_router_bwd_workspace_size(T,d,E) bytes.
+ */
+size_t moe_router_bwd_workspace_size(int T, int d, int E);
+moe_status_t moe_router_bwd(const float* probs, const int32_t* topk_idx, const float* dgate,
+                            const void* x, const void* wr, int T, int d, int E, int k, int dt,
+                            void* dx, void* dwr, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRG_MOE_H */

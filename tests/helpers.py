@@ -1,0 +1,38 @@
+"""Shared helpers for the GPU parity tests (no arithmetic of the method here)."""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Float tolerances for bf16 storage (and reused for fp32 layers): per tensor,
+# rel-L2 <= 1e-2 and max-abs <= 2e-2 * max|ref|.
+REL_L2 = 1e-2
+MAX_ABS_FRAC = 2e-2
+
+
+def rel_l2(a, r) -> float:
+    a = np.asarray(a, np.float64)
+    r = np.asarray(r, np.float64)
+    den = np.linalg.norm(r)
+    return float(np.linalg.norm(a - r) / den) if den > 0 else float(np.linalg.norm(a))
+
+
+def assert_close(name, got, ref, rel=REL_L2, max_frac=MAX_ABS_FRAC):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    r = rel_l2(got, ref)
+    m = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    assert r <= rel, f"{name}: rel-L2 {r:.3e} > {rel:.1e}"
+    assert m <= max_frac * scale + 1e-30, f"{name}: max-abs {m:.3e} > {max_frac:.0e} * {scale:.3e}"
+    return r, m
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy() if t.dtype.is_floating_point else t.detach().cpu().numpy()
+
+
+def say(*a):
+    print(*a, flush=True)

@@ -1,0 +1,71 @@
+"""CPU checks of the boundary: the built library loads and exports every
+function declared in include/moe.h, and the binding covers all of them."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "token_routing_grouped_amd", "libtrg_moe.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:moe|mx)_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for must in ("moe_route", "moe_permute", "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd", "moe_combine",
+                 "moe_combine_bwd", "moe_unpermute_sum", "moe_router_logits", "moe_router_bwd"):
+        assert must in names
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built (run __graft_entry__.build())")
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    from token_routing_grouped_amd import _abi
+
+    assert sorted(_abi.EXPORTED) == _declared()
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_host_side_validation_without_gpu():
+    """Argument checks run before any device call, so they work without a GPU."""
+    from token_routing_grouped_amd import _abi
+
+    lib = _abi.lib()
+    assert lib.moe_version().decode().startswith("trg-moe")
+    # k > E
+    st = lib.moe_route(None, 4, 2, 3, None, None, None, None, None, None, None, None, None, None, None, 0, None)
+    assert st == 1 and b"k (3) > E (2)" in lib.moe_last_error_string()
+    # bad dtype
+    st = lib.moe_permute(None, 7, 4, 64, 2, None, None, None)
+    assert st == 2
+    # row width not a multiple of 16 bytes
+    st = lib.moe_permute(None, 1, 4, 12, 2, None, None, None)
+    assert st == 3
+    # workspace too small
+    st = lib.moe_route(ctypes.c_void_p(16), 8, 4, 2, None, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                       ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                       ctypes.c_void_p(16), None, None, None, 0, None)
+    assert st == 4
+    # unaligned pointer
+    st = lib.moe_permute(ctypes.c_void_p(8), 1, 4, 64, 2, ctypes.c_void_p(16), ctypes.c_void_p(16), None)
+    assert st == 3
+    # bf16 grouped GEMM needs h % 64 == 0
+    st = lib.moe_grouped_gemm_fwd(None, None, None, None, None, 4, 8, 64, 40, 1, None, None, None, None, None, 0,
+                                  None)
+    assert st == 1
+    # k out of range
+    st = lib.moe_combine(None, None, None, 4, 64, 0, 1, None, None)
+    assert st == 1

@@ -1,0 +1,240 @@
+"""ctypes binding of the C ABI in include/moe.h (argument marshalling only).
+
+Every function takes torch tensors that live on the current HIP device, checks
+device, dtype and contiguity, and passes raw pointers plus torch's current
+stream.  All arithmetic happens in the HIP library; if the library is missing
+the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrg_moe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+FLAG_INDEX_RANGE, FLAG_DUPLICATE = 1, 2
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_Z = ctypes.c_size_t
+
+_SIGS = {
+    "moe_version": ([], ctypes.c_char_p),
+    "moe_last_error_string": ([], ctypes.c_char_p),
+    "moe_prof_enable": ([_I], _I),
+    "moe_prof_reset": ([], _I),
+    "moe_prof_query": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)], _I),
+    "moe_prof_names": ([ctypes.c_char_p, _Z], _Z),
+    "moe_router_logits": ([_P, _I, _P, _I, _I, _I, _P, _P], _I),
+    "moe_route_workspace_size": ([_I, _I, _I], _Z),
+    "moe_route": ([_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "moe_permute": ([_P, _I, _I, _I, _I, _P, _P, _P], _I),
+    "moe_combine": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
+    "moe_combine_bwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P], _I),
+    "moe_unpermute_sum": ([_P, _P, _I, _I, _I, _I, _P, _P], _I),
+    "moe_grouped_gemm_workspace_size": ([_I, _I, _I, _I], _Z),
+    "moe_grouped_gemm_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "moe_grouped_gemm_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z,
+                              _P], _I),
+    "moe_router_bwd_workspace_size": ([_I, _I, _I], _Z),
+    "moe_router_bwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+}
+
+EXPORTED = tuple(_SIGS)
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(f"HIP library not built: {LIB_PATH} is missing (run __graft_entry__.build())")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(h, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = h
+    return _lib
+
+
+def version() -> str:
+    return lib().moe_version().decode()
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        msg = lib().moe_last_error_string().decode()
+        raise MoeError(f"{fn} failed (status {status}): {msg}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise MoeError(f"tensor on {t.device}, expected the GPU")
+    if not t.is_contiguous():
+        raise MoeError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t) -> int:
+    if t.dtype not in _DT:
+        raise MoeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _expect(t, dtype, name):
+    if t is not None and t.dtype != dtype:
+        raise MoeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# optional per-kernel event timing (benchmarks)
+# ---------------------------------------------------------------------------
+
+def prof_enable(on: bool = True):
+    _check(lib().moe_prof_enable(1 if on else 0), "moe_prof_enable")
+
+
+def prof_reset():
+    _check(lib().moe_prof_reset(), "moe_prof_reset")
+
+
+def prof_names():
+    n = lib().moe_prof_names(None, 0)
+    buf = ctypes.create_string_buffer(int(n))
+    lib().moe_prof_names(buf, n)
+    return [s for s in buf.value.decode().split("\n") if s]
+
+
+def prof_query(name: str):
+    """(launch count, total milliseconds) of the recorded launches called name."""
+    c = ctypes.c_int(0)
+    ms = ctypes.c_float(0.0)
+    _check(lib().moe_prof_query(name.encode(), ctypes.byref(c), ctypes.byref(ms)), "moe_prof_query")
+    return c.value, ms.value
+
+
+# ---------------------------------------------------------------------------
+# workspace sizes
+# ---------------------------------------------------------------------------
+
+def moe_route_workspace_size(T: int, E: int, k: int) -> int:
+    return int(lib().moe_route_workspace_size(T, E, k))
+
+
+def moe_grouped_gemm_workspace_size(E: int, R: int, d: int, h: int) -> int:
+    return int(lib().moe_grouped_gemm_workspace_size(E, R, d, h))
+
+
+def moe_router_bwd_workspace_size(T: int, d: int, E: int) -> int:
+    return int(lib().moe_router_bwd_workspace_size(T, d, E))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# calls
+# ---------------------------------------------------------------------------
+
+def moe_router_logits(x, wr, logits):
+    T, d = x.shape
+    E = wr.shape[0]
+    _expect(wr, x.dtype, "wr")
+    _expect(logits, torch.float32, "logits")
+    _check(lib().moe_router_logits(_p(x), _dt(x), _p(wr), T, d, E, _p(logits), _stream()), "moe_router_logits")
+
+
+def moe_route(logits, k, probs, topk_idx, topk_w, counts, offsets, pos, src, ws, off32=None, forced_idx=None,
+              err_flag=None):
+    T, E = logits.shape
+    for t, n, dt in ((logits, "logits", torch.float32), (probs, "probs", torch.float32),
+                     (topk_w, "topk_w", torch.float32), (topk_idx, "topk_idx", torch.int32),
+                     (counts, "counts", torch.int32), (offsets, "offsets", torch.int32), (pos, "pos", torch.int32),
+                     (src, "src", torch.int32), (off32, "off32", torch.int32), (forced_idx, "forced_idx", torch.int32),
+                     (err_flag, "err_flag", torch.int32)):
+        _expect(t, dt, n)
+    _check(lib().moe_route(_p(logits), T, E, k, _p(forced_idx), _p(probs), _p(topk_idx), _p(topk_w), _p(counts),
+                           _p(offsets), _p(pos), _p(src), _p(off32), _p(err_flag), _p(ws), ws.numel(), _stream()),
+           "moe_route")
+
+
+def moe_permute(x, pos, xp):
+    T, d = x.shape
+    k = pos.shape[1]
+    _expect(xp, x.dtype, "xp")
+    _check(lib().moe_permute(_p(x), _dt(x), T, d, k, _p(pos), _p(xp), _stream()), "moe_permute")
+
+
+def moe_combine(yp, topk_w, pos, y):
+    T, k = pos.shape
+    d = yp.shape[1]
+    _expect(y, yp.dtype, "y")
+    _check(lib().moe_combine(_p(yp), _p(topk_w), _p(pos), T, d, k, _dt(yp), _p(y), _stream()), "moe_combine")
+
+
+def moe_combine_bwd(dy, yp, topk_w, pos, dyp, dgate):
+    T, k = pos.shape
+    d = yp.shape[1]
+    _expect(dy, yp.dtype, "dy")
+    _expect(dyp, yp.dtype, "dyp")
+    _expect(dgate, torch.float32, "dgate")
+    _check(lib().moe_combine_bwd(_p(dy), _p(yp), _p(topk_w), _p(pos), T, d, k, _dt(yp), _p(dyp), _p(dgate),
+                                 _stream()), "moe_combine_bwd")
+
+
+def moe_unpermute_sum(dxp, pos, dx):
+    T, k = pos.shape
+    d = dxp.shape[1]
+    _expect(dx, dxp.dtype, "dx")
+    _check(lib().moe_unpermute_sum(_p(dxp), _p(pos), T, d, k, _dt(dxp), _p(dx), _stream()), "moe_unpermute_sum")
+
+
+def moe_grouped_gemm_fwd(xp, w1, w3, w2, offsets, g, u, hbuf, yp, ws):
+    R, d = xp.shape
+    E, h, _ = w1.shape
+    for t, n in ((w1, "w1"), (w3, "w3"), (w2, "w2"), (g, "g"), (u, "u"), (hbuf, "hbuf"), (yp, "yp")):
+        _expect(t, xp.dtype, n)
+    _check(lib().moe_grouped_gemm_fwd(_p(xp), _p(w1), _p(w3), _p(w2), _p(offsets), E, R, d, h, _dt(xp), _p(g), _p(u),
+                                      _p(hbuf), _p(yp), _p(ws), ws.numel(), _stream()), "moe_grouped_gemm_fwd")
+
+
+def moe_grouped_gemm_bwd(dyp, xp, g, u, hbuf, w1, w3, w2, offsets, dgu, dxp, dw1, dw3, dw2, ws):
+    R, d = xp.shape
+    E, h, _ = w1.shape
+    for t, n in ((dyp, "dyp"), (g, "g"), (u, "u"), (hbuf, "hbuf"), (w1, "w1"), (w3, "w3"), (w2, "w2"), (dgu, "dgu"),
+                 (dxp, "dxp"), (dw1, "dw1"), (dw3, "dw3"), (dw2, "dw2")):
+        _expect(t, xp.dtype, n)
+    _check(lib().moe_grouped_gemm_bwd(_p(dyp), _p(xp), _p(g), _p(u), _p(hbuf), _p(w1), _p(w3), _p(w2), _p(offsets), E,
+                                      R, d, h, _dt(xp), _p(dgu), _p(dxp), _p(dw1), _p(dw3), _p(dw2), _p(ws), ws.numel(),
+                                      _stream()), "moe_grouped_gemm_bwd")
+
+
+def moe_router_bwd(probs, topk_idx, dgate, x, wr, dx, dwr, ws):
+    T, d = x.shape
+    E = wr.shape[0]
+    k = topk_idx.shape[1]
+    _expect(dx, x.dtype, "dx")
+    _expect(dwr, x.dtype, "dwr")
+    _check(lib().moe_router_bwd(_p(probs), _p(topk_idx), _p(dgate), _p(x), _p(wr), T, d, E, k, _dt(x), _p(dx), _p(dwr),
+                                _p(ws), ws.numel(), _stream()), "moe_router_bwd")

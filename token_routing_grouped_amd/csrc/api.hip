@@ -1,0 +1,370 @@
+// C ABI of the MoE expert-layer library: argument validation, workspace
+// checks, error reporting, and the launches.  Every entry point only enqueues
+// work on the caller's stream; none copies device data to the host or
+// synchronises (the routing metadata never leaves the GPU).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+#include "prof.h"
+
+// ---- optional HIP-event timing of individual launches -----------------------
+namespace trg {
+namespace {
+std::atomic<bool> g_prof{false};
+std::mutex g_prof_mu;
+struct ProfRec {
+  std::string name;
+  hipEvent_t b, e;
+};
+std::vector<ProfRec> g_prof_done;
+std::vector<std::pair<std::string, hipEvent_t>> g_prof_open;
+}  // namespace
+
+bool prof_on() { return g_prof.load(std::memory_order_relaxed); }
+
+void prof_begin(const char* name, hipStream_t s) {
+  hipEvent_t ev;
+  if (hipEventCreate(&ev) != hipSuccess) return;
+  (void)hipEventRecord(ev, s);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_open.emplace_back(name, ev);
+}
+
+void prof_end(const char* name, hipStream_t s) {
+  hipEvent_t ev;
+  if (hipEventCreate(&ev) != hipSuccess) return;
+  (void)hipEventRecord(ev, s);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (size_t i = g_prof_open.size(); i-- > 0;) {
+    if (g_prof_open[i].first == name) {
+      g_prof_done.push_back({name, g_prof_open[i].second, ev});
+      g_prof_open.erase(g_prof_open.begin() + (long)i);
+      return;
+    }
+  }
+  (void)hipEventDestroy(ev);
+}
+}  // namespace trg
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status_t ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+// gfx950 check, cached per device.
+constexpr int kMaxDev = 64;
+int g_arch_ok[kMaxDev];  // 0 unknown, 1 ok, -1 not gfx950
+std::mutex g_arch_mu;
+
+moe_status_t check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDev) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDeviceProperties failed");
+    g_arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  if (g_arch_ok[dev] != 1) return fail(MOE_ERR_UNSUPPORTED, "this library is built for gfx950 only");
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status_t check_ptrs(const char* fn, std::initializer_list<std::pair<const char*, const void*>> ps) {
+  for (auto& p : ps) {
+    if (p.second == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: %s is null", fn, p.first);
+    if (!aligned16(p.second)) return fail(MOE_ERR_ALIGNMENT, "%s: %s is not 16-byte aligned", fn, p.first);
+  }
+  return MOE_OK;
+}
+
+moe_status_t check_dt(const char* fn, int dt) {
+  if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: dt must be MOE_F32 or MOE_BF16", fn);
+  return MOE_OK;
+}
+
+int esize(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+moe_status_t check_row(const char* fn, const char* name, long n, int dt) {
+  if (n <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: %s must be positive", fn, name);
+  if ((n * esize(dt)) % 16 != 0)
+    return fail(MOE_ERR_ALIGNMENT, "%s: %s * element size must be a multiple of 16 bytes", fn, name);
+  return MOE_OK;
+}
+
+moe_status_t check_tk(const char* fn, int T, int k) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T must be >= 0", fn);
+  if (k < 1 || k > 32) return fail(MOE_ERR_INVALID_ARG, "%s: k must be in [1, 32]", fn);
+  if ((long)T * k >= (1L << 31)) return fail(MOE_ERR_INVALID_ARG, "%s: T*k must be < 2^31", fn);
+  return MOE_OK;
+}
+
+moe_status_t hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+#define TRY(x)                      \
+  do {                              \
+    moe_status_t _st = (x);         \
+    if (_st != MOE_OK) return _st;  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "trg-moe 0.1 (gfx950)"; }
+
+const char* moe_last_error_string(void) { return g_err.c_str(); }
+
+moe_status_t moe_prof_enable(int on) {
+  trg::g_prof.store(on != 0);
+  return ok();
+}
+
+moe_status_t moe_prof_reset(void) {
+  std::lock_guard<std::mutex> lk(trg::g_prof_mu);
+  for (auto& r : trg::g_prof_done) {
+    (void)hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.e);
+  }
+  for (auto& o : trg::g_prof_open) (void)hipEventDestroy(o.second);
+  trg::g_prof_done.clear();
+  trg::g_prof_open.clear();
+  return ok();
+}
+
+moe_status_t moe_prof_query(const char* name, int* count, float* total_ms) {
+  if (!name || !count || !total_ms) return fail(MOE_ERR_INVALID_ARG, "moe_prof_query: null argument");
+  std::lock_guard<std::mutex> lk(trg::g_prof_mu);
+  int n = 0;
+  float tot = 0.f;
+  for (auto& r : trg::g_prof_done) {
+    if (r.name != name) continue;
+    if (hipEventSynchronize(r.e) != hipSuccess) return fail(MOE_ERR_HIP, "moe_prof_query: event wait failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.b, r.e) != hipSuccess) return fail(MOE_ERR_HIP, "moe_prof_query: elapsed failed");
+    tot += ms;
+    ++n;
+  }
+  *count = n;
+  *total_ms = tot;
+  return ok();
+}
+
+size_t moe_prof_names(char* buf, size_t n) {
+  std::lock_guard<std::mutex> lk(trg::g_prof_mu);
+  std::string all;
+  for (auto& r : trg::g_prof_done) {
+    std::string key = r.name + "\n";
+    if (all.find(key) == std::string::npos && ("\n" + all).find("\n" + key) == std::string::npos) all += key;
+  }
+  if (buf && n > 0) {
+    size_t m = all.size() < n - 1 ? all.size() : n - 1;
+    memcpy(buf, all.data(), m);
+    buf[m] = 0;
+  }
+  return all.size() + 1;
+}
+
+moe_status_t moe_router_logits(const void* x, int dt, const void* wr, int T, int d, int E, float* logits,
+                               void* stream) {
+  const char* fn = "moe_router_logits";
+  TRY(check_dt(fn, dt));
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T must be >= 0", fn);
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
+  TRY(check_row(fn, "d", d, dt));
+  if (!(dt == MOE_BF16 && E >= 64 && E % 8 == 0) && E > 64)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E > 64 needs bf16 storage and E %% 8 == 0", fn);
+  TRY(check_ptrs(fn, {{"x", x}, {"wr", wr}, {"logits", logits}}));
+  TRY(check_device());
+  trg::ProfScope ps(fn, (hipStream_t)stream);
+  return hip_status(fn, trg::launch_router_logits(x, dt == MOE_BF16, wr, T, d, E, logits, (hipStream_t)stream));
+}
+
+size_t moe_route_workspace_size(int T, int E, int k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  return trg::route_ws_bytes(T, E, k);
+}
+
+moe_status_t moe_route(const float* logits, int T, int E, int k, const int32_t* forced_idx, float* probs,
+                       int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* pos,
+                       int32_t* src, int32_t* off32, int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_route";
+  TRY(check_tk(fn, T, k));
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "%s: k (%d) > E (%d)", fn, k, E);
+  if (T > 0)
+    TRY(check_ptrs(fn, {{"logits", logits}, {"probs", probs}, {"topk_idx", topk_idx}, {"topk_w", topk_w},
+                        {"pos", pos}, {"src", src}}));
+  TRY(check_ptrs(fn, {{"counts", counts}, {"offsets", offsets}}));
+  const size_t need = trg::route_ws_bytes(T, E, k);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  if (ws && !aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+  TRY(check_device());
+  trg::ProfScope ps(fn, (hipStream_t)stream);
+  return hip_status(fn, trg::launch_route(logits, T, E, k, forced_idx, probs, topk_idx, topk_w, counts, offsets, pos,
+                                          src, off32, err_flag, ws, (hipStream_t)stream));
+}
+
+moe_status_t moe_permute(const void* x, int dt, int T, int d, int k, const int32_t* pos, void* xp, void* stream) {
+  const char* fn = "moe_permute";
+  TRY(check_dt(fn, dt));
+  TRY(check_tk(fn, T, k));
+  TRY(check_row(fn, "d", d, dt));
+  if (T == 0) return ok();
+  TRY(check_ptrs(fn, {{"x", x}, {"pos", pos}, {"xp", xp}}));
+  TRY(check_device());
+  trg::ProfScope ps(fn, (hipStream_t)stream);
+  return hip_status(fn, trg::launch_permute(x, dt == MOE_BF16, T, d, k, pos, xp, (hipStream_t)stream));
+}
+
+moe_status_t moe_combine(const void* yp, const float* topk_w, const int32_t* pos, int T, int d, int k, int dt,
+                         void* y, void* stream) {
+  const char* fn = "moe_combine";
+  TRY(check_dt(fn, dt));
+  TRY(check_tk(fn, T, k));
+  TRY(check_row(fn, "d", d, dt));
+  if (T == 0) return ok();
+  TRY(check_ptrs(fn, {{"yp", yp}, {"topk_w", topk_w}, {"pos", pos}, {"y", y}}));
+  TRY(check_device());
+  trg::ProfScope ps(fn, (hipStream_t)stream);
+  return hip_status(fn, trg::launch_gather_sum(yp, topk_w, pos, T, d, k, dt == MOE_BF16, y, (hipStream_t)stream));
+}
+
+moe_status_t moe_combine_bwd(const void* dy, const void* yp, const float* topk_w, const int32_t* pos, int T, int d,
+                             int k, int dt, void* dyp, float* dgate, void* stream) {
+  const char* fn = "moe_combine_bwd";
+  TRY(check_dt(fn, dt));
+  TRY(check_tk(fn, T, k));
+  TRY(check_row(fn, "d", d, dt));
+  if (T == 0) return ok();
+  TRY(check_ptrs(fn, {{"dy", dy}, {"yp", yp}, {"topk_w", topk_w}, {"pos", pos}, {"dyp", dyp}, {"dgate", dgate}}));
+  TRY(check_device());
+  trg::ProfScope ps(fn, (hipStream_t)stream);
+  return hip_status(fn, trg::launch_combine_bwd(dy, yp, topk_w, pos, T, d, k, dt == MOE_BF16, dyp, dgate,
+                                                (hipStream_t)stream));
+}
+
+moe_status_t moe_unpermute_sum(const void* dxp, const int32_t* pos, int T, int d, int k, int dt, void* dx,
+                               void* stream) {
+  const char* fn = "moe_unpermute_sum";
+  TRY(check_dt(fn, dt));
+  TRY(check_tk(fn, T, k));
+  TRY(check_row(fn, "d", d, dt));
+  if (T == 0) return ok();
+  TRY(check_ptrs(fn, {{"dxp", dxp}, {"pos", pos}, {"dx", dx}}));
+  TRY(check_device());
+  trg::ProfScope ps(fn, (hipStream_t)stream);
+  return hip_status(fn, trg::launch_gather_sum(dxp, nullptr, pos, T, d, k, dt == MOE_BF16, dx, (hipStream_t)stream));
+}
+
+static moe_status_t check_ggemm_dims(const char* fn, int E, int R, int d, int h, int dt) {
+  TRY(check_dt(fn, dt));
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
+  if (R < 0) return fail(MOE_ERR_INVALID_ARG, "%s: R must be >= 0", fn);
+  TRY(check_row(fn, "d", d, dt));
+  TRY(check_row(fn, "h", h, dt));
+  if (dt == MOE_BF16 && (h % 64 != 0 || d % 8 != 0))
+    return fail(MOE_ERR_INVALID_ARG, "%s: bf16 path needs h %% 64 == 0 and d %% 8 == 0", fn);
+  return MOE_OK;
+}
+
+size_t moe_grouped_gemm_workspace_size(int E, int R, int d, int h) {
+  if (E < 1) return 0;
+  return trg::ggemm_ws_bytes(E, R, d, h);
+}
+
+moe_status_t moe_grouped_gemm_fwd(const void* xp, const void* w1, const void* w3, const void* w2,
+                                  const int32_t* offsets, int E, int R, int d, int h, int dt, void* g, void* u,
+                                  void* hbuf, void* yp, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_gemm_fwd";
+  TRY(check_ggemm_dims(fn, E, R, d, h, dt));
+  TRY(check_ptrs(fn, {{"w1", w1}, {"w3", w3}, {"w2", w2}, {"offsets", offsets}}));
+  if (R == 0) return ok();
+  TRY(check_ptrs(fn, {{"xp", xp}, {"g", g}, {"u", u}, {"hbuf", hbuf}, {"yp", yp}}));
+  const size_t need = trg::ggemm_ws_bytes(E, R, d, h);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  if (!aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+  TRY(check_device());
+  return hip_status(fn, trg::launch_ggemm_fwd(xp, w1, w3, w2, offsets, E, R, d, h, dt == MOE_BF16, g, u, hbuf, yp, ws,
+                                              (hipStream_t)stream));
+}
+
+moe_status_t moe_grouped_gemm_bwd(const void* dyp, const void* xp, const void* g, const void* u, const void* hbuf,
+                                  const void* w1, const void* w3, const void* w2, const int32_t* offsets, int E, int R,
+                                  int d, int h, int dt, void* dgu, void* dxp, void* dw1, void* dw3, void* dw2,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_gemm_bwd";
+  TRY(check_ggemm_dims(fn, E, R, d, h, dt));
+  TRY(check_ptrs(fn, {{"w1", w1}, {"w3", w3}, {"w2", w2}, {"offsets", offsets}, {"dw1", dw1}, {"dw3", dw3},
+                      {"dw2", dw2}}));
+  if (R > 0)
+    TRY(check_ptrs(fn, {{"dyp", dyp}, {"xp", xp}, {"g", g}, {"u", u}, {"hbuf", hbuf}, {"dgu", dgu}, {"dxp", dxp}}));
+  const size_t need = trg::ggemm_ws_bytes(E, R, d, h);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  if (!aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+  TRY(check_device());
+  return hip_status(fn, trg::launch_ggemm_bwd(dyp, xp, g, u, hbuf, w1, w3, w2, offsets, E, R, d, h, dt == MOE_BF16,
+                                              dgu, dxp, dw1, dw3, dw2, ws, (hipStream_t)stream));
+}
+
+size_t moe_router_bwd_workspace_size(int T, int d, int E) {
+  if (T < 0 || d < 1 || E < 1) return 0;
+  return trg::router_bwd_ws_bytes(T, d, E);
+}
+
+moe_status_t moe_router_bwd(const float* probs, const int32_t* topk_idx, const float* dgate, const void* x,
+                            const void* wr, int T, int d, int E, int k, int dt, void* dx, void* dwr, void* ws,
+                            size_t ws_bytes, void* stream) {
+  const char* fn = "moe_router_bwd";
+  TRY(check_dt(fn, dt));
+  TRY(check_tk(fn, T, k));
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "%s: k (%d) > E (%d)", fn, k, E);
+  TRY(check_row(fn, "d", d, dt));
+  if (!(dt == MOE_BF16 && E >= 64 && E % 8 == 0) && E > 64)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E > 64 needs bf16 storage and E %% 8 == 0", fn);
+  TRY(check_ptrs(fn, {{"wr", wr}, {"dwr", dwr}}));
+  if (T > 0)
+    TRY(check_ptrs(fn, {{"probs", probs}, {"topk_idx", topk_idx}, {"dgate", dgate}, {"x", x}, {"dx", dx}}));
+  const size_t need = trg::router_bwd_ws_bytes(T, d, E);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  if (!aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+  TRY(check_device());
+  trg::ProfScope ps(fn, (hipStream_t)stream);
+  return hip_status(fn, trg::launch_router_bwd(probs, topk_idx, dgate, x, wr, T, d, E, k, dt == MOE_BF16, dx, dwr, ws,
+                                               (hipStream_t)stream));
+}
+
+}  // extern "C"

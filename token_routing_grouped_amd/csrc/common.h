@@ -1,0 +1,111 @@
+// Internal helpers shared by the gfx950 kernels of the MoE library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define TRG_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#include <utility>
+
+namespace trg {
+
+constexpr int kWave = 64;
+
+// Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>).  Keeps
+// register-array indices constant where #pragma unroll may give up.
+template <class F, int... I>
+TRG_DEV void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+TRG_DEV void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ---- bfloat16 <-> float (storage is raw uint16_t) ---------------------------
+TRG_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+TRG_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+TRG_DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round to nearest even; NaN stays NaN.
+TRG_DEV uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+TRG_DEV uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Element access for the two storage types.
+template <class T> struct Elt;
+template <> struct Elt<float> {
+  static TRG_DEV float ld(const float* p) { return *p; }
+  static TRG_DEV void st(float* p, float v) { *p = v; }
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+};
+template <> struct Elt<uint16_t> {
+  static TRG_DEV float ld(const uint16_t* p) { return bf2f(*p); }
+  static TRG_DEV void st(uint16_t* p, float v) { *p = f2bf(v); }
+  static constexpr int kVec = 8;
+};
+
+// Unpack a 16-byte vector into floats, and pack floats back.
+template <class T> TRG_DEV void unpack16(const uint4& v, float* f);
+template <> TRG_DEV void unpack16<float>(const uint4& v, float* f) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+template <> TRG_DEV void unpack16<uint16_t>(const uint4& v, float* f) {
+  f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+  f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+}
+template <class T> TRG_DEV uint4 pack16(const float* f);
+template <> TRG_DEV uint4 pack16<float>(const float* f) {
+  return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                    __float_as_uint(f[3]));
+}
+template <> TRG_DEV uint4 pack16<uint16_t>(const float* f) {
+  return make_uint4(pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]), pack_bf2(f[4], f[5]),
+                    pack_bf2(f[6], f[7]));
+}
+
+// ---- wave reductions ---------------------------------------------------------
+TRG_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+TRG_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Exclusive scan of one value per thread over a block of 1024 threads.
+TRG_DEV int block_excl_scan_1024(int v, int* tmp /* 1024 */, int* total) {
+  const int tid = threadIdx.x;
+  tmp[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int add = tid >= o ? tmp[tid - o] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  int incl = tmp[tid];
+  *total = tmp[1023];
+  __syncthreads();
+  return incl - v;
+}
+
+TRG_DEV float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+TRG_DEV float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+}  // namespace trg

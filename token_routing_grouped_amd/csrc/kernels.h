@@ -1,0 +1,59 @@
+// Internal launch entry points (host side) of the gfx950 kernels.  The C ABI
+// in api.hip validates arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace trg {
+
+// routing
+size_t route_ws_bytes(int T, int E, int k);
+hipError_t launch_route(const float* logits, int T, int E, int k, const int* forced, float* probs, int* idx,
+                        float* w, int* counts, int* offsets, int* pos, int* src, int* off32, int* err_flag,
+                        void* ws, hipStream_t s);
+
+// dispatch / combine (bf16 = uint16_t storage, or float)
+hipError_t launch_permute(const void* x, bool bf16, int T, int d, int k, const int* pos, void* xp, hipStream_t s);
+hipError_t launch_gather_sum(const void* yp, const float* w, const int* pos, int T, int d, int k, bool bf16,
+                             void* y, hipStream_t s);
+hipError_t launch_combine_bwd(const void* dy, const void* yp, const float* w, const int* pos, int T, int d, int k,
+                              bool bf16, void* dyp, float* dgate, hipStream_t s);
+
+// router GEMMs
+size_t router_bwd_ws_bytes(int T, int d, int E);
+hipError_t launch_router_logits(const void* x, bool bf16, const void* wr, int T, int d, int E, float* logits,
+                                hipStream_t s);
+hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dgate, const void* x, const void* wr,
+                             int T, int d, int E, int k, bool bf16, void* dx, void* dwr, void* ws, hipStream_t s);
+
+// grouped GEMMs
+size_t ggemm_ws_bytes(int E, int R, int d, int h);
+hipError_t launch_ggemm_fwd(const void* xp, const void* w1, const void* w3, const void* w2, const int* offsets,
+                            int E, int R, int d, int h, bool bf16, void* g, void* u, void* hb, void* yp, void* ws,
+                            hipStream_t s);
+hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, const void* u, const void* hb,
+                            const void* w1, const void* w3, const void* w2, const int* offsets, int E, int R, int d,
+                            int h, bool bf16, void* dgu, void* dxp, void* dw1, void* dw3, void* dw2, void* ws,
+                            hipStream_t s);
+
+// bf16 MFMA dense GEMM helpers used by the router (E >= 64)
+hipError_t launch_dense_nt_f32out(const uint16_t* A, const uint16_t* B, float* C, int M, int N, int K,
+                                  hipStream_t s);
+hipError_t launch_router_dwr_mfma(const uint16_t* dL, const uint16_t* x, uint16_t* dwr, float* part, int T, int d,
+                                  int E, hipStream_t s);
+hipError_t launch_router_dx_mfma(const uint16_t* dL, const uint16_t* wr, uint16_t* dx, int T, int d, int E,
+                                 hipStream_t s);
+size_t router_dwr_mfma_part_bytes(int T, int d, int E);
+
+// fp32 reference-shaped grouped GEMMs (small fp32 layers)
+hipError_t launch_ggemm_fwd_f32(const float* xp, const float* w1, const float* w3, const float* w2,
+                                const int* offsets, int E, int R, int d, int h, float* g, float* u, float* hb,
+                                float* yp, hipStream_t s);
+hipError_t launch_ggemm_bwd_f32(const float* dyp, const float* xp, const float* g, const float* u, const float* hb,
+                                const float* w1, const float* w3, const float* w2, const int* offsets, int E, int R,
+                                int d, int h, float* dgu, float* dxp, float* dw1, float* dw3, float* dw2,
+                                hipStream_t s);
+
+}  // namespace trg

@@ -1,0 +1,261 @@
+// GPU-resident routing: softmax / top-k, expert histogram, prefix sum and
+// stable positions.  Nothing here leaves the device (Olmo-core 3 overview,
+// "Routing and compute optimisation": routing metadata is kept on the GPU so
+// the CPU never waits on it).
+//
+// Four launches, all deterministic (integer LDS atomics only, order-free):
+//   route_topk   one wave per token: max, sum of exp, k rounds of wave argmax
+//   route_count  one wave per chunk of 256 flattened (t, j) entries -> per-chunk
+//                per-expert counts
+//   route_scan   one workgroup: per-expert exclusive scan over chunks, counts,
+//                offsets, off32
+//   route_rank   one wave per chunk: rank of each entry among equal experts in
+//                (token, slot) order via LDS match masks + popcount
+#include "common.h"
+#include "kernels.h"
+
+namespace trg {
+
+constexpr int kChunk = 256;  // flattened (t, j) entries per rank/count chunk
+
+// Lexicographic (value desc, index asc) comparison used for top-k.
+TRG_DEV bool better(float v, int e, float bv, int be) { return v > bv || (v == bv && e < be); }
+
+template <int EPL>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                         int k, const int* __restrict__ forced,
+                                                         float* __restrict__ probs, int* __restrict__ idx_out,
+                                                         float* __restrict__ w_out, int* __restrict__ err_flag) {
+  const int lane = threadIdx.x & 63;
+  const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  if (t >= T) return;  // the whole wave leaves together
+  const float* L = logits + (long)t * E;
+  float v[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    int e = lane + 64 * i;
+    float x = e < E ? L[e] : -INFINITY;
+    v[i] = (x != x) ? -INFINITY : x;  // NaN never wins a slot
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) m = fmaxf(m, v[i]);
+  m = wave_max(m);
+  float ex[EPL], s = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    int e = lane + 64 * i;
+    ex[i] = e < E ? expf(v[i] - m) : 0.f;
+    s += ex[i];
+  }
+  s = wave_sum(s);
+  float p[EPL];
+  float* P = probs + (long)t * E;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    int e = lane + 64 * i;
+    p[i] = ex[i] / s;
+    if (e < E) P[e] = p[i];
+  }
+
+  if (forced != nullptr) {
+    // Given indices: validate, clamp into range, flag problems.
+    int fe = lane < k ? forced[(long)t * k + lane] : 0;
+    int flags = 0;
+    if (lane < k && (fe < 0 || fe >= E)) {
+      flags |= 1;
+      fe = fe < 0 ? 0 : E - 1;
+    }
+    for (int j = 0; j < k; ++j) {
+      int other = __shfl(fe, j, 64);
+      if (lane < k && j < lane && other == fe) flags |= 2;
+    }
+    // gate = p of expert fe, owned by lane fe % 64, slot fe / 64
+    float w = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      float c = __shfl(p[i], fe & 63, 64);
+      if ((fe >> 6) == i) w = c;
+    }
+    if (lane < k) {
+      idx_out[(long)t * k + lane] = fe;
+      w_out[(long)t * k + lane] = w;
+      if (flags && err_flag) atomicOr(err_flag, flags);
+    }
+    return;
+  }
+
+  unsigned chosen = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      int e = lane + 64 * i;
+      if (e < E && !((chosen >> i) & 1u) && better(v[i], e, bv, be)) {
+        bv = v[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      float ov = __shfl_xor(bv, o, 64);
+      int oe = __shfl_xor(be, o, 64);
+      if (better(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    // be is now uniform across the wave
+    float w = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if ((be >> 6) == i && (be & 63) == lane) chosen |= 1u << i;
+      float c = __shfl(p[i], be & 63, 64);
+      if ((be >> 6) == i) w = c;
+    }
+    if (lane == 0) {
+      idx_out[(long)t * k + j] = be;
+      w_out[(long)t * k + j] = w;
+    }
+  }
+}
+
+// Per-chunk expert histogram.  4 waves per block, one chunk per wave.
+__global__ __launch_bounds__(256) void route_count_kernel(const int* __restrict__ idx, int R, int E, int nchunks,
+                                                          int* __restrict__ chunk_cnt) {
+  extern __shared__ int hist[];  // [4][E]
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int chunk = blockIdx.x * 4 + w;
+  int* hw = hist + w * E;
+  for (int e = lane; e < E; e += 64) hw[e] = 0;
+  __syncthreads();
+  if (chunk < nchunks) {
+#pragma unroll
+    for (int r = 0; r < kChunk / 64; ++r) {
+      long i = (long)chunk * kChunk + r * 64 + lane;
+      if (i < R) atomicAdd(&hw[idx[i]], 1);
+    }
+  }
+  __syncthreads();
+  if (chunk < nchunks)
+    for (int e = lane; e < E; e += 64) chunk_cnt[(long)chunk * E + e] = hw[e];
+}
+
+// One block of 1024 threads.  Thread e: exclusive scan of its expert's counts
+// over chunks, then the expert offsets and the 32-padded offsets; finally the
+// chunk bases become absolute row positions.
+__global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ chunk_cnt, int nchunks, int E,
+                                                          int* __restrict__ counts, int* __restrict__ offsets,
+                                                          int* __restrict__ off32) {
+  __shared__ int tmp[1024];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E) {
+    int c = 0;
+    for (; c + 8 <= nchunks; c += 8) {
+      int vals[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) vals[u] = chunk_cnt[(long)(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        chunk_cnt[(long)(c + u) * E + e] = tot;
+        tot += vals[u];
+      }
+    }
+    for (; c < nchunks; ++c) {
+      int val = chunk_cnt[(long)c * E + e];
+      chunk_cnt[(long)c * E + e] = tot;
+      tot += val;
+    }
+  }
+  int total, total32;
+  int off = block_excl_scan_1024(e < E ? tot : 0, tmp, &total);
+  int t32 = (tot + 31) & ~31;
+  int o32 = block_excl_scan_1024(e < E ? t32 : 0, tmp, &total32);
+  if (e < E) {
+    counts[e] = tot;
+    offsets[e] = off;
+    if (off32) off32[e] = o32;
+    for (int c = 0; c < nchunks; ++c) chunk_cnt[(long)c * E + e] += off;
+  }
+  if (e == 0) {
+    offsets[E] = total;
+    if (off32) off32[E] = total32;
+  }
+}
+
+// One wave per chunk.  Entries are visited in flattened (t, j) order, 64 at a
+// time; the rank among equal experts is the popcount of the lower lanes in
+// that expert's match mask, plus the running count carried between rounds.
+__global__ __launch_bounds__(64) void route_rank_kernel(const int* __restrict__ idx, int R, int E,
+                                                        const int* __restrict__ chunk_base, int* __restrict__ pos,
+                                                        int* __restrict__ src) {
+  extern __shared__ unsigned long long lds_rank[];  // masks [E] then run [E] (int)
+  unsigned long long* mask = lds_rank;
+  int* run = (int*)(lds_rank + E);
+  const int lane = threadIdx.x;
+  const int chunk = blockIdx.x;
+  for (int e = lane; e < E; e += 64) {
+    mask[e] = 0ull;
+    run[e] = chunk_base[(long)chunk * E + e];
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int r = 0; r < kChunk / 64; ++r) {
+    long i = (long)chunk * kChunk + r * 64 + lane;
+    bool valid = i < R;
+    int e = valid ? idx[i] : 0;
+    if (valid) atomicOr(&mask[e], 1ull << lane);
+    __syncthreads();
+    unsigned long long mm = valid ? mask[e] : 0ull;
+    int rank = __popcll(mm & ((1ull << lane) - 1ull));
+    int p = valid ? run[e] + rank : 0;
+    __syncthreads();
+    if (valid && rank == 0) {
+      run[e] += __popcll(mm);
+      mask[e] = 0ull;
+    }
+    __syncthreads();
+    if (valid) {
+      pos[i] = p;
+      src[p] = (int)i;
+    }
+  }
+}
+
+size_t route_ws_bytes(int T, int E, int k) {
+  long R = (long)T * k;
+  long nchunks = (R + kChunk - 1) / kChunk;
+  return (size_t)(nchunks * E * sizeof(int));
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, const int* forced, float* probs, int* idx,
+                        float* w, int* counts, int* offsets, int* pos, int* src, int* off32, int* err_flag,
+                        void* ws, hipStream_t s) {
+  long R = (long)T * k;
+  int nchunks = (int)((R + kChunk - 1) / kChunk);
+  int* chunk_cnt = (int*)ws;
+  if (R == 0) {  // no tokens: counts and offsets are all zero
+    route_scan_kernel<<<1, 1024, 0, s>>>(chunk_cnt, 0, E, counts, offsets, off32);
+    return hipGetLastError();
+  }
+  dim3 g1((T + 3) / 4);
+  if (E <= 64)
+    route_topk_kernel<1><<<g1, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
+  else if (E <= 128)
+    route_topk_kernel<2><<<g1, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
+  else if (E <= 256)
+    route_topk_kernel<4><<<g1, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
+  else if (E <= 512)
+    route_topk_kernel<8><<<g1, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
+  else
+    route_topk_kernel<16><<<g1, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
+  route_count_kernel<<<(nchunks + 3) / 4, 256, 4 * E * sizeof(int), s>>>(idx, (int)R, E, nchunks, chunk_cnt);
+  route_scan_kernel<<<1, 1024, 0, s>>>(chunk_cnt, nchunks, E, counts, offsets, off32);
+  route_rank_kernel<<<nchunks, 64, E * (sizeof(unsigned long long) + sizeof(int)), s>>>(idx, (int)R, E, chunk_cnt,
+                                                                                        pos, src);
+  return hipGetLastError();
+}
+
+}  // namespace trg
