@@ -87,6 +87,20 @@ def cpu_baseline(cfg, mode, sample_T, min_seconds=10.0):
             "seconds_per_run": el}
 
 
+def copy_probe(nbytes=1 << 30, reps=5):
+    """A plain copy kernel of known size: each launch reads and writes exactly
+    nbytes.  Profiled with the FETCH_SIZE / WRITE_SIZE counters it gives the
+    factor that turns those counters into HBM bytes."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +110,8 @@ def main():
     ap.add_argument("--mode", default=None, help="router | uniform | zipf (default: the config's first mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
 
     if a.gpus != 1:
@@ -108,6 +124,10 @@ def main():
 
     from token_routing_grouped_amd import _abi, configs, inputs
     from token_routing_grouped_amd.layer import MoELayerGPU
+
+    if a.copy_probe:
+        copy_probe()
+        return
 
     cfg = configs.get(a.config)
     mode = a.mode or cfg.modes[0]
