@@ -163,6 +163,7 @@ moe_status_t moe_unpermute_sum(const void* dxp, const int32_t* pos, int T, int d
  *   epilogue; g, u, hbuf stored in dt for the backward),
  * and a second launch yp = hbuf w2[e]^T.  The tile map is derived on the
  * device from offsets.  ws: moe_grouped_gemm_workspace_size() bytes.
+ * bf16 needs d and h to be multiples of 64 and R * max(d, 2h) * 2 < 2^31.
  */
 size_t moe_grouped_gemm_workspace_size(int E, int R, int d, int h);
 moe_status_t moe_grouped_gemm_fwd(const void* xp, const void* w1, const void* w3, const void* w2,

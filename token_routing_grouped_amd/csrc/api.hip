@@ -292,8 +292,12 @@ static moe_status_t check_ggemm_dims(const char* fn, int E, int R, int d, int h,
   if (R < 0) return fail(MOE_ERR_INVALID_ARG, "%s: R must be >= 0", fn);
   TRY(check_row(fn, "d", d, dt));
   TRY(check_row(fn, "h", h, dt));
-  if (dt == MOE_BF16 && (h % 64 != 0 || d % 8 != 0))
-    return fail(MOE_ERR_INVALID_ARG, "%s: bf16 path needs h %% 64 == 0 and d %% 8 == 0", fn);
+  if (dt == MOE_BF16 && (h % 64 != 0 || d % 64 != 0))
+    return fail(MOE_ERR_INVALID_ARG, "%s: bf16 path needs d %% 64 == 0 and h %% 64 == 0", fn);
+  // operand byte offsets inside one grouped GEMM are 32-bit
+  const long widest = 2L * h > d ? 2L * h : (long)d;
+  if ((long)R * widest * esize(dt) >= (1L << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: R * max(d, 2h) * element size must be < 2^31 bytes", fn);
   return MOE_OK;
 }
 

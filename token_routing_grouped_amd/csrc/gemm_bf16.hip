@@ -1,7 +1,7 @@
-// Grouped bf16 GEMMs on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), fp32
-// accumulation.  One launch covers every expert: the many small per-expert
-// products are batched into a single grouped GEMM call (Olmo-core 3 overview,
-// "Routing and compute optimisation").
+// Register-staged bf16 GEMMs on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16),
+// fp32 accumulation, used for the router's dense products when the expert count
+// makes them real GEMMs (logits, dWr with a fixed-order split-K, dx).  The
+// grouped expert GEMMs live in ggemm.hip.
 //
 // Design (CDNA4-first):
 //  * 256 threads = 4 waves in a WM x WN grid; block tile BM x BN, K step 64.
@@ -401,22 +401,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-// Per-expert M-tile prefix for BM = 64, 128, 256 from the expert offsets.
-__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict__ offsets, int E,
-                                                           int* __restrict__ tile_off) {
-  __shared__ int tmp[1024];
-  const int e = threadIdx.x;
-  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-#pragma unroll 1
-  for (int b = 0; b < 3; ++b) {
-    const int bm = 64 << b;
-    int total;
-    const int ex = block_excl_scan_1024((c + bm - 1) / bm, tmp, &total);
-    if (e < E) tile_off[b * (E + 1) + e] = ex;
-    if (e == 0) tile_off[b * (E + 1) + E] = total;
-  }
-}
-
 // Fixed-order sum of split-K partials: out[i] = sum_s part[s][i].
 __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const float* __restrict__ part, int splits, long n,
                                                                  uint16_t* __restrict__ out) {
@@ -437,100 +421,6 @@ static void run(const char* name, const GemmArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return;
   ProfScope ps(name, s);
   gemm_bf16_kernel<BM, BN, WM, WN, AKC, BKC, MODE, BSEL, CSEL, EPI><<<grid, 256, 0, s>>>(a);
-}
-
-size_t ggemm_ws_bytes(int E, int R, int d, int h) {
-  (void)R; (void)d; (void)h;
-  return (size_t)(3 * (E + 1)) * sizeof(int);
-}
-
-hipError_t launch_ggemm_fwd(const void* xp, const void* w1, const void* w3, const void* w2, const int* offsets,
-                            int E, int R, int d, int h, bool bf16, void* g, void* u, void* hb, void* yp, void* ws,
-                            hipStream_t s) {
-  if (!bf16)
-    return launch_ggemm_fwd_f32((const float*)xp, (const float*)w1, (const float*)w3, (const float*)w2, offsets, E,
-                                R, d, h, (float*)g, (float*)u, (float*)hb, (float*)yp, s);
-  int* tile_off = (int*)ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off);
-  const int* to256 = tile_off + 2 * (E + 1);
-  const int mt_max = cdiv(R, 256) + E;
-  {  // up projection with the SwiGLU epilogue: N covers W1 and W3 rows
-    GemmArgs a{};
-    a.A = (const uint16_t*)xp; a.lda = d;
-    a.B = (const uint16_t*)w1; a.B2 = (const uint16_t*)w3; a.ldb = d; a.b_es = (long)h * d;
-    a.C = g; a.C2 = u; a.C3 = hb; a.ldc = h;
-    a.N = 2 * h; a.K = d; a.split = h;
-    a.offsets = offsets; a.tile_off = to256; a.E = E;
-    a.tiles_n = cdiv(2L * h, 256);
-    run<256, 256, 2, 2, true, true, RAGGED_M, BSEL_GLU, CSEL_NONE, EPI_SWIGLU_FWD>("ggemm_up_swiglu", a, mt_max * a.tiles_n, s);
-  }
-  {  // down projection
-    GemmArgs a{};
-    a.A = (const uint16_t*)hb; a.lda = h;
-    a.B = (const uint16_t*)w2; a.ldb = h; a.b_es = (long)d * h;
-    a.C = yp; a.ldc = d;
-    a.N = d; a.K = h;
-    a.offsets = offsets; a.tile_off = to256; a.E = E;
-    a.tiles_n = cdiv(d, 256);
-    run<256, 256, 2, 2, true, true, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_down", a, mt_max * a.tiles_n, s);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, const void* u, const void* hb,
-                            const void* w1, const void* w3, const void* w2, const int* offsets, int E, int R, int d,
-                            int h, bool bf16, void* dgu, void* dxp, void* dw1, void* dw3, void* dw2, void* ws,
-                            hipStream_t s) {
-  if (!bf16)
-    return launch_ggemm_bwd_f32((const float*)dyp, (const float*)xp, (const float*)g, (const float*)u,
-                                (const float*)hb, (const float*)w1, (const float*)w3, (const float*)w2, offsets, E,
-                                R, d, h, (float*)dgu, (float*)dxp, (float*)dw1, (float*)dw3, (float*)dw2, s);
-  int* tile_off = (int*)ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off);
-  const int* to256 = tile_off + 2 * (E + 1);
-  const int mt_max = cdiv(R, 256) + E;
-  {  // dgrad down + SwiGLU backward: dH = dYp W2[e] -> dG, dU
-    GemmArgs a{};
-    a.A = (const uint16_t*)dyp; a.lda = d;
-    a.B = (const uint16_t*)w2; a.ldb = h; a.b_es = (long)d * h;
-    a.C = dgu; a.ldc = 2L * h;
-    a.G = (const uint16_t*)g; a.U = (const uint16_t*)u; a.ldgu = h;
-    a.N = h; a.K = d; a.split = h;
-    a.offsets = offsets; a.tile_off = to256; a.E = E;
-    a.tiles_n = cdiv(h, 256);
-    run<256, 256, 2, 2, true, false, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_SWIGLU_BWD>("ggemm_dgrad_down_swiglu", a, mt_max * a.tiles_n, s);
-  }
-  {  // wgrad down: dW2[e] = dYp_e^T H_e
-    GemmArgs a{};
-    a.A = (const uint16_t*)dyp; a.lda = d;
-    a.B = (const uint16_t*)hb; a.ldb = h;
-    a.C = dw2; a.ldc = h; a.c_es = (long)d * h;
-    a.M = d; a.N = h;
-    a.offsets = offsets; a.E = E;
-    a.tiles_m = cdiv(d, 256); a.tiles_n = cdiv(h, 256);
-    run<256, 256, 2, 2, false, false, RAGGED_K, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_wgrad_down", a, E * a.tiles_m * a.tiles_n, s);
-  }
-  {  // dgrad up: dXp = [dG | dU] [W1; W3]
-    GemmArgs a{};
-    a.A = (const uint16_t*)dgu; a.lda = 2L * h;
-    a.B = (const uint16_t*)w1; a.B2 = (const uint16_t*)w3; a.ldb = d; a.b_es = (long)h * d;
-    a.C = dxp; a.ldc = d;
-    a.N = d; a.K = 2 * h; a.split = h;
-    a.offsets = offsets; a.tile_off = to256; a.E = E;
-    a.tiles_n = cdiv(d, 256);
-    run<256, 256, 2, 2, true, false, RAGGED_M, BSEL_KSPLIT, CSEL_NONE, EPI_BF16>("ggemm_dgrad_up", a, mt_max * a.tiles_n, s);
-  }
-  {  // wgrad up: [dW1; dW3][e] = [dG | dU]_e^T Xp_e
-    GemmArgs a{};
-    a.A = (const uint16_t*)dgu; a.lda = 2L * h;
-    a.B = (const uint16_t*)xp; a.ldb = d;
-    a.C = dw1; a.C2 = dw3; a.ldc = d; a.c_es = (long)h * d;
-    a.M = 2 * h; a.N = d; a.split = h;
-    a.offsets = offsets; a.E = E;
-    a.tiles_m = cdiv(2L * h, 256); a.tiles_n = cdiv(d, 256);
-    run<256, 256, 2, 2, false, false, RAGGED_K, BSEL_NONE, CSEL_MSPLIT, EPI_BF16>("ggemm_wgrad_up", a, E * a.tiles_m * a.tiles_n, s);
-  }
-  return hipGetLastError();
 }
 
 // ---------------- router GEMMs on the matrix cores (E >= 64) ----------------

@@ -1,0 +1,608 @@
+// Grouped bf16 GEMMs of the expert SwiGLU FFNs on gfx950 matrix cores
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  One launch per GEMM kind
+// covers every expert: the many small per-expert products are batched into a
+// single grouped GEMM call (Olmo-core 3 overview, "Routing and compute
+// optimisation").
+//
+// CDNA4 design:
+//  * Persistent, XCD-aware scheduler.  The grid is one workgroup per compute
+//    unit.  The logical tile list (derived on the device from the expert
+//    offsets, so the host never waits for routing) is cut into eight
+//    contiguous ranges, one per XCD (workgroup i runs on XCD i % 8), and the
+//    workgroups of an XCD walk their range together.  At any moment an XCD's
+//    32 CUs work on neighbouring tiles that share A rows and B columns, so the
+//    XCD's own L2 serves the re-reads.
+//  * 512 threads = 8 waves in a 2 x 4 grid (two waves per SIMD, so one hides
+//    the other's LDS latency); block tile BM x 256, K step 64.
+//  * Operands move HBM -> LDS with buffer_load_dwordx4 ... lds (no register
+//    staging).  A buffer resource bounds every operand: reads past the end of
+//    an operand return zero, which also zero-fills the ragged K tail of the
+//    weight-gradient GEMMs.
+//  * LDS holds two stages.  An operand stored K-contiguous lands as
+//    [rows][64] bf16 (128-byte rows) with 16-byte chunks XOR-swizzled by the
+//    row pair (conflict-free for 64 banks); fragments are read with
+//    ds_read_b128.  An operand stored
+//    MN-contiguous (dgrad weights, both wgrad operands) lands as [64][BMN]
+//    bf16 with chunks XOR-swizzled by the k row and is read with the gfx950
+//    transpose read ds_read_b64_tr_b16, which hands each lane 4 k-consecutive
+//    values of its column.  Either way every MFMA sees the same fragments.
+//  * Fragments are double-buffered in registers: the reads for the next
+//    16-wide k slice are in flight while the current slice's MFMAs issue; the
+//    next K tile's HBM loads are in flight during the whole current tile.
+//  * The MFMA is issued as (B fragment, A fragment): each lane then owns 4
+//    consecutive output columns of one row.
+//  * Epilogues: bf16 store, SwiGLU forward (G, U, H), SwiGLU backward (dG, dU
+//    from dH, G, U).
+#include "common.h"
+#include "kernels.h"
+#include "prof.h"
+
+namespace trg {
+namespace gg {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+enum Mode { RAGGED_M = 1, RAGGED_K = 2 };
+enum BSel { BSEL_NONE = 0, BSEL_GLU = 1, BSEL_KSPLIT = 2 };
+enum CSel { CSEL_NONE = 0, CSEL_MSPLIT = 1 };
+enum Epi { EPI_BF16 = 0, EPI_SWIGLU_FWD = 2, EPI_SWIGLU_BWD = 3 };
+
+constexpr int BK = 64;
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
+
+struct Args {
+  // Operand X[mn][k]: K-contiguous -> X[mn*ld + k]; MN-contiguous -> X[k*ld + mn]
+  const uint16_t* A;
+  long lda;
+  const uint16_t* B;
+  const uint16_t* B2;  // BSEL_GLU: W3 next to W1;  BSEL_KSPLIT: second K half
+  long ldb, b_es;      // b_es: per-expert element stride of B
+  void* C;
+  void* C2;  // CSEL_MSPLIT: rows >= split;  SWIGLU_FWD: U
+  void* C3;  // SWIGLU_FWD: H
+  long ldc, c_es;
+  const uint16_t* G;  // SWIGLU_BWD inputs
+  const uint16_t* U;
+  long ldgu;
+  int M, N, K;  // RAGGED_K: M x N output per expert;  RAGGED_M: N, K
+  int split;    // GLU: h;  KSPLIT: first K half;  MSPLIT: first M half
+  const int* offsets;
+  const int* tile_off;  // RAGGED_M: per-expert prefix of BM row tiles
+  int E, R;
+  int tiles_m, tiles_n;
+};
+
+TRG_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  const unsigned n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFL ? 0xFFFFFFFFu : (unsigned)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcFlags);
+}
+
+TRG_DEV void lds_load16(__amdgpu_buffer_rsrc_t rs, char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+}
+
+// K-contiguous operand: BMN rows of 64 bf16 (128-byte rows).  gfx950's LDS
+// has 64 banks and serves ds_read_b128 16 lanes at a time; a fragment read
+// hands those 16 lanes 16 consecutive rows at one logical chunk, so the 16-byte
+// chunk slot of row r is swizzled as p = c ^ ((r >> 1) & 7): two rows share a
+// 256-byte bank window and the XOR spreads the 8 row pairs over all 8 chunk
+// positions.  Wave w fills 1 KiB blocks [w*P, (w+1)*P), P = BMN/8 / waves;
+// block b holds rows 8b..8b+7.  The lane's part of the byte offset depends only on the
+// block's parity.  row8(b) -> (resource, first row of block b inside that
+// resource).
+template <int BMN, int NW, class Row8>
+TRG_DEV void load_kc(char* dst, int wave, const int (&lane_off)[2], int kbyte, int ld_bytes, Row8 row8) {
+  constexpr int PER = BMN / 8 / NW;  // 1 KiB blocks per wave
+  static_assert(PER >= 1 && (BMN / 8) % NW == 0, "blocks per wave");
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int blk = wave * PER + i;
+    int r0;
+    const __amdgpu_buffer_rsrc_t rs = row8(blk * 8, r0);
+    lds_load16(rs, dst + blk * 1024, lane_off[blk & 1] + r0 * ld_bytes + kbyte);
+  }
+}
+
+TRG_DEV int kc_lane_off(int lane, int parity, int ld_bytes) {
+  const int l8 = lane >> 3;  // row inside the block
+  const int sw = (parity << 2) | (l8 >> 1);
+  return l8 * ld_bytes + (((lane & 7) ^ sw) << 4);
+}
+
+// MN-contiguous operand: 64 k rows of BMN bf16 (row = BMN*2 bytes).  LDS
+// chunk slot p of k row kr receives global chunk p ^ ((kr & 3) << 2).  A 1 KiB
+// block covers 1024/ROWB k rows; the lane's offset inside a block depends only
+// on the block's parity (BMN = 256) or not at all (BMN = 128).
+template <int BMN>
+TRG_DEV int mnc_lane_off(int lane, int parity, int ld_bytes) {
+  constexpr int ROWB = BMN * 2;
+  const int off = parity * 1024 + lane * 16;
+  const int kr = off / ROWB;
+  const int c = ((off % ROWB) >> 4) ^ ((kr & 3) << 2);
+  return (kr - parity * (1024 / ROWB)) * ld_bytes + c * 16;
+}
+
+template <int BMN, int NW>
+TRG_DEV void load_mnc(char* dst, int wave, const int (&lane_off)[2], __amdgpu_buffer_rsrc_t rs, int krow0,
+                      int ld_bytes) {
+  constexpr int ROWB = BMN * 2;
+  constexpr int NBLK = 64 * ROWB / 1024;
+  constexpr int RPB = 1024 / ROWB;  // k rows per block
+  constexpr int PER = NBLK / NW;
+  static_assert(PER >= 1 && NBLK % NW == 0, "blocks per wave");
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int blk = wave * PER + i;
+    lds_load16(rs, dst + blk * 1024, lane_off[blk & 1] + (krow0 + blk * RPB) * ld_bytes);
+  }
+}
+
+// Fragment of 8 k-consecutive values for MFMA lane `lane` (its row / column
+// is base + (lane & 31), its k range kk*16 + (lane >> 5)*8 + [0, 8)).
+TRG_DEV bf16x8_t frag_kc(const char* s, int base, int kk, int lane) {
+  const int row = base + (lane & 31);
+  const int c = kk * 2 + (lane >> 5);
+  return *(const bf16x8_t*)(s + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+}
+
+template <int BMN>
+TRG_DEV bf16x8_t frag_mnc(const char* s, int base, int kk, int lane) {
+  constexpr int ROWB = BMN * 2;
+  // Transpose read: the 16 lanes of a group load a 4 (k) x 16 (column) block,
+  // lane s of the group the 4 values of row s/4 starting at column 4*(s%4);
+  // after the read lane s holds column s's 4 values, k ascending.
+  const int g = lane >> 4, s16 = lane & 15;
+  const int col = base + (g & 1) * 16 + (s16 & 3) * 4;
+  const int kr = kk * 16 + (g >> 1) * 8 + (s16 >> 2);
+  const int sw = (kr & 3) << 2;
+  const int cb = ((col >> 3) ^ sw) << 4;
+  const int within = (col & 7) * 2;
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s + kr * ROWB + cb + within));
+  const bf16x4_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s + (kr + 4) * ROWB + cb + within));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int BMN, bool KC>
+TRG_DEV bf16x8_t frag(const char* s, int base, int kk, int lane) {
+  if constexpr (KC) return frag_kc(s, base, kk, lane);
+  else return frag_mnc<BMN>(s, base, kk, lane);
+}
+
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int MODE, int BSEL, int CSEL, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int SA = BM * 128, SB = BN * 128;  // bytes per stage and operand
+  constexpr int STAGE = SA + SB;
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "tile");
+  static_assert(BSEL != BSEL_GLU || (TN % 2 == 0), "GLU pairs subtiles");
+  static_assert(MODE == RAGGED_M || (!AKC && !BKC), "weight gradients read both operands MN-contiguous");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  int total;
+  if constexpr (MODE == RAGGED_M) total = g.tile_off[g.E] * g.tiles_n;
+  else total = g.E * g.tiles_m * g.tiles_n;
+  const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+  const int per = (total + 7) >> 3;
+  const int t_begin = xcd * per, t_end = min(total, t_begin + per);
+
+  for (int t = t_begin + lb; t < t_end; t += nbx) {
+    // ---------------- tile decode ----------------
+    int e, m0, m_end, n0, k0, k_end;
+    if constexpr (MODE == RAGGED_M) {
+      const int mtg = t / g.tiles_n, nt = t - (t / g.tiles_n) * g.tiles_n;
+      int lo = 0, hi = g.E;  // last expert with tile_off[e] <= mtg
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (g.tile_off[mid] <= mtg) lo = mid; else hi = mid;
+      }
+      e = lo;
+      m0 = g.offsets[e] + (mtg - g.tile_off[e]) * BM;
+      m_end = g.offsets[e + 1];
+      n0 = nt * BN;
+      k0 = 0;
+      k_end = g.K;
+    } else {
+      const int per_e = g.tiles_m * g.tiles_n;
+      e = t / per_e;
+      const int r = t - e * per_e;
+      const int mt = r / g.tiles_n, nt = r - mt * g.tiles_n;
+      m0 = mt * BM;
+      m_end = g.M;
+      n0 = nt * BN;
+      k0 = g.offsets[e];
+      k_end = g.offsets[e + 1];
+    }
+
+    // ---------------- operand resources ----------------
+    __amdgpu_buffer_rsrc_t rsA, rsB, rsB2;
+    const long a_ldb = g.lda * 2, b_ldb = g.ldb * 2;
+    if constexpr (MODE == RAGGED_M) {
+      // A: routed rows from m0 on, K-contiguous
+      rsA = make_rsrc(g.A + (long)m0 * g.lda, (long)(g.R - m0) * a_ldb);
+      if constexpr (BSEL == BSEL_GLU) {
+        const long hh0 = n0 / 2;
+        rsB = make_rsrc(g.B + (long)e * g.b_es + hh0 * g.ldb, (g.split - hh0) * b_ldb);
+        rsB2 = make_rsrc(g.B2 + (long)e * g.b_es + hh0 * g.ldb, (g.split - hh0) * b_ldb);
+      } else if constexpr (BKC) {
+        rsB = make_rsrc(g.B + (long)e * g.b_es + (long)n0 * g.ldb, (long)(g.N - n0) * b_ldb);
+        rsB2 = rsB;
+      } else {
+        // MN-contiguous B: X[k][n] with the expert's block of b_es elements
+        rsB = make_rsrc(g.B + (long)e * g.b_es + n0, (g.b_es - n0) * 2);
+        rsB2 = (BSEL == BSEL_KSPLIT) ? make_rsrc(g.B2 + (long)e * g.b_es + n0, (g.b_es - n0) * 2) : rsB;
+      }
+    } else {
+      // weight gradients: K = the expert's rows; rows past k_end read as zero
+      const long nrows = k_end - k0;
+      rsA = make_rsrc(g.A + (long)k0 * g.lda + m0, nrows * a_ldb - (long)m0 * 2);
+      rsB = make_rsrc(g.B + (long)k0 * g.ldb + n0, nrows * b_ldb - (long)n0 * 2);
+      rsB2 = rsB;
+    }
+
+    int a_lane[2], b_lane[2];
+    if constexpr (AKC) {
+      a_lane[0] = kc_lane_off(lane, 0, (int)a_ldb);
+      a_lane[1] = kc_lane_off(lane, 1, (int)a_ldb);
+    } else {
+      a_lane[0] = mnc_lane_off<BM>(lane, 0, (int)a_ldb);
+      a_lane[1] = mnc_lane_off<BM>(lane, 1, (int)a_ldb);
+    }
+    if constexpr (BKC) {
+      b_lane[0] = kc_lane_off(lane, 0, (int)b_ldb);
+      b_lane[1] = kc_lane_off(lane, 1, (int)b_ldb);
+    } else {
+      b_lane[0] = mnc_lane_off<BN>(lane, 0, (int)b_ldb);
+      b_lane[1] = mnc_lane_off<BN>(lane, 1, (int)b_ldb);
+    }
+    auto issue = [&](int kt, int stage) {  // kt: K offset relative to k0
+      char* sA = smem + stage * STAGE;
+      char* sB = sA + SA;
+      if constexpr (AKC) {
+        load_kc<BM, NW>(sA, wave, a_lane, kt * 2, (int)a_ldb, [&](int r8, int& r0) {
+          r0 = r8;
+          return rsA;
+        });
+      } else {
+        load_mnc<BM, NW>(sA, wave, a_lane, rsA, kt, (int)a_ldb);
+      }
+      if constexpr (BKC) {
+        if constexpr (BSEL == BSEL_GLU) {
+          load_kc<BN, NW>(sB, wave, b_lane, kt * 2, (int)b_ldb, [&](int r8, int& r0) {
+            // LDS rows of wave column `part`: first WTN/2 from W1, next WTN/2
+            // from W3, both for the same hidden units
+            const int p = r8 % WTN;
+            r0 = (r8 / WTN) * (WTN / 2) + (p % (WTN / 2));
+            return (p >= WTN / 2) ? rsB2 : rsB;
+          });
+        } else {
+          load_kc<BN, NW>(sB, wave, b_lane, kt * 2, (int)b_ldb, [&](int r8, int& r0) {
+            r0 = r8;
+            return rsB;
+          });
+        }
+      } else {
+        if constexpr (BSEL == BSEL_KSPLIT) {
+          if (kt >= g.split) load_mnc<BN, NW>(sB, wave, b_lane, rsB2, kt - g.split, (int)b_ldb);
+          else load_mnc<BN, NW>(sB, wave, b_lane, rsB, kt, (int)b_ldb);
+        } else {
+          load_mnc<BN, NW>(sB, wave, b_lane, rsB, kt, (int)b_ldb);
+        }
+      }
+    };
+
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = k_end > k0 ? (k_end - k0 + BK - 1) / BK : 0;
+    __syncthreads();  // the previous tile's waves are done with both stages
+    if (nk > 0) issue(0, 0);
+    for (int it = 0; it < nk; ++it) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // stage it&1 is complete; stage (it+1)&1 is free
+      if (it + 1 < nk) issue((it + 1) * BK, (it + 1) & 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, (BM + BN) / 8 / NW, 0);  // HBM->LDS loads first
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);  // slice-0 fragments
+      const char* sA = smem + (it & 1) * STAGE;
+      const char* sB = sA + SA;
+      bf16x8_t af[2][TM], bfr[2][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[0][i] = frag<BM, AKC>(sA, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[0][j] = frag<BN, BKC>(sB, wn * WTN + j * 32, 0, lane);
+      static_for<BK / 16>([&](auto KK) {
+        constexpr int kk = decltype(KK)::value;
+        constexpr int cur = kk & 1;
+        if constexpr (kk + 1 < BK / 16) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = frag<BM, AKC>(sA, wm * WTM + i * 32, kk + 1, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bfr[cur ^ 1][j] = frag<BN, BKC>(sB, wn * WTN + j * 32, kk + 1, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+        // Issue order: the next slice's LDS reads between this slice's MFMAs.
+        constexpr int NR = (TM + TN) * ((AKC ? 1 : 2) + (BKC ? 1 : 2)) / 2;  // DS reads per slice (approx.)
+        if constexpr (kk + 1 < BK / 16) {
+          static_for<(NR < TM * TN ? NR : TM * TN)>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+          });
+          if constexpr (NR < TM * TN) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - NR, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+        }
+      });
+    }
+
+    // ---------------- epilogue ----------------
+    // Lane (lrow, lgrp) owns row ... + lrow and 4 consecutive columns per
+    // group q: ... + q*8 + lgrp + {0..3}.
+    const int lrow = lane & 31, lgrp = (lane >> 5) * 4;
+    if constexpr (EPI == EPI_SWIGLU_FWD) {
+      uint16_t* Gp = (uint16_t*)g.C;
+      uint16_t* Up = (uint16_t*)g.C2;
+      uint16_t* Hp = (uint16_t*)g.C3;
+      static_for<TM>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const int m = m0 + wm * WTM + i * 32 + lrow;
+        if (m < m_end) {
+          static_for<TN / 2>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            static_for<4>([&](auto Q) {
+              constexpr int q = decltype(Q)::value;
+              const int hh = n0 / 2 + wn * (WTN / 2) + j * 32 + q * 8 + lgrp;
+              if (hh < g.split) {
+                float gv[4], uv[4], hv[4];
+                static_for<4>([&](auto Rr) {
+                  constexpr int r = decltype(Rr)::value;
+                  gv[r] = acc[i][j][q * 4 + r];
+                  uv[r] = acc[i][j + TN / 2][q * 4 + r];
+                  hv[r] = silu_f(gv[r]) * uv[r];
+                });
+                const long o = (long)m * g.ldc + hh;
+                *(uint2*)(Gp + o) = make_uint2(pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3]));
+                *(uint2*)(Up + o) = make_uint2(pack_bf2(uv[0], uv[1]), pack_bf2(uv[2], uv[3]));
+                *(uint2*)(Hp + o) = make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
+              }
+            });
+          });
+        }
+      });
+    } else {
+      static_for<TM>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const int m = m0 + wm * WTM + i * 32 + lrow;
+        if (m < m_end) {
+          void* Cb = g.C;
+          int mrow0 = 0;
+          if constexpr (CSEL == CSEL_MSPLIT) {
+            if (m >= g.split) {
+              Cb = g.C2;
+              mrow0 = g.split;
+            }
+          }
+          static_for<TN>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            static_for<4>([&](auto Q) {
+              constexpr int q = decltype(Q)::value;
+              const int n = n0 + wn * WTN + j * 32 + q * 8 + lgrp;
+              if (n < g.N) {
+                const float v0 = acc[i][j][q * 4 + 0], v1 = acc[i][j][q * 4 + 1];
+                const float v2 = acc[i][j][q * 4 + 2], v3 = acc[i][j][q * 4 + 3];
+                if constexpr (EPI == EPI_BF16) {
+                  const long o = (long)e * g.c_es + (long)(m - mrow0) * g.ldc + n;
+                  *(uint2*)((uint16_t*)Cb + o) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+                } else {
+                  // SWIGLU_BWD: (v0..v3) = dH[m][n..n+3]; n indexes h
+                  const long gu = (long)m * g.ldgu + n;
+                  const uint2 gw = *(const uint2*)(g.G + gu);
+                  const uint2 uw = *(const uint2*)(g.U + gu);
+                  const float vv[4] = {v0, v1, v2, v3};
+                  const float gg[4] = {bf_lo(gw.x), bf_hi(gw.x), bf_lo(gw.y), bf_hi(gw.y)};
+                  const float uu[4] = {bf_lo(uw.x), bf_hi(uw.x), bf_lo(uw.y), bf_hi(uw.y)};
+                  float dg[4], du[4];
+                  static_for<4>([&](auto Rr) {
+                    constexpr int r = decltype(Rr)::value;
+                    const float s = sigmoid_f(gg[r]);
+                    du[r] = vv[r] * gg[r] * s;
+                    dg[r] = vv[r] * uu[r] * s * (1.0f + gg[r] * (1.0f - s));
+                  });
+                  uint16_t* D = (uint16_t*)Cb + (long)m * g.ldc;
+                  *(uint2*)(D + n) = make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+                  *(uint2*)(D + g.split + n) = make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+                }
+              }
+            });
+          });
+        }
+      });
+    }
+  }
+}
+
+// Per-expert row-tile prefix for BM = 128 and 256 from the expert offsets.
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict__ offsets, int E,
+                                                           int* __restrict__ tile_off) {
+  __shared__ int tmp[1024];
+  const int e = threadIdx.x;
+  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+#pragma unroll 1
+  for (int b = 0; b < 2; ++b) {
+    const int bm = 128 << b;
+    int total;
+    const int ex = block_excl_scan_1024((c + bm - 1) / bm, tmp, &total);
+    if (e < E) tile_off[b * (E + 1) + e] = ex;
+    if (e == 0) tile_off[b * (E + 1) + E] = total;
+  }
+}
+
+static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+struct DevInfo {
+  int cus = 0;
+};
+static DevInfo g_dev[64];
+
+static int grid_for(int tiles) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (g_dev[dev].cus == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_dev[dev].cus = n;
+  }
+  int grid = (g_dev[dev].cus + 7) / 8 * 8;  // a multiple of 8: whole XCD groups
+  const int need = (tiles + 7) / 8 * 8;
+  if (need < grid) grid = need;
+  return grid < 8 ? 8 : grid;
+}
+
+// 8 waves (two per SIMD) per 256-wide tile: while one wave of a SIMD waits
+// on LDS the other issues MFMAs.
+template <int BM, int BN, bool AKC, bool BKC, int MODE, int BSEL, int CSEL, int EPI>
+static void run(const char* name, const Args& a, int max_tiles, hipStream_t s) {
+  if (max_tiles <= 0) return;
+  ProfScope ps(name, s);
+  constexpr int WM = 2, WN = (BN >= 256 ? 4 : 2);
+  ggemm_kernel<BM, BN, WM, WN, AKC, BKC, MODE, BSEL, CSEL, EPI><<<grid_for(max_tiles), 64 * WM * WN, 0, s>>>(a);
+}
+
+// Row tile of the ragged-M GEMMs: 256 unless experts are small on average.
+static inline bool small_rows(int E, int R) { return R < 192L * E; }
+
+}  // namespace gg
+
+size_t ggemm_ws_bytes(int E, int R, int d, int h) {
+  (void)R; (void)d; (void)h;
+  return (size_t)(2 * (E + 1)) * sizeof(int);
+}
+
+using namespace gg;
+
+template <int BM>
+static void fwd_bm(const void* xp, const void* w1, const void* w3, const void* w2, const int* offsets, int E, int R,
+                   int d, int h, void* gq, void* u, void* hb, void* yp, const int* tile_off, hipStream_t s) {
+  const int mt_max = cdiv(R, BM) + E;
+  {  // up projection with the SwiGLU epilogue: N covers W1 and W3 rows
+    Args a{};
+    a.A = (const uint16_t*)xp; a.lda = d;
+    a.B = (const uint16_t*)w1; a.B2 = (const uint16_t*)w3; a.ldb = d; a.b_es = (long)h * d;
+    a.C = gq; a.C2 = u; a.C3 = hb; a.ldc = h;
+    a.N = 2 * h; a.K = d; a.split = h;
+    a.offsets = offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.tiles_n = cdiv(2L * h, 256);
+    run<BM, 256, true, true, RAGGED_M, BSEL_GLU, CSEL_NONE, EPI_SWIGLU_FWD>("ggemm_up_swiglu", a, mt_max * a.tiles_n, s);
+  }
+  {  // down projection
+    Args a{};
+    a.A = (const uint16_t*)hb; a.lda = h;
+    a.B = (const uint16_t*)w2; a.ldb = h; a.b_es = (long)d * h;
+    a.C = yp; a.ldc = d;
+    a.N = d; a.K = h;
+    a.offsets = offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.tiles_n = cdiv(d, 256);
+    run<BM, 256, true, true, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_down", a, mt_max * a.tiles_n, s);
+  }
+}
+
+hipError_t launch_ggemm_fwd(const void* xp, const void* w1, const void* w3, const void* w2, const int* offsets,
+                            int E, int R, int d, int h, bool bf16, void* g, void* u, void* hb, void* yp, void* ws,
+                            hipStream_t s) {
+  if (!bf16)
+    return launch_ggemm_fwd_f32((const float*)xp, (const float*)w1, (const float*)w3, (const float*)w2, offsets, E,
+                                R, d, h, (float*)g, (float*)u, (float*)hb, (float*)yp, s);
+  int* tile_off = (int*)ws;
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off);
+  if (small_rows(E, R))
+    fwd_bm<128>(xp, w1, w3, w2, offsets, E, R, d, h, g, u, hb, yp, tile_off, s);
+  else
+    fwd_bm<256>(xp, w1, w3, w2, offsets, E, R, d, h, g, u, hb, yp, tile_off + (E + 1), s);
+  return hipGetLastError();
+}
+
+template <int BM>
+static void dgrad_bm(const void* dyp, const void* g, const void* u, const void* w1, const void* w3, const void* w2,
+                     const int* offsets, int E, int R, int d, int h, void* dgu, void* dxp, const int* tile_off,
+                     hipStream_t s) {
+  const int mt_max = cdiv(R, BM) + E;
+  {  // dgrad down + SwiGLU backward: dH = dYp W2[e] -> dG, dU
+    Args a{};
+    a.A = (const uint16_t*)dyp; a.lda = d;
+    a.B = (const uint16_t*)w2; a.ldb = h; a.b_es = (long)d * h;
+    a.C = dgu; a.ldc = 2L * h;
+    a.G = (const uint16_t*)g; a.U = (const uint16_t*)u; a.ldgu = h;
+    a.N = h; a.K = d; a.split = h;
+    a.offsets = offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.tiles_n = cdiv(h, 256);
+    run<BM, 256, true, false, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_SWIGLU_BWD>("ggemm_dgrad_down_swiglu", a,
+                                                                              mt_max * a.tiles_n, s);
+  }
+  {  // dgrad up: dXp = [dG | dU] [W1; W3]
+    Args a{};
+    a.A = (const uint16_t*)dgu; a.lda = 2L * h;
+    a.B = (const uint16_t*)w1; a.B2 = (const uint16_t*)w3; a.ldb = d; a.b_es = (long)h * d;
+    a.C = dxp; a.ldc = d;
+    a.N = d; a.K = 2 * h; a.split = h;
+    a.offsets = offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.tiles_n = cdiv(d, 256);
+    run<BM, 256, true, false, RAGGED_M, BSEL_KSPLIT, CSEL_NONE, EPI_BF16>("ggemm_dgrad_up", a, mt_max * a.tiles_n, s);
+  }
+}
+
+hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, const void* u, const void* hb,
+                            const void* w1, const void* w3, const void* w2, const int* offsets, int E, int R, int d,
+                            int h, bool bf16, void* dgu, void* dxp, void* dw1, void* dw3, void* dw2, void* ws,
+                            hipStream_t s) {
+  if (!bf16)
+    return launch_ggemm_bwd_f32((const float*)dyp, (const float*)xp, (const float*)g, (const float*)u,
+                                (const float*)hb, (const float*)w1, (const float*)w3, (const float*)w2, offsets, E,
+                                R, d, h, (float*)dgu, (float*)dxp, (float*)dw1, (float*)dw3, (float*)dw2, s);
+  int* tile_off = (int*)ws;
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off);
+  if (small_rows(E, R))
+    dgrad_bm<128>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off, s);
+  else
+    dgrad_bm<256>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off + (E + 1), s);
+  {  // wgrad down: dW2[e] = dYp_e^T H_e  (M = d, N = h, K = the expert's rows)
+    Args a{};
+    a.A = (const uint16_t*)dyp; a.lda = d;
+    a.B = (const uint16_t*)hb; a.ldb = h;
+    a.C = dw2; a.ldc = h; a.c_es = (long)d * h;
+    a.M = d; a.N = h;
+    a.offsets = offsets; a.E = E; a.R = R;
+    a.tiles_m = cdiv(d, 256); a.tiles_n = cdiv(h, 256);
+    run<256, 256, false, false, RAGGED_K, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_wgrad_down", a,
+                                                                          E * a.tiles_m * a.tiles_n, s);
+  }
+  {  // wgrad up: [dW1; dW3][e] = [dG | dU]_e^T Xp_e  (M = 2h, N = d)
+    Args a{};
+    a.A = (const uint16_t*)dgu; a.lda = 2L * h;
+    a.B = (const uint16_t*)xp; a.ldb = d;
+    a.C = dw1; a.C2 = dw3; a.ldc = d; a.c_es = (long)h * d;
+    a.M = 2 * h; a.N = d; a.split = h;
+    a.offsets = offsets; a.E = E; a.R = R;
+    a.tiles_m = cdiv(2L * h, 256); a.tiles_n = cdiv(d, 256);
+    run<256, 256, false, false, RAGGED_K, BSEL_NONE, CSEL_MSPLIT, EPI_BF16>("ggemm_wgrad_up", a,
+                                                                            E * a.tiles_m * a.tiles_n, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace trg
