@@ -31,8 +31,9 @@
 //    next K tile's HBM loads are in flight during the whole current tile.
 //  * The MFMA is issued as (B fragment, A fragment): each lane then owns 4
 //    consecutive output columns of one row.
-//  * Epilogues: bf16 store, SwiGLU forward (G, U, H), SwiGLU backward (dG, dU
-//    from dH, G, U).
+//  * Epilogues (bf16 store, SwiGLU forward G/U/H, SwiGLU backward dG/dU from
+//    dH, G, U) stage each wave's 32-row slabs in LDS and move whole row
+//    segments with 16-byte loads and stores.
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -194,111 +195,123 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
   const int per = (total + 7) >> 3;
   const int t_begin = xcd * per, t_end = min(total, t_begin + per);
 
-  for (int t = t_begin + lb; t < t_end; t += nbx) {
-    // ---------------- tile decode ----------------
+  // Per-tile geometry and operand resources.
+  struct Tile {
     int e, m0, m_end, n0, k0, k_end;
+    __amdgpu_buffer_rsrc_t rsA, rsB, rsB2;
+  };
+  const long a_ldb = g.lda * 2, b_ldb = g.ldb * 2;
+  auto decode = [&](int t) {
+    Tile c;
     if constexpr (MODE == RAGGED_M) {
-      const int mtg = t / g.tiles_n, nt = t - (t / g.tiles_n) * g.tiles_n;
+      const int mtg = t / g.tiles_n, nt = t - mtg * g.tiles_n;
       int lo = 0, hi = g.E;  // last expert with tile_off[e] <= mtg
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (g.tile_off[mid] <= mtg) lo = mid; else hi = mid;
       }
-      e = lo;
-      m0 = g.offsets[e] + (mtg - g.tile_off[e]) * BM;
-      m_end = g.offsets[e + 1];
-      n0 = nt * BN;
-      k0 = 0;
-      k_end = g.K;
+      c.e = lo;
+      c.m0 = g.offsets[lo] + (mtg - g.tile_off[lo]) * BM;
+      c.m_end = g.offsets[lo + 1];
+      c.n0 = nt * BN;
+      c.k0 = 0;
+      c.k_end = g.K;
+      // A: routed rows from m0 on, K-contiguous
+      c.rsA = make_rsrc(g.A + (long)c.m0 * g.lda, (long)(g.R - c.m0) * a_ldb);
+      if constexpr (BSEL == BSEL_GLU) {
+        const long hh0 = c.n0 / 2;
+        c.rsB = make_rsrc(g.B + (long)c.e * g.b_es + hh0 * g.ldb, (g.split - hh0) * b_ldb);
+        c.rsB2 = make_rsrc(g.B2 + (long)c.e * g.b_es + hh0 * g.ldb, (g.split - hh0) * b_ldb);
+      } else if constexpr (BKC) {
+        c.rsB = make_rsrc(g.B + (long)c.e * g.b_es + (long)c.n0 * g.ldb, (long)(g.N - c.n0) * b_ldb);
+        c.rsB2 = c.rsB;
+      } else {
+        // MN-contiguous B: X[k][n] inside the expert's block of b_es elements
+        c.rsB = make_rsrc(g.B + (long)c.e * g.b_es + c.n0, (g.b_es - c.n0) * 2);
+        c.rsB2 = (BSEL == BSEL_KSPLIT) ? make_rsrc(g.B2 + (long)c.e * g.b_es + c.n0, (g.b_es - c.n0) * 2) : c.rsB;
+      }
     } else {
       const int per_e = g.tiles_m * g.tiles_n;
-      e = t / per_e;
-      const int r = t - e * per_e;
+      c.e = t / per_e;
+      const int r = t - c.e * per_e;
       const int mt = r / g.tiles_n, nt = r - mt * g.tiles_n;
-      m0 = mt * BM;
-      m_end = g.M;
-      n0 = nt * BN;
-      k0 = g.offsets[e];
-      k_end = g.offsets[e + 1];
-    }
-
-    // ---------------- operand resources ----------------
-    __amdgpu_buffer_rsrc_t rsA, rsB, rsB2;
-    const long a_ldb = g.lda * 2, b_ldb = g.ldb * 2;
-    if constexpr (MODE == RAGGED_M) {
-      // A: routed rows from m0 on, K-contiguous
-      rsA = make_rsrc(g.A + (long)m0 * g.lda, (long)(g.R - m0) * a_ldb);
-      if constexpr (BSEL == BSEL_GLU) {
-        const long hh0 = n0 / 2;
-        rsB = make_rsrc(g.B + (long)e * g.b_es + hh0 * g.ldb, (g.split - hh0) * b_ldb);
-        rsB2 = make_rsrc(g.B2 + (long)e * g.b_es + hh0 * g.ldb, (g.split - hh0) * b_ldb);
-      } else if constexpr (BKC) {
-        rsB = make_rsrc(g.B + (long)e * g.b_es + (long)n0 * g.ldb, (long)(g.N - n0) * b_ldb);
-        rsB2 = rsB;
-      } else {
-        // MN-contiguous B: X[k][n] with the expert's block of b_es elements
-        rsB = make_rsrc(g.B + (long)e * g.b_es + n0, (g.b_es - n0) * 2);
-        rsB2 = (BSEL == BSEL_KSPLIT) ? make_rsrc(g.B2 + (long)e * g.b_es + n0, (g.b_es - n0) * 2) : rsB;
-      }
-    } else {
+      c.m0 = mt * BM;
+      c.m_end = g.M;
+      c.n0 = nt * BN;
+      c.k0 = g.offsets[c.e];
+      c.k_end = g.offsets[c.e + 1];
       // weight gradients: K = the expert's rows; rows past k_end read as zero
-      const long nrows = k_end - k0;
-      rsA = make_rsrc(g.A + (long)k0 * g.lda + m0, nrows * a_ldb - (long)m0 * 2);
-      rsB = make_rsrc(g.B + (long)k0 * g.ldb + n0, nrows * b_ldb - (long)n0 * 2);
-      rsB2 = rsB;
+      const long nrows = c.k_end - c.k0;
+      c.rsA = make_rsrc(g.A + (long)c.k0 * g.lda + c.m0, nrows * a_ldb - (long)c.m0 * 2);
+      c.rsB = make_rsrc(g.B + (long)c.k0 * g.ldb + c.n0, nrows * b_ldb - (long)c.n0 * 2);
+      c.rsB2 = c.rsB;
     }
+    return c;
+  };
+  auto num_k = [&](const Tile& c) { return c.k_end > c.k0 ? (c.k_end - c.k0 + BK - 1) / BK : 0; };
 
-    int a_lane[2], b_lane[2];
+  int a_lane[2], b_lane[2];
+  if constexpr (AKC) {
+    a_lane[0] = kc_lane_off(lane, 0, (int)a_ldb);
+    a_lane[1] = kc_lane_off(lane, 1, (int)a_ldb);
+  } else {
+    a_lane[0] = mnc_lane_off<BM>(lane, 0, (int)a_ldb);
+    a_lane[1] = mnc_lane_off<BM>(lane, 1, (int)a_ldb);
+  }
+  if constexpr (BKC) {
+    b_lane[0] = kc_lane_off(lane, 0, (int)b_ldb);
+    b_lane[1] = kc_lane_off(lane, 1, (int)b_ldb);
+  } else {
+    b_lane[0] = mnc_lane_off<BN>(lane, 0, (int)b_ldb);
+    b_lane[1] = mnc_lane_off<BN>(lane, 1, (int)b_ldb);
+  }
+  auto issue = [&](const Tile& c, int kt, int stage) {  // kt: K offset relative to c.k0
+    char* sA = smem + stage * STAGE;
+    char* sB = sA + SA;
     if constexpr (AKC) {
-      a_lane[0] = kc_lane_off(lane, 0, (int)a_ldb);
-      a_lane[1] = kc_lane_off(lane, 1, (int)a_ldb);
+      load_kc<BM, NW>(sA, wave, a_lane, kt * 2, (int)a_ldb, [&](int r8, int& r0) {
+        r0 = r8;
+        return c.rsA;
+      });
     } else {
-      a_lane[0] = mnc_lane_off<BM>(lane, 0, (int)a_ldb);
-      a_lane[1] = mnc_lane_off<BM>(lane, 1, (int)a_ldb);
+      load_mnc<BM, NW>(sA, wave, a_lane, c.rsA, kt, (int)a_ldb);
     }
     if constexpr (BKC) {
-      b_lane[0] = kc_lane_off(lane, 0, (int)b_ldb);
-      b_lane[1] = kc_lane_off(lane, 1, (int)b_ldb);
-    } else {
-      b_lane[0] = mnc_lane_off<BN>(lane, 0, (int)b_ldb);
-      b_lane[1] = mnc_lane_off<BN>(lane, 1, (int)b_ldb);
-    }
-    auto issue = [&](int kt, int stage) {  // kt: K offset relative to k0
-      char* sA = smem + stage * STAGE;
-      char* sB = sA + SA;
-      if constexpr (AKC) {
-        load_kc<BM, NW>(sA, wave, a_lane, kt * 2, (int)a_ldb, [&](int r8, int& r0) {
-          r0 = r8;
-          return rsA;
+      if constexpr (BSEL == BSEL_GLU) {
+        load_kc<BN, NW>(sB, wave, b_lane, kt * 2, (int)b_ldb, [&](int r8, int& r0) {
+          // LDS rows of wave column `part`: first WTN/2 from W1, next WTN/2
+          // from W3, both for the same hidden units
+          const int p = r8 % WTN;
+          r0 = (r8 / WTN) * (WTN / 2) + (p % (WTN / 2));
+          return (p >= WTN / 2) ? c.rsB2 : c.rsB;
         });
       } else {
-        load_mnc<BM, NW>(sA, wave, a_lane, rsA, kt, (int)a_ldb);
+        load_kc<BN, NW>(sB, wave, b_lane, kt * 2, (int)b_ldb, [&](int r8, int& r0) {
+          r0 = r8;
+          return c.rsB;
+        });
       }
-      if constexpr (BKC) {
-        if constexpr (BSEL == BSEL_GLU) {
-          load_kc<BN, NW>(sB, wave, b_lane, kt * 2, (int)b_ldb, [&](int r8, int& r0) {
-            // LDS rows of wave column `part`: first WTN/2 from W1, next WTN/2
-            // from W3, both for the same hidden units
-            const int p = r8 % WTN;
-            r0 = (r8 / WTN) * (WTN / 2) + (p % (WTN / 2));
-            return (p >= WTN / 2) ? rsB2 : rsB;
-          });
-        } else {
-          load_kc<BN, NW>(sB, wave, b_lane, kt * 2, (int)b_ldb, [&](int r8, int& r0) {
-            r0 = r8;
-            return rsB;
-          });
-        }
+    } else {
+      if constexpr (BSEL == BSEL_KSPLIT) {
+        if (kt >= g.split) load_mnc<BN, NW>(sB, wave, b_lane, c.rsB2, kt - g.split, (int)b_ldb);
+        else load_mnc<BN, NW>(sB, wave, b_lane, c.rsB, kt, (int)b_ldb);
       } else {
-        if constexpr (BSEL == BSEL_KSPLIT) {
-          if (kt >= g.split) load_mnc<BN, NW>(sB, wave, b_lane, rsB2, kt - g.split, (int)b_ldb);
-          else load_mnc<BN, NW>(sB, wave, b_lane, rsB, kt, (int)b_ldb);
-        } else {
-          load_mnc<BN, NW>(sB, wave, b_lane, rsB, kt, (int)b_ldb);
-        }
+        load_mnc<BN, NW>(sB, wave, b_lane, c.rsB, kt, (int)b_ldb);
       }
-    };
+    }
+  };
 
+  // The first K step of a tile is loaded into stage 0 before the previous
+  // tile's epilogue runs (the epilogue stages through stage 1), so a tile
+  // boundary costs no full memory round trip.
+  int t = t_begin + lb;
+  Tile cur;
+  if (t < t_end) {
+    cur = decode(t);
+    if (num_k(cur) > 0) issue(cur, 0, 0);
+  }
+  for (; t < t_end; t += nbx) {
+    const int e = cur.e, m0 = cur.m0, m_end = cur.m_end, n0 = cur.n0;
     f32x16_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -307,15 +320,11 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int nk = k_end > k0 ? (k_end - k0 + BK - 1) / BK : 0;
-    __syncthreads();  // the previous tile's waves are done with both stages
-    if (nk > 0) issue(0, 0);
+    const int nk = num_k(cur);
     for (int it = 0; it < nk; ++it) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // stage it&1 is complete; stage (it+1)&1 is free
-      if (it + 1 < nk) issue((it + 1) * BK, (it + 1) & 1);
-      __builtin_amdgcn_sched_group_barrier(0x020, (BM + BN) / 8 / NW, 0);  // HBM->LDS loads first
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);  // slice-0 fragments
+      if (it + 1 < nk) issue(cur, (it + 1) * BK, (it + 1) & 1);
       const char* sA = smem + (it & 1) * STAGE;
       const char* sB = sA + SA;
       bf16x8_t af[2][TM], bfr[2][TN];
@@ -323,117 +332,181 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
       for (int i = 0; i < TM; ++i) af[0][i] = frag<BM, AKC>(sA, wm * WTM + i * 32, 0, lane);
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[0][j] = frag<BN, BKC>(sB, wn * WTN + j * 32, 0, lane);
+      // Scheduling fences keep the next slice's reads ahead of this slice's
+      // MFMAs (two fragment sets stay live instead of one re-used per MFMA).
+      __builtin_amdgcn_sched_barrier(0);
       static_for<BK / 16>([&](auto KK) {
         constexpr int kk = decltype(KK)::value;
-        constexpr int cur = kk & 1;
+        constexpr int fb = kk & 1;  // fragment set of this slice
         if constexpr (kk + 1 < BK / 16) {
 #pragma unroll
-          for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = frag<BM, AKC>(sA, wm * WTM + i * 32, kk + 1, lane);
+          for (int i = 0; i < TM; ++i) af[fb ^ 1][i] = frag<BM, AKC>(sA, wm * WTM + i * 32, kk + 1, lane);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) bfr[cur ^ 1][j] = frag<BN, BKC>(sB, wn * WTN + j * 32, kk + 1, lane);
+          for (int j = 0; j < TN; ++j) bfr[fb ^ 1][j] = frag<BN, BKC>(sB, wn * WTN + j * 32, kk + 1, lane);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
-        // Issue order: the next slice's LDS reads between this slice's MFMAs.
-        constexpr int NR = (TM + TN) * ((AKC ? 1 : 2) + (BKC ? 1 : 2)) / 2;  // DS reads per slice (approx.)
-        if constexpr (kk + 1 < BK / 16) {
-          static_for<(NR < TM * TN ? NR : TM * TN)>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
-          });
-          if constexpr (NR < TM * TN) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - NR, 0);
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
-        }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       });
     }
 
     // ---------------- epilogue ----------------
-    // Lane (lrow, lgrp) owns row ... + lrow and 4 consecutive columns per
-    // group q: ... + q*8 + lgrp + {0..3}.
+    // Each wave stages 16-row slabs of its tile in a private LDS area (inside
+    // stage 1, while the next tile's first K step streams into stage 0) and
+    // writes whole row segments with 16-byte stores; the accumulator layout
+    // alone would scatter 8-byte pieces over 32 rows per store instruction.  Accumulator
+    // lane (lrow, lgrp) owns row lrow and, per 32-column subtile j and group q,
+    // columns j*32 + q*8 + lgrp + {0..3}.
+    __syncthreads();  // every wave is done with the last K stage
+    {
+      const int tn = t + nbx;
+      if (tn < t_end) {
+        const Tile nxt = decode(tn);
+        if (num_k(nxt) > 0) issue(nxt, 0, 0);
+        cur = nxt;
+      }
+    }
+    constexpr int WLDS = STAGE / NW;  // LDS bytes per wave, inside stage 1
+    constexpr int P = WTN * 2 + 16;       // staged row pitch (16-byte aligned)
+    constexpr int PG = WTN + 16;          // GLU: WTN/2 columns per array
+    constexpr int SR = 16;                // slab rows: half an accumulator subtile
+    static_assert(EPI != EPI_SWIGLU_BWD || 2 * SR * P <= WLDS, "epilogue LDS");
+    static_assert(EPI != EPI_SWIGLU_FWD || 3 * SR * PG <= WLDS, "epilogue LDS");
+    static_assert(SR * P <= WLDS, "epilogue LDS");
+    char* wl = smem + STAGE + wave * WLDS;
     const int lrow = lane & 31, lgrp = (lane >> 5) * 4;
-    if constexpr (EPI == EPI_SWIGLU_FWD) {
-      uint16_t* Gp = (uint16_t*)g.C;
-      uint16_t* Up = (uint16_t*)g.C2;
-      uint16_t* Hp = (uint16_t*)g.C3;
-      static_for<TM>([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        const int m = m0 + wm * WTM + i * 32 + lrow;
-        if (m < m_end) {
+    const int mw = m0 + wm * WTM;
+    const int srow = lrow & (SR - 1);
+    auto stage4 = [&](char* slab, int pitch, int col, float v0, float v1, float v2, float v3) {
+      *(uint2*)(slab + srow * pitch + col * 2) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+    };
+    // Slab rows -> memory: chunk c of COLS/8 16-byte chunks per row.
+    auto store_rows = [&](const char* slab, int pitch, int cols, int ms, auto&& dst) {
+      const int cpr = cols / 8;
+      for (int c = lane; c < SR * cpr; c += 64) {
+        const int row = c / cpr, cc = c - row * cpr;
+        if (ms + row < m_end) dst(ms + row, cc * 8, *(const uint4*)(slab + row * pitch + cc * 16));
+      }
+    };
+    static_for<TM * 2>([&](auto IH) {
+      constexpr int i = decltype(IH)::value / 2;
+      const int ms = mw + i * 32 + (decltype(IH)::value & 1) * SR;
+      const bool mine = (lrow / SR) == (decltype(IH)::value & 1);  // lane's row is in this half
+      if (ms < m_end) {
+        if constexpr (EPI == EPI_SWIGLU_FWD) {
+          char* sG = wl;
+          char* sU = wl + SR * PG;
+          char* sH = wl + 2 * SR * PG;
           static_for<TN / 2>([&](auto J) {
             constexpr int j = decltype(J)::value;
             static_for<4>([&](auto Q) {
               constexpr int q = decltype(Q)::value;
-              const int hh = n0 / 2 + wn * (WTN / 2) + j * 32 + q * 8 + lgrp;
-              if (hh < g.split) {
-                float gv[4], uv[4], hv[4];
-                static_for<4>([&](auto Rr) {
-                  constexpr int r = decltype(Rr)::value;
-                  gv[r] = acc[i][j][q * 4 + r];
-                  uv[r] = acc[i][j + TN / 2][q * 4 + r];
-                  hv[r] = silu_f(gv[r]) * uv[r];
-                });
-                const long o = (long)m * g.ldc + hh;
-                *(uint2*)(Gp + o) = make_uint2(pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3]));
-                *(uint2*)(Up + o) = make_uint2(pack_bf2(uv[0], uv[1]), pack_bf2(uv[2], uv[3]));
-                *(uint2*)(Hp + o) = make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
+              float gv[4], uv[4], hv[4];
+              static_for<4>([&](auto Rr) {
+                constexpr int r = decltype(Rr)::value;
+                gv[r] = acc[i][j][q * 4 + r];
+                uv[r] = acc[i][j + TN / 2][q * 4 + r];
+                hv[r] = silu_f(gv[r]) * uv[r];
+              });
+              const int col = j * 32 + q * 8 + lgrp;
+              if (mine) {
+                stage4(sG, PG, col, gv[0], gv[1], gv[2], gv[3]);
+                stage4(sU, PG, col, uv[0], uv[1], uv[2], uv[3]);
+                stage4(sH, PG, col, hv[0], hv[1], hv[2], hv[3]);
               }
             });
           });
-        }
-      });
-    } else {
-      static_for<TM>([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        const int m = m0 + wm * WTM + i * 32 + lrow;
-        if (m < m_end) {
-          void* Cb = g.C;
-          int mrow0 = 0;
-          if constexpr (CSEL == CSEL_MSPLIT) {
-            if (m >= g.split) {
-              Cb = g.C2;
-              mrow0 = g.split;
+          __builtin_amdgcn_wave_barrier();
+          const int hh0 = n0 / 2 + wn * (WTN / 2);
+          auto put = [&](uint16_t* base) {
+            return [&, base](int m, int c, uint4 v) {
+              if (hh0 + c < g.split) *(uint4*)(base + (long)m * g.ldc + hh0 + c) = v;
+            };
+          };
+          store_rows(sG, PG, WTN / 2, ms, put((uint16_t*)g.C));
+          store_rows(sU, PG, WTN / 2, ms, put((uint16_t*)g.C2));
+          store_rows(sH, PG, WTN / 2, ms, put((uint16_t*)g.C3));
+        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+          // dH = acc; G and U come in coalesced, dG and dU go out the same way.
+          char* sG = wl;
+          char* sU = wl + SR * P;
+          const int nw = n0 + wn * WTN;
+          for (int c = lane; c < SR * (WTN / 8); c += 64) {
+            const int row = c / (WTN / 8), cc = c - row * (WTN / 8);
+            const int m = ms + row, n = nw + cc * 8;
+            uint4 gv = make_uint4(0, 0, 0, 0), uv = gv;
+            if (m < m_end && n < g.N) {
+              gv = *(const uint4*)(g.G + (long)m * g.ldgu + n);
+              uv = *(const uint4*)(g.U + (long)m * g.ldgu + n);
             }
+            *(uint4*)(sG + row * P + cc * 16) = gv;
+            *(uint4*)(sU + row * P + cc * 16) = uv;
           }
+          __builtin_amdgcn_wave_barrier();
           static_for<TN>([&](auto J) {
             constexpr int j = decltype(J)::value;
             static_for<4>([&](auto Q) {
               constexpr int q = decltype(Q)::value;
-              const int n = n0 + wn * WTN + j * 32 + q * 8 + lgrp;
-              if (n < g.N) {
-                const float v0 = acc[i][j][q * 4 + 0], v1 = acc[i][j][q * 4 + 1];
-                const float v2 = acc[i][j][q * 4 + 2], v3 = acc[i][j][q * 4 + 3];
-                if constexpr (EPI == EPI_BF16) {
-                  const long o = (long)e * g.c_es + (long)(m - mrow0) * g.ldc + n;
-                  *(uint2*)((uint16_t*)Cb + o) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
-                } else {
-                  // SWIGLU_BWD: (v0..v3) = dH[m][n..n+3]; n indexes h
-                  const long gu = (long)m * g.ldgu + n;
-                  const uint2 gw = *(const uint2*)(g.G + gu);
-                  const uint2 uw = *(const uint2*)(g.U + gu);
-                  const float vv[4] = {v0, v1, v2, v3};
-                  const float gg[4] = {bf_lo(gw.x), bf_hi(gw.x), bf_lo(gw.y), bf_hi(gw.y)};
-                  const float uu[4] = {bf_lo(uw.x), bf_hi(uw.x), bf_lo(uw.y), bf_hi(uw.y)};
-                  float dg[4], du[4];
-                  static_for<4>([&](auto Rr) {
-                    constexpr int r = decltype(Rr)::value;
-                    const float s = sigmoid_f(gg[r]);
-                    du[r] = vv[r] * gg[r] * s;
-                    dg[r] = vv[r] * uu[r] * s * (1.0f + gg[r] * (1.0f - s));
-                  });
-                  uint16_t* D = (uint16_t*)Cb + (long)m * g.ldc;
-                  *(uint2*)(D + n) = make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
-                  *(uint2*)(D + g.split + n) = make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
-                }
-              }
+              if (!mine) return;
+              const int off = srow * P + (j * 32 + q * 8 + lgrp) * 2;
+              const uint2 gw = *(const uint2*)(sG + off);
+              const uint2 uw = *(const uint2*)(sU + off);
+              const float gg[4] = {bf_lo(gw.x), bf_hi(gw.x), bf_lo(gw.y), bf_hi(gw.y)};
+              const float uu[4] = {bf_lo(uw.x), bf_hi(uw.x), bf_lo(uw.y), bf_hi(uw.y)};
+              float dg[4], du[4];
+              static_for<4>([&](auto Rr) {
+                constexpr int r = decltype(Rr)::value;
+                const float v = acc[i][j][q * 4 + r];
+                const float sg = sigmoid_f(gg[r]);
+                du[r] = v * gg[r] * sg;
+                dg[r] = v * uu[r] * sg * (1.0f + gg[r] * (1.0f - sg));
+              });
+              *(uint2*)(sG + off) = make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+              *(uint2*)(sU + off) = make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
             });
           });
+          __builtin_amdgcn_wave_barrier();
+          uint16_t* D = (uint16_t*)g.C;
+          store_rows(sG, P, WTN, ms, [&](int m, int c, uint4 v) {
+            if (nw + c < g.N) *(uint4*)(D + (long)m * g.ldc + nw + c) = v;
+          });
+          store_rows(sU, P, WTN, ms, [&](int m, int c, uint4 v) {
+            if (nw + c < g.N) *(uint4*)(D + (long)m * g.ldc + g.split + nw + c) = v;
+          });
+        } else {
+          char* sC = wl;
+          static_for<TN>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            static_for<4>([&](auto Q) {
+              constexpr int q = decltype(Q)::value;
+              if (mine)
+                stage4(sC, P, j * 32 + q * 8 + lgrp, acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1],
+                       acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+            });
+          });
+          __builtin_amdgcn_wave_barrier();
+          const int nw = n0 + wn * WTN;
+          store_rows(sC, P, WTN, ms, [&](int m, int c, uint4 v) {
+            if (nw + c < g.N) {
+              uint16_t* Cb = (uint16_t*)g.C;
+              int mr = m;
+              if constexpr (CSEL == CSEL_MSPLIT) {
+                if (m >= g.split) {
+                  Cb = (uint16_t*)g.C2;
+                  mr = m - g.split;
+                }
+              }
+              *(uint4*)(Cb + (long)e * g.c_es + (long)mr * g.ldc + nw + c) = v;
+            }
+          });
         }
-      });
-    }
+        __builtin_amdgcn_wave_barrier();  // the slab area is rewritten next
+      }
+    });
   }
 }
 
