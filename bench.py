@@ -31,11 +31,13 @@ METRIC = "MoE layer fwd+bwd tokens/s and grouped-GEMM TFLOP/s (% of MFMA peak), 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0
 
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
 GEMM_KERNELS = {
     # name: flops per launch as a multiple of R*d*h
     "ggemm_up_swiglu": 4, "ggemm_down": 2, "ggemm_dgrad_down_swiglu": 2, "ggemm_wgrad_down": 2,
     "ggemm_dgrad_up": 4, "ggemm_wgrad_up": 4,
 }
+GEMM_KERNELS.update({n.replace("ggemm_", "ggemm_mx_"): m for n, m in list(GEMM_KERNELS.items())})
 
 
 def log(*a):
@@ -66,24 +68,27 @@ def cpu_baseline(cfg, mode, sample_T, min_seconds=10.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    from oracle import moe_mx_ref as mxl
+
     inp = inputs.layer_inputs(cfg, T=sample_T)
     forced = None
     if mode != "router":
         forced = inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)[:sample_T]
     args = (inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"])
+    fwd, bwd = (mxl.layer_forward_mx, mxl.layer_backward_mx) if cfg.mx else (ref.layer_forward, ref.layer_backward)
     times = []
     while True:  # repeat the same sample until ~10 s of CPU work (at most 20 runs)
         t0 = time.perf_counter()
-        f = ref.layer_forward(*args, cfg.k, forced_idx=forced)
-        ref.layer_backward(f, inp["dy"], *args)
+        f = fwd(*args, cfg.k, forced_idx=forced)
+        bwd(f, inp["dy"], *args)
         times.append(time.perf_counter() - t0)
         if sum(times) >= min_seconds or len(times) >= 20:
             break
     el = float(np.median(times))
     return {"value": sample_T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {sample_T} of {cfg.T} tokens, all {cfg.E} experts, full d={cfg.d} h={cfg.h}; "
-                      f"float64 numpy fwd+bwd, median of {len(times)} runs ({sum(times):.1f} s total) "
-                      f"on {cpu_model()}",
+                      f"float64 numpy {'MXFP8 (quantise-dequantise) ' if cfg.mx else ''}fwd+bwd, median of "
+                      f"{len(times)} runs ({sum(times):.1f} s total) on {cpu_model()}",
             "seconds_per_run": el}
 
 
@@ -131,8 +136,6 @@ def main():
 
     cfg = configs.get(a.config)
     mode = a.mode or cfg.modes[0]
-    if cfg.mx:
-        raise SystemExit("the MXFP8 path is not built yet")
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     log(f"bench: {cfg.slug} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} h={cfg.h} {cfg.dtype} mode={mode}")
@@ -142,7 +145,7 @@ def main():
     if mode != "router":
         forced = torch.from_numpy(inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)).to(dev)
     del inp
-    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, dev)
+    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, dev, mx=cfg.mx)
     args = (t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])
 
     for _ in range(a.warmup):
@@ -190,6 +193,7 @@ def main():
     dom = max((n for n in GEMM_KERNELS if n in kern), key=lambda n: kern[n]["avg_us"])
     dom_flops = GEMM_KERNELS[dom] * rdh
     achieved = dom_flops / (kern[dom]["avg_us"] * 1e-6) / 1e12
+    gemm_peak = FP8_PEAK_TFLOPS if cfg.mx else BF16_PEAK_TFLOPS
 
     counts = layer.counts.cpu().numpy()
     out = {
@@ -203,19 +207,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "mxfp8" if cfg.mx else cfg.dtype,
         "data": "synthetic (seeded: x~N(0,1), weights~N(0,0.02^2), dy~N(0,1); values fixed across steps)",
         "config": {"workload": f"{cfg.slug}: MoE expert layer fwd+bwd, T={cfg.T} d_model={cfg.d} experts={cfg.E} "
-                               f"top-{cfg.k} SwiGLU hidden={cfg.h} {cfg.dtype}, routing={mode}",
+                               f"top-{cfg.k} SwiGLU hidden={cfg.h} "
+                               f"{'MXFP8 grouped GEMMs (bf16 router/combine)' if cfg.mx else cfg.dtype}, "
+                               f"routing={mode}",
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "h": cfg.h, "routing": mode,
                    "parallelism": "single GPU"},
         "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
         "layer_frac_bf16_peak": layer_flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "ggemm_tflops": gemm_flops / (gemm_us * 1e-6) / 1e12,
         "ggemm_frac_bf16_peak": gemm_flops / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+        "ggemm_frac_own_peak": gemm_flops / (gemm_us * 1e-6) / 1e12 / gemm_peak,
         "ms_per_step_no_events": 1000.0 * elapsed_clean / a.steps,
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": gemm_peak,
+                     "unit": "TFLOP/s", "frac": achieved / gemm_peak, "traffic": None,
                      "algorithmic_per_launch": f"{GEMM_KERNELS[dom]}*R*d*h = {dom_flops:.4g} flop"},
         "kernels_avg_us": {n: round(v["avg_us"], 2) for n, v in sorted(kern.items())},
         "expert_load": {"max": int(counts.max()), "mean": float(counts.mean()), "min": int(counts.min())},

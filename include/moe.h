@@ -200,6 +200,88 @@ moe_status_t moe_router_bwd(const float* probs, const int32_t* topk_idx, const f
                             const void* x, const void* wr, int T, int d, int E, int k, int dt,
                             void* dx, void* dwr, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * MXFP8 path ("Precision optimisation with MXFP8": MXFP8 cuts both compute and
+ * the traffic between experts).  Encoding (OCP microscaling): E4M3FN elements
+ * and one E8M0 scale byte per 32 consecutive values along a GEMM's reduction
+ * dimension; s = clamp(floor(log2(amax)) - 8, -127, 127) taken from the
+ * exponent bits (s = -127 for an all-zero block), scale byte s + 127,
+ * elements E4M3FN(v / 2^s) rounded to nearest even and saturated to +-448,
+ * sign of zero kept.  Layouts:
+ *   rowwise      q [rows, cols] u8, s [rows, cols/32] u8 (blocks along cols)
+ *   columnwise   q [cols, ldc] u8, s [cols, ldc/32] u8: blocks of 32
+ *                consecutive rows inside each row segment, the last block of
+ *                a segment zero-padded; segment e starts at column off32[e]
+ *                (the transpose of the rowwise form of each padded segment)
+ * ---------------------------------------------------------------------------
+ *
+ * mx_quantize: quantise `rows` rows of a [*, cols] matrix `in` (dt = MOE_BF16
+ * or MOE_F32, row stride cols) to either or both layouts in one pass.
+ *   gather_src (nullable): logical row r is in[gather_src[r] / gather_k]
+ *     (pass moe_route's src and k to quantise the routed rows of x straight
+ *     from x: the rowwise dispatch and the quantisation in one step).
+ *   seg_off / seg_off32 (nullable, [nseg+1]): row segments and their 32-padded
+ *     starts (moe_route's offsets / off32); if null, segments of seg_rows rows
+ *     (rows a multiple of seg_rows, or seg_rows = rows), each padded to 32.
+ *   q_row/s_row (nullable): rowwise output.  q_col/s_col (nullable): columnwise
+ *     output with row stride ldc (a multiple of 32, at least the padded row
+ *     count: rows + 31*nseg with seg_off, else segments x round32(seg_rows)).
+ * cols must be a multiple of 32.  Bit-exact and deterministic.
+ */
+moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32_t* gather_src, int gather_k,
+                         const int32_t* seg_off, const int32_t* seg_off32, int nseg, int seg_rows, uint8_t* q_row,
+                         uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, int ldc, void* stream);
+
+/*
+ * MXFP8 grouped GEMMs of the expert FFNs: the same SwiGLU forward and backward
+ * as moe_grouped_gemm_fwd / _bwd, with every GEMM operand quantised along its
+ * own reduction dimension and multiplied on gfx950's scaled matrix cores
+ * (fp32 accumulation, bf16 outputs).  d and h must be multiples of 128; r32cap
+ * (row stride of every columnwise copy) a multiple of 32 and >= R + 31*E.
+ * The caller quantises x (mx_quantize with gather) and the weights; the calls
+ * quantise H, dYp and dG|dU themselves (both layouts, from the stored bf16
+ * values).  ws: moe_grouped_gemm_workspace_size() bytes.
+ */
+typedef struct {
+  int E, R, d, h, r32cap;
+  const int32_t* offsets;                 /* [E+1] expert row offsets          */
+  const int32_t* off32;                   /* [E+1] 32-padded segment starts    */
+  const uint8_t* xq; const uint8_t* xs;   /* [R,d], [R,d/32] routed x, rowwise */
+  const uint8_t* w1q; const uint8_t* w1s; /* [E,h,d], [E,h,d/32] rowwise       */
+  const uint8_t* w3q; const uint8_t* w3s; /* [E,h,d], [E,h,d/32] rowwise       */
+  const uint8_t* w2q; const uint8_t* w2s; /* [E,d,h], [E,d,h/32] rowwise       */
+  void* g; void* u; void* hbuf;           /* out: [R,h] bf16                   */
+  uint8_t* hq; uint8_t* hs;               /* out: [R,h], [R,h/32] rowwise H    */
+  uint8_t* hqT; uint8_t* hsT;             /* out: [h,r32cap], [h,r32cap/32]    */
+  void* yp;                               /* out: [R,d] bf16                   */
+  void* ws; size_t ws_bytes;
+} moe_mx_fwd_args;
+
+typedef struct {
+  int E, R, d, h, r32cap;
+  const int32_t* offsets;
+  const int32_t* off32;
+  const void* dyp;                          /* [R,d] bf16 (moe_combine_bwd)         */
+  uint8_t* dyq; uint8_t* dys;               /* out: [R,d], [R,d/32] rowwise dYp     */
+  uint8_t* dyqT; uint8_t* dysT;             /* out: [d,r32cap], [d,r32cap/32]       */
+  const void* g; const void* u;             /* [R,h] bf16 from the forward          */
+  const uint8_t* hqT; const uint8_t* hsT;   /* columnwise H from the forward        */
+  const uint8_t* xqT; const uint8_t* xsT;   /* [d,r32cap] columnwise routed x       */
+  const uint8_t* w1tq; const uint8_t* w1ts; /* [d,E*h], [d,E*h/32]: W1 blocked on h */
+  const uint8_t* w3tq; const uint8_t* w3ts; /* same for W3                          */
+  const uint8_t* w2tq; const uint8_t* w2ts; /* [h,E*d], [h,E*d/32]: W2 blocked on d */
+  void* dgu;                                /* out: [R,2h] bf16 (dG | dU)           */
+  uint8_t* dguq; uint8_t* dgus;             /* out: [R,2h], [R,2h/32]               */
+  uint8_t* dguqT; uint8_t* dgusT;           /* out: [2h,r32cap], [2h,r32cap/32]     */
+  void* dxp;                                /* out: [R,d] bf16                      */
+  void* dw1; void* dw3; void* dw2;          /* out: weight gradients, bf16          */
+  void* ws; size_t ws_bytes;
+} moe_mx_bwd_args;
+
+moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* args, void* stream);
+moe_status_t moe_grouped_gemm_bwd_mx(const moe_mx_bwd_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,3 +69,51 @@ def test_host_side_validation_without_gpu():
     # k out of range
     st = lib.moe_combine(None, None, None, 4, 64, 0, 1, None, None)
     assert st == 1
+
+
+def test_mx_arg_structs_match_the_header(tmp_path):
+    """The ctypes mirrors of moe_mx_fwd_args / moe_mx_bwd_args have the C
+    layout: every field offset and the size, as gcc lays out include/moe.h."""
+    import ctypes
+    import shutil
+    import subprocess
+
+    from token_routing_grouped_amd import _abi
+
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void) {"]
+    for cname, py in (("moe_mx_fwd_args", _abi.MxFwdArgs), ("moe_mx_bwd_args", _abi.MxBwdArgs)):
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in (("moe_mx_fwd_args", _abi.MxFwdArgs), ("moe_mx_bwd_args", _abi.MxBwdArgs)):
+        assert got[(cname, "size")] == ctypes.sizeof(py)
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_mx_host_side_validation_without_gpu():
+    from token_routing_grouped_amd import _abi
+
+    lib = _abi.lib()
+    # cols not a multiple of 32
+    st = lib.mx_quantize(None, 1, 4, 48, None, 1, None, None, 0, 4, None, None, None, None, 0, None)
+    assert st == 1
+    # nothing to write
+    st = lib.mx_quantize(None, 1, 4, 64, None, 1, None, None, 0, 4, None, None, None, None, 0, None)
+    assert st == 1 and b"nothing to write" in lib.moe_last_error_string()
+    # MX grouped GEMM needs d, h multiples of 128
+    a = _abi.MxFwdArgs(E=2, R=8, d=192, h=128, r32cap=96)
+    assert lib.moe_grouped_gemm_fwd_mx(ctypes.byref(a), None) == 1
+    # r32cap below R + 31*E
+    a = _abi.MxFwdArgs(E=2, R=8, d=128, h=128, r32cap=64)
+    assert lib.moe_grouped_gemm_fwd_mx(ctypes.byref(a), None) == 1

@@ -45,7 +45,27 @@ _SIGS = {
                               _P], _I),
     "moe_router_bwd_workspace_size": ([_I, _I, _I], _Z),
     "moe_router_bwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "mx_quantize": ([_P, _I, _I, _I, _P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P], _I),
+    "moe_grouped_gemm_fwd_mx": ([_P, _P], _I),
+    "moe_grouped_gemm_bwd_mx": ([_P, _P], _I),
 }
+
+
+class MxFwdArgs(ctypes.Structure):
+    """moe_mx_fwd_args (include/moe.h)."""
+    _fields_ = [(n, ctypes.c_int) for n in ("E", "R", "d", "h", "r32cap")] + \
+        [(n, ctypes.c_void_p) for n in ("offsets", "off32", "xq", "xs", "w1q", "w1s", "w3q", "w3s", "w2q", "w2s", "g",
+                                        "u", "hbuf", "hq", "hs", "hqT", "hsT", "yp", "ws")] + \
+        [("ws_bytes", ctypes.c_size_t)]
+
+
+class MxBwdArgs(ctypes.Structure):
+    """moe_mx_bwd_args (include/moe.h)."""
+    _fields_ = [(n, ctypes.c_int) for n in ("E", "R", "d", "h", "r32cap")] + \
+        [(n, ctypes.c_void_p) for n in ("offsets", "off32", "dyp", "dyq", "dys", "dyqT", "dysT", "g", "u", "hqT", "hsT",
+                                        "xqT", "xsT", "w1tq", "w1ts", "w3tq", "w3ts", "w2tq", "w2ts", "dgu", "dguq",
+                                        "dgus", "dguqT", "dgusT", "dxp", "dw1", "dw3", "dw2", "ws")] + \
+        [("ws_bytes", ctypes.c_size_t)]
 
 EXPORTED = tuple(_SIGS)
 
@@ -238,3 +258,44 @@ def moe_router_bwd(probs, topk_idx, dgate, x, wr, dx, dwr, ws):
     _expect(dwr, x.dtype, "dwr")
     _check(lib().moe_router_bwd(_p(probs), _p(topk_idx), _p(dgate), _p(x), _p(wr), T, d, E, k, _dt(x), _p(dx), _p(dwr),
                                 _p(ws), ws.numel(), _stream()), "moe_router_bwd")
+
+
+# ---------------------------------------------------------------------------
+# MXFP8
+# ---------------------------------------------------------------------------
+
+def mx_quantize(x, rows, q_row=None, s_row=None, q_col=None, s_col=None, gather_src=None, gather_k=1, seg_off=None,
+                seg_off32=None, seg_rows=0):
+    """Quantise `rows` rows of x (bf16/f32, [*, cols]) to rowwise and/or
+    columnwise MX (E4M3 + E8M0); see mx_quantize in include/moe.h."""
+    cols = x.shape[1]
+    nseg = 0 if seg_off is None else seg_off.numel() - 1
+    for t, n in ((q_row, "q_row"), (s_row, "s_row"), (q_col, "q_col"), (s_col, "s_col")):
+        _expect(t, torch.uint8, n)
+    for t, n in ((gather_src, "gather_src"), (seg_off, "seg_off"), (seg_off32, "seg_off32")):
+        _expect(t, torch.int32, n)
+    ldc = 0 if q_col is None else q_col.shape[1]
+    _check(lib().mx_quantize(_p(x), _dt(x), rows, cols, _p(gather_src), gather_k, _p(seg_off), _p(seg_off32), nseg,
+                             seg_rows, _p(q_row), _p(s_row), _p(q_col), _p(s_col), ldc, _stream()), "mx_quantize")
+
+
+def _fill(st, **kw):
+    for k, v in kw.items():
+        if isinstance(v, torch.Tensor):
+            _p(v)
+            setattr(st, k, v.data_ptr())
+        else:
+            setattr(st, k, v)
+    return st
+
+
+def moe_grouped_gemm_fwd_mx(**kw):
+    """Keyword arguments are the fields of moe_mx_fwd_args (tensors or ints)."""
+    a = _fill(MxFwdArgs(), **kw)
+    _check(lib().moe_grouped_gemm_fwd_mx(ctypes.byref(a), _stream()), "moe_grouped_gemm_fwd_mx")
+
+
+def moe_grouped_gemm_bwd_mx(**kw):
+    """Keyword arguments are the fields of moe_mx_bwd_args (tensors or ints)."""
+    a = _fill(MxBwdArgs(), **kw)
+    _check(lib().moe_grouped_gemm_bwd_mx(ctypes.byref(a), _stream()), "moe_grouped_gemm_bwd_mx")

@@ -34,143 +34,10 @@
 //  * Epilogues (bf16 store, SwiGLU forward G/U/H, SwiGLU backward dG/dU from
 //    dH, G, U) stage each wave's 32-row slabs in LDS and move whole row
 //    segments with 16-byte loads and stores.
-#include "common.h"
-#include "kernels.h"
-#include "prof.h"
+#include "ggemm_impl.h"
 
 namespace trg {
 namespace gg {
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-
-enum Mode { RAGGED_M = 1, RAGGED_K = 2 };
-enum BSel { BSEL_NONE = 0, BSEL_GLU = 1, BSEL_KSPLIT = 2 };
-enum CSel { CSEL_NONE = 0, CSEL_MSPLIT = 1 };
-enum Epi { EPI_BF16 = 0, EPI_SWIGLU_FWD = 2, EPI_SWIGLU_BWD = 3 };
-
-constexpr int BK = 64;
-constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
-
-struct Args {
-  // Operand X[mn][k]: K-contiguous -> X[mn*ld + k]; MN-contiguous -> X[k*ld + mn]
-  const uint16_t* A;
-  long lda;
-  const uint16_t* B;
-  const uint16_t* B2;  // BSEL_GLU: W3 next to W1;  BSEL_KSPLIT: second K half
-  long ldb, b_es;      // b_es: per-expert element stride of B
-  void* C;
-  void* C2;  // CSEL_MSPLIT: rows >= split;  SWIGLU_FWD: U
-  void* C3;  // SWIGLU_FWD: H
-  long ldc, c_es;
-  const uint16_t* G;  // SWIGLU_BWD inputs
-  const uint16_t* U;
-  long ldgu;
-  int M, N, K;  // RAGGED_K: M x N output per expert;  RAGGED_M: N, K
-  int split;    // GLU: h;  KSPLIT: first K half;  MSPLIT: first M half
-  const int* offsets;
-  const int* tile_off;  // RAGGED_M: per-expert prefix of BM row tiles
-  int E, R;
-  int tiles_m, tiles_n;
-};
-
-TRG_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
-  const unsigned n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFL ? 0xFFFFFFFFu : (unsigned)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcFlags);
-}
-
-TRG_DEV void lds_load16(__amdgpu_buffer_rsrc_t rs, char* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, 0, 0, 0);
-}
-
-// K-contiguous operand: BMN rows of 64 bf16 (128-byte rows).  gfx950's LDS
-// has 64 banks and serves ds_read_b128 16 lanes at a time; a fragment read
-// hands those 16 lanes 16 consecutive rows at one logical chunk, so the 16-byte
-// chunk slot of row r is swizzled as p = c ^ ((r >> 1) & 7): two rows share a
-// 256-byte bank window and the XOR spreads the 8 row pairs over all 8 chunk
-// positions.  Wave w fills 1 KiB blocks [w*P, (w+1)*P), P = BMN/8 / waves;
-// block b holds rows 8b..8b+7.  The lane's part of the byte offset depends only on the
-// block's parity.  row8(b) -> (resource, first row of block b inside that
-// resource).
-template <int BMN, int NW, class Row8>
-TRG_DEV void load_kc(char* dst, int wave, const int (&lane_off)[2], int kbyte, int ld_bytes, Row8 row8) {
-  constexpr int PER = BMN / 8 / NW;  // 1 KiB blocks per wave
-  static_assert(PER >= 1 && (BMN / 8) % NW == 0, "blocks per wave");
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int blk = wave * PER + i;
-    int r0;
-    const __amdgpu_buffer_rsrc_t rs = row8(blk * 8, r0);
-    lds_load16(rs, dst + blk * 1024, lane_off[blk & 1] + r0 * ld_bytes + kbyte);
-  }
-}
-
-TRG_DEV int kc_lane_off(int lane, int parity, int ld_bytes) {
-  const int l8 = lane >> 3;  // row inside the block
-  const int sw = (parity << 2) | (l8 >> 1);
-  return l8 * ld_bytes + (((lane & 7) ^ sw) << 4);
-}
-
-// MN-contiguous operand: 64 k rows of BMN bf16 (row = BMN*2 bytes).  LDS
-// chunk slot p of k row kr receives global chunk p ^ ((kr & 3) << 2).  A 1 KiB
-// block covers 1024/ROWB k rows; the lane's offset inside a block depends only
-// on the block's parity (BMN = 256) or not at all (BMN = 128).
-template <int BMN>
-TRG_DEV int mnc_lane_off(int lane, int parity, int ld_bytes) {
-  constexpr int ROWB = BMN * 2;
-  const int off = parity * 1024 + lane * 16;
-  const int kr = off / ROWB;
-  const int c = ((off % ROWB) >> 4) ^ ((kr & 3) << 2);
-  return (kr - parity * (1024 / ROWB)) * ld_bytes + c * 16;
-}
-
-template <int BMN, int NW>
-TRG_DEV void load_mnc(char* dst, int wave, const int (&lane_off)[2], __amdgpu_buffer_rsrc_t rs, int krow0,
-                      int ld_bytes) {
-  constexpr int ROWB = BMN * 2;
-  constexpr int NBLK = 64 * ROWB / 1024;
-  constexpr int RPB = 1024 / ROWB;  // k rows per block
-  constexpr int PER = NBLK / NW;
-  static_assert(PER >= 1 && NBLK % NW == 0, "blocks per wave");
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int blk = wave * PER + i;
-    lds_load16(rs, dst + blk * 1024, lane_off[blk & 1] + (krow0 + blk * RPB) * ld_bytes);
-  }
-}
-
-// Fragment of 8 k-consecutive values for MFMA lane `lane` (its row / column
-// is base + (lane & 31), its k range kk*16 + (lane >> 5)*8 + [0, 8)).
-TRG_DEV bf16x8_t frag_kc(const char* s, int base, int kk, int lane) {
-  const int row = base + (lane & 31);
-  const int c = kk * 2 + (lane >> 5);
-  return *(const bf16x8_t*)(s + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
-}
-
-template <int BMN>
-TRG_DEV bf16x8_t frag_mnc(const char* s, int base, int kk, int lane) {
-  constexpr int ROWB = BMN * 2;
-  // Transpose read: the 16 lanes of a group load a 4 (k) x 16 (column) block,
-  // lane s of the group the 4 values of row s/4 starting at column 4*(s%4);
-  // after the read lane s holds column s's 4 values, k ascending.
-  const int g = lane >> 4, s16 = lane & 15;
-  const int col = base + (g & 1) * 16 + (s16 & 3) * 4;
-  const int kr = kk * 16 + (g >> 1) * 8 + (s16 >> 2);
-  const int sw = (kr & 3) << 2;
-  const int cb = ((col >> 3) ^ sw) << 4;
-  const int within = (col & 7) * 2;
-  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s + kr * ROWB + cb + within));
-  const bf16x4_t hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s + (kr + 4) * ROWB + cb + within));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-template <int BMN, bool KC>
-TRG_DEV bf16x8_t frag(const char* s, int base, int kk, int lane) {
-  if constexpr (KC) return frag_kc(s, base, kk, lane);
-  else return frag_mnc<BMN>(s, base, kk, lane);
-}
 
 template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int MODE, int BSEL, int CSEL, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
@@ -355,12 +222,8 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
     }
 
     // ---------------- epilogue ----------------
-    // Each wave stages 16-row slabs of its tile in a private LDS area (inside
-    // stage 1, while the next tile's first K step streams into stage 0) and
-    // writes whole row segments with 16-byte stores; the accumulator layout
-    // alone would scatter 8-byte pieces over 32 rows per store instruction.  Accumulator
-    // lane (lrow, lgrp) owns row lrow and, per 32-column subtile j and group q,
-    // columns j*32 + q*8 + lgrp + {0..3}.
+    // Staged through stage 1 while the next tile's first K step streams into
+    // stage 0.
     __syncthreads();  // every wave is done with the last K stage
     {
       const int tn = t + nbx;
@@ -371,142 +234,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
       }
     }
     constexpr int WLDS = STAGE / NW;  // LDS bytes per wave, inside stage 1
-    constexpr int P = WTN * 2 + 16;       // staged row pitch (16-byte aligned)
-    constexpr int PG = WTN + 16;          // GLU: WTN/2 columns per array
-    constexpr int SR = 16;                // slab rows: half an accumulator subtile
-    static_assert(EPI != EPI_SWIGLU_BWD || 2 * SR * P <= WLDS, "epilogue LDS");
-    static_assert(EPI != EPI_SWIGLU_FWD || 3 * SR * PG <= WLDS, "epilogue LDS");
-    static_assert(SR * P <= WLDS, "epilogue LDS");
-    char* wl = smem + STAGE + wave * WLDS;
-    const int lrow = lane & 31, lgrp = (lane >> 5) * 4;
-    const int mw = m0 + wm * WTM;
-    const int srow = lrow & (SR - 1);
-    auto stage4 = [&](char* slab, int pitch, int col, float v0, float v1, float v2, float v3) {
-      *(uint2*)(slab + srow * pitch + col * 2) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
-    };
-    // Slab rows -> memory: chunk c of COLS/8 16-byte chunks per row.
-    auto store_rows = [&](const char* slab, int pitch, int cols, int ms, auto&& dst) {
-      const int cpr = cols / 8;
-      for (int c = lane; c < SR * cpr; c += 64) {
-        const int row = c / cpr, cc = c - row * cpr;
-        if (ms + row < m_end) dst(ms + row, cc * 8, *(const uint4*)(slab + row * pitch + cc * 16));
-      }
-    };
-    static_for<TM * 2>([&](auto IH) {
-      constexpr int i = decltype(IH)::value / 2;
-      const int ms = mw + i * 32 + (decltype(IH)::value & 1) * SR;
-      const bool mine = (lrow / SR) == (decltype(IH)::value & 1);  // lane's row is in this half
-      if (ms < m_end) {
-        if constexpr (EPI == EPI_SWIGLU_FWD) {
-          char* sG = wl;
-          char* sU = wl + SR * PG;
-          char* sH = wl + 2 * SR * PG;
-          static_for<TN / 2>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            static_for<4>([&](auto Q) {
-              constexpr int q = decltype(Q)::value;
-              float gv[4], uv[4], hv[4];
-              static_for<4>([&](auto Rr) {
-                constexpr int r = decltype(Rr)::value;
-                gv[r] = acc[i][j][q * 4 + r];
-                uv[r] = acc[i][j + TN / 2][q * 4 + r];
-                hv[r] = silu_f(gv[r]) * uv[r];
-              });
-              const int col = j * 32 + q * 8 + lgrp;
-              if (mine) {
-                stage4(sG, PG, col, gv[0], gv[1], gv[2], gv[3]);
-                stage4(sU, PG, col, uv[0], uv[1], uv[2], uv[3]);
-                stage4(sH, PG, col, hv[0], hv[1], hv[2], hv[3]);
-              }
-            });
-          });
-          __builtin_amdgcn_wave_barrier();
-          const int hh0 = n0 / 2 + wn * (WTN / 2);
-          auto put = [&](uint16_t* base) {
-            return [&, base](int m, int c, uint4 v) {
-              if (hh0 + c < g.split) *(uint4*)(base + (long)m * g.ldc + hh0 + c) = v;
-            };
-          };
-          store_rows(sG, PG, WTN / 2, ms, put((uint16_t*)g.C));
-          store_rows(sU, PG, WTN / 2, ms, put((uint16_t*)g.C2));
-          store_rows(sH, PG, WTN / 2, ms, put((uint16_t*)g.C3));
-        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-          // dH = acc; G and U come in coalesced, dG and dU go out the same way.
-          char* sG = wl;
-          char* sU = wl + SR * P;
-          const int nw = n0 + wn * WTN;
-          for (int c = lane; c < SR * (WTN / 8); c += 64) {
-            const int row = c / (WTN / 8), cc = c - row * (WTN / 8);
-            const int m = ms + row, n = nw + cc * 8;
-            uint4 gv = make_uint4(0, 0, 0, 0), uv = gv;
-            if (m < m_end && n < g.N) {
-              gv = *(const uint4*)(g.G + (long)m * g.ldgu + n);
-              uv = *(const uint4*)(g.U + (long)m * g.ldgu + n);
-            }
-            *(uint4*)(sG + row * P + cc * 16) = gv;
-            *(uint4*)(sU + row * P + cc * 16) = uv;
-          }
-          __builtin_amdgcn_wave_barrier();
-          static_for<TN>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            static_for<4>([&](auto Q) {
-              constexpr int q = decltype(Q)::value;
-              if (!mine) return;
-              const int off = srow * P + (j * 32 + q * 8 + lgrp) * 2;
-              const uint2 gw = *(const uint2*)(sG + off);
-              const uint2 uw = *(const uint2*)(sU + off);
-              const float gg[4] = {bf_lo(gw.x), bf_hi(gw.x), bf_lo(gw.y), bf_hi(gw.y)};
-              const float uu[4] = {bf_lo(uw.x), bf_hi(uw.x), bf_lo(uw.y), bf_hi(uw.y)};
-              float dg[4], du[4];
-              static_for<4>([&](auto Rr) {
-                constexpr int r = decltype(Rr)::value;
-                const float v = acc[i][j][q * 4 + r];
-                const float sg = sigmoid_f(gg[r]);
-                du[r] = v * gg[r] * sg;
-                dg[r] = v * uu[r] * sg * (1.0f + gg[r] * (1.0f - sg));
-              });
-              *(uint2*)(sG + off) = make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
-              *(uint2*)(sU + off) = make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
-            });
-          });
-          __builtin_amdgcn_wave_barrier();
-          uint16_t* D = (uint16_t*)g.C;
-          store_rows(sG, P, WTN, ms, [&](int m, int c, uint4 v) {
-            if (nw + c < g.N) *(uint4*)(D + (long)m * g.ldc + nw + c) = v;
-          });
-          store_rows(sU, P, WTN, ms, [&](int m, int c, uint4 v) {
-            if (nw + c < g.N) *(uint4*)(D + (long)m * g.ldc + g.split + nw + c) = v;
-          });
-        } else {
-          char* sC = wl;
-          static_for<TN>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            static_for<4>([&](auto Q) {
-              constexpr int q = decltype(Q)::value;
-              if (mine)
-                stage4(sC, P, j * 32 + q * 8 + lgrp, acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1],
-                       acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-            });
-          });
-          __builtin_amdgcn_wave_barrier();
-          const int nw = n0 + wn * WTN;
-          store_rows(sC, P, WTN, ms, [&](int m, int c, uint4 v) {
-            if (nw + c < g.N) {
-              uint16_t* Cb = (uint16_t*)g.C;
-              int mr = m;
-              if constexpr (CSEL == CSEL_MSPLIT) {
-                if (m >= g.split) {
-                  Cb = (uint16_t*)g.C2;
-                  mr = m - g.split;
-                }
-              }
-              *(uint4*)(Cb + (long)e * g.c_es + (long)mr * g.ldc + nw + c) = v;
-            }
-          });
-        }
-        __builtin_amdgcn_wave_barrier();  // the slab area is rewritten next
-      }
-    });
+    epilogue<WTM, WTN, CSEL, EPI, WLDS>(g, acc, smem + STAGE + wave * WLDS, lane, wm, wn, e, m0, m_end, n0);
   }
 }
 
@@ -526,27 +254,6 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict
   }
 }
 
-static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
-
-struct DevInfo {
-  int cus = 0;
-};
-static DevInfo g_dev[64];
-
-static int grid_for(int tiles) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (g_dev[dev].cus == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    g_dev[dev].cus = n;
-  }
-  int grid = (g_dev[dev].cus + 7) / 8 * 8;  // a multiple of 8: whole XCD groups
-  const int need = (tiles + 7) / 8 * 8;
-  if (need < grid) grid = need;
-  return grid < 8 ? 8 : grid;
-}
-
 // 8 waves (two per SIMD) per 256-wide tile: while one wave of a SIMD waits
 // on LDS the other issues MFMAs.
 template <int BM, int BN, bool AKC, bool BKC, int MODE, int BSEL, int CSEL, int EPI>
@@ -556,9 +263,6 @@ static void run(const char* name, const Args& a, int max_tiles, hipStream_t s) {
   constexpr int WM = 2, WN = (BN >= 256 ? 4 : 2);
   ggemm_kernel<BM, BN, WM, WN, AKC, BKC, MODE, BSEL, CSEL, EPI><<<grid_for(max_tiles), 64 * WM * WN, 0, s>>>(a);
 }
-
-// Row tile of the ragged-M GEMMs: 256 unless experts are small on average.
-static inline bool small_rows(int E, int R) { return R < 192L * E; }
 
 }  // namespace gg
 

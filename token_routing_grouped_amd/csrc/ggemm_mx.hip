@@ -1,0 +1,428 @@
+// MXFP8 grouped GEMMs on gfx950's scaled matrix cores
+// (v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 operands, one E8M0 scale per 32
+// K values on each side, fp32 accumulation).  MXFP8 is the low-precision path
+// the pages describe as cutting both compute and the traffic between experts
+// (Olmo-core 3 overview, "Precision optimisation with MXFP8").
+//
+// Every operand arrives quantised along its own GEMM's reduction dimension and
+// stored K-contiguous (payload rows of bytes plus a scale row per 32 bytes), so
+// one kernel shape serves all six GEMMs of the layer:
+//   forward      up (SwiGLU epilogue), down                 ragged M
+//   backward     dgrad down (SwiGLU-bwd epilogue), dgrad up  ragged M
+//                wgrad down, wgrad up                        ragged K over
+//                the experts' 32-padded column segments
+// The scheduler, the HBM->LDS operand path and the epilogues are the bf16
+// kernel's (ggemm_impl.h).  Differences:
+//   * K step of 128 bytes = 128 values: LDS rows stay 128 bytes.
+//   * A fragment is 32 bytes per lane: for a 64-wide k slice, lane l (row
+//     l % 32, half h = l / 32) holds k [16h, 16h+16) and [32+16h, 32+16h+16);
+//     its scale register covers the 32-wide block h of its row (probed on the
+//     hardware).  Scales load straight into registers one K step ahead.
+//   * K tails (h % 128 != 0 never happens: K is a multiple of 128 on the
+//     ragged-M side; the wgrad segments are multiples of 32) are masked per
+//     32-wide block: the block's data is zeroed and its scale set to 1.
+#include "ggemm_impl.h"
+
+namespace trg {
+namespace gg {
+
+typedef int v8i32_t __attribute__((ext_vector_type(8)));
+typedef unsigned v2u32_t __attribute__((ext_vector_type(2)));
+
+struct MxArgs {
+  const uint8_t* sA;  // A scales: row r at sA + r*lds_a (+ the K block)
+  long lds_a;
+  const uint8_t* sB;  // B scales, per expert + e*sb_es
+  const uint8_t* sB2;
+  long lds_b, sb_es;
+  long sA_bytes, sB_bytes;  // extents (bounds for the scale loads)
+};
+
+// 4 scale bytes starting at byte `off` of the resource (any alignment).
+TRG_DEV uint32_t load_scale4(__amdgpu_buffer_rsrc_t rs, int off) {
+  const v2u32_t v = __builtin_bit_cast(v2u32_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off & ~3, 0, 0));
+  return __builtin_amdgcn_alignbyte(v.y, v.x, off & 3);
+}
+
+// 32-byte fragment of the 64-wide k slice kk for MFMA lane `lane`.
+TRG_DEV v8i32_t frag_mx(const char* s, int base, int kk, int lane) {
+  const int row = base + (lane & 31);
+  const int h = lane >> 5;
+  const int sw = (row >> 1) & 7;
+  const uint4 lo = *(const uint4*)(s + row * 128 + (((kk * 4 + h) ^ sw) << 4));
+  const uint4 hi = *(const uint4*)(s + row * 128 + (((kk * 4 + 2 + h) ^ sw) << 4));
+  v8i32_t r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+template <int BM, int BN, int WM, int WN, int MODE, int BSEL, int CSEL, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x) {
+  constexpr int BK = 128;
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int SA = BM * 128, SB = BN * 128;
+  constexpr int STAGE = SA + SB;
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "tile");
+  static_assert(BSEL != BSEL_GLU || (TN % 2 == 0), "GLU pairs subtiles");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const uint8_t* A = (const uint8_t*)g.A;
+  const uint8_t* B = (const uint8_t*)g.B;
+  const uint8_t* B2 = (const uint8_t*)g.B2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int half = lane >> 5;
+
+  int total;
+  if constexpr (MODE == RAGGED_M) total = g.tile_off[g.E] * g.tiles_n;
+  else total = g.E * g.tiles_m * g.tiles_n;
+  const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+  const int per = (total + 7) >> 3;
+  const int t_begin = xcd * per, t_end = min(total, t_begin + per);
+
+  const __amdgpu_buffer_rsrc_t rsSA = make_rsrc(x.sA, x.sA_bytes);
+  const __amdgpu_buffer_rsrc_t rsSB = make_rsrc(x.sB, x.sB_bytes);
+  const __amdgpu_buffer_rsrc_t rsSB2 = make_rsrc(BSEL != BSEL_NONE ? x.sB2 : x.sB, x.sB_bytes);
+  const int a_lane[2] = {kc_lane_off(lane, 0, (int)g.lda), kc_lane_off(lane, 1, (int)g.lda)};
+  const int b_lane[2] = {kc_lane_off(lane, 0, (int)g.ldb), kc_lane_off(lane, 1, (int)g.ldb)};
+
+  struct Tile {
+    int e, m0, m_end, n0, k0, klen;
+    __amdgpu_buffer_rsrc_t rsA, rsB, rsB2;
+  };
+  auto decode = [&](int t) {
+    Tile c;
+    if constexpr (MODE == RAGGED_M) {
+      const int mtg = t / g.tiles_n, nt = t - mtg * g.tiles_n;
+      int lo = 0, hi = g.E;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (g.tile_off[mid] <= mtg) lo = mid; else hi = mid;
+      }
+      c.e = lo;
+      c.m0 = g.offsets[lo] + (mtg - g.tile_off[lo]) * BM;
+      c.m_end = g.offsets[lo + 1];
+      c.n0 = nt * BN;
+      c.k0 = 0;
+      c.klen = g.K;
+      c.rsA = make_rsrc(A + (long)c.m0 * g.lda, (long)(g.R - c.m0) * g.lda);
+      if constexpr (BSEL == BSEL_GLU) {
+        const long hh0 = c.n0 / 2;
+        c.rsB = make_rsrc(B + (long)c.e * g.b_es + hh0 * g.ldb, (g.split - hh0) * g.ldb);
+        c.rsB2 = make_rsrc(B2 + (long)c.e * g.b_es + hh0 * g.ldb, (g.split - hh0) * g.ldb);
+      } else {
+        c.rsB = make_rsrc(B + (long)c.e * g.b_es + (long)c.n0 * g.ldb, (long)(g.N - c.n0) * g.ldb);
+        c.rsB2 = (BSEL == BSEL_KSPLIT) ? make_rsrc(B2 + (long)c.e * g.b_es + (long)c.n0 * g.ldb,
+                                                   (long)(g.N - c.n0) * g.ldb)
+                                       : c.rsB;
+      }
+    } else {
+      // weight gradients: K = the expert's 32-padded column segment
+      const int per_e = g.tiles_m * g.tiles_n;
+      c.e = t / per_e;
+      const int r = t - c.e * per_e;
+      const int mt = r / g.tiles_n, nt = r - mt * g.tiles_n;
+      c.m0 = mt * BM;
+      c.m_end = g.M;
+      c.n0 = nt * BN;
+      c.k0 = g.offsets[c.e];
+      c.klen = g.offsets[c.e + 1] - c.k0;
+      c.rsA = make_rsrc(A + (long)c.m0 * g.lda + c.k0, (long)(g.M - c.m0) * g.lda - c.k0);
+      c.rsB = make_rsrc(B + (long)c.n0 * g.ldb + c.k0, (long)(g.N - c.n0) * g.ldb - c.k0);
+      c.rsB2 = c.rsB;
+    }
+    return c;
+  };
+  auto num_k = [&](const Tile& c) { return c.klen > 0 ? (c.klen + BK - 1) / BK : 0; };
+
+  auto issue = [&](const Tile& c, int kt, int stage) {  // kt: K offset relative to c.k0
+    char* sA = smem + stage * STAGE;
+    char* sB = sA + SA;
+    load_kc<BM, NW>(sA, wave, a_lane, kt, (int)g.lda, [&](int r8, int& r0) {
+      r0 = r8;
+      return c.rsA;
+    });
+    if constexpr (BSEL == BSEL_GLU) {
+      load_kc<BN, NW>(sB, wave, b_lane, kt, (int)g.ldb, [&](int r8, int& r0) {
+        const int p = r8 % WTN;
+        r0 = (r8 / WTN) * (WTN / 2) + (p % (WTN / 2));
+        return (p >= WTN / 2) ? c.rsB2 : c.rsB;
+      });
+    } else if constexpr (BSEL == BSEL_KSPLIT) {
+      const bool second = kt >= g.split;
+      load_kc<BN, NW>(sB, wave, b_lane, second ? kt - g.split : kt, (int)g.ldb, [&](int r8, int& r0) {
+        r0 = r8;
+        return second ? c.rsB2 : c.rsB;
+      });
+    } else {
+      load_kc<BN, NW>(sB, wave, b_lane, kt, (int)g.ldb, [&](int r8, int& r0) {
+        r0 = r8;
+        return c.rsB;
+      });
+    }
+  };
+
+  // Scales of K step kt for this lane's A and B subtiles, shifted so that
+  // byte 0 / byte 2 are the lane's blocks of slice 0 / slice 1.
+  auto load_scales = [&](const Tile& c, int kt, uint32_t (&sa)[TM], uint32_t (&sb)[TN]) {
+    const int blk = (c.k0 + kt) >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = c.m0 + wm * WTM + i * 32 + (lane & 31);
+      sa[i] = load_scale4(rsSA, (int)(m * x.lds_a) + blk) >> (8 * half);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (BSEL == BSEL_GLU) {
+        const int hh = c.n0 / 2 + wn * (WTN / 2) + (j % (TN / 2)) * 32 + (lane & 31);
+        const int off = (int)(c.e * x.sb_es + hh * x.lds_b) + blk;
+        sb[j] = (j < TN / 2 ? load_scale4(rsSB, off) : load_scale4(rsSB2, off)) >> (8 * half);
+      } else if constexpr (BSEL == BSEL_KSPLIT) {
+        const int n = c.n0 + wn * WTN + j * 32 + (lane & 31);
+        const bool second = kt >= g.split;
+        const int off = (int)(c.e * x.sb_es + n * x.lds_b) + ((second ? kt - g.split : kt) >> 5);
+        sb[j] = (second ? load_scale4(rsSB2, off) : load_scale4(rsSB, off)) >> (8 * half);
+      } else {
+        const int n = c.n0 + wn * WTN + j * 32 + (lane & 31);
+        sb[j] = load_scale4(rsSB, (int)(c.e * x.sb_es + n * x.lds_b) + blk) >> (8 * half);
+      }
+    }
+  };
+
+  int t = t_begin + lb;
+  Tile cur;
+  uint32_t sa[2][TM], sb[2][TN];
+  if (t < t_end) {
+    cur = decode(t);
+    if (num_k(cur) > 0) {
+      issue(cur, 0, 0);
+      load_scales(cur, 0, sa[0], sb[0]);
+    }
+  }
+  for (; t < t_end; t += nbx) {
+    const int e = cur.e, m0 = cur.m0, m_end = cur.m_end, n0 = cur.n0;
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = num_k(cur);
+    for (int it = 0; it < nk; ++it) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // stage it&1 and this step's scales are in; stage (it+1)&1 is free
+      const int sc = it & 1;
+      if (it + 1 < nk) {
+        issue(cur, (it + 1) * BK, (it + 1) & 1);
+        load_scales(cur, (it + 1) * BK, sa[sc ^ 1], sb[sc ^ 1]);
+      }
+      const char* sA = smem + (it & 1) * STAGE;
+      const char* sB = sA + SA;
+      const int kt = it * BK;
+      static_for<BK / 64>([&](auto KK) {
+        constexpr int kk = decltype(KK)::value;
+        __builtin_amdgcn_sched_barrier(0);  // one slice's fragments live at a time
+        const int kb = kt + kk * 64;  // first k of the slice
+        // block validity of the slice's two 32-wide blocks (uniform)
+        const bool v0 = kb < cur.klen, v1 = kb + 32 < cur.klen;
+        v8i32_t af[TM], bfr[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = frag_mx(sA, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bfr[j] = frag_mx(sB, wn * WTN + j * 32, kk, lane);
+        if (!v1) {  // tail: zero the invalid block(s) of every fragment
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int z = 0; z < 8; ++z)
+              if (z >= 4 || !v0) af[i][z] = 0;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int z = 0; z < 8; ++z)
+              if (z >= 4 || !v0) bfr[j][z] = 0;
+        }
+        const bool lane_ok = half ? v1 : v0;  // this lane's scale block
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int sA_ = lane_ok ? (int)sa[sc][i] : 127 << (16 * kk);
+            const int sB_ = lane_ok ? (int)sb[sc][j] : 127 << (16 * kk);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 2 * kk, sB_,
+                                                                         2 * kk, sA_);
+          }
+      });
+    }
+
+    __syncthreads();  // every wave is done with the last K stage
+    {
+      const int tn = t + nbx;
+      if (tn < t_end) {
+        const Tile nxt = decode(tn);
+        if (num_k(nxt) > 0) {
+          issue(nxt, 0, 0);
+          load_scales(nxt, 0, sa[0], sb[0]);
+        }
+        cur = nxt;
+      }
+    }
+    constexpr int WLDS = STAGE / NW;
+    epilogue<WTM, WTN, CSEL, EPI, WLDS>(g, acc, smem + STAGE + wave * WLDS, lane, wm, wn, e, m0, m_end, n0);
+  }
+}
+
+template <int BM, int BN, int MODE, int BSEL, int CSEL, int EPI>
+static void run_mx(const char* name, const Args& a, const MxArgs& x, int max_tiles, hipStream_t s) {
+  if (max_tiles <= 0) return;
+  ProfScope ps(name, s);
+  ggemm_mx_kernel<BM, BN, 2, 4, MODE, BSEL, CSEL, EPI><<<grid_for(max_tiles), 512, 0, s>>>(a, x);
+}
+
+}  // namespace gg
+
+using namespace gg;
+
+template <int BM>
+static hipError_t mx_fwd_bm(const MxFwd& p, const int* tile_off, hipStream_t s) {
+  const int E = p.E, R = p.R, d = p.d, h = p.h;
+  const int mt_max = cdiv(R, BM) + E;
+  {  // up projection + SwiGLU: xq [R,d] x (W1q | W3q) [E,h,d]
+    Args a{};
+    a.A = (const uint16_t*)p.xq; a.lda = d;
+    a.B = (const uint16_t*)p.w1q; a.B2 = (const uint16_t*)p.w3q; a.ldb = d; a.b_es = (long)h * d;
+    a.C = p.g; a.C2 = p.u; a.C3 = p.hbuf; a.ldc = h;
+    a.N = 2 * h; a.K = d; a.split = h;
+    a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.tiles_n = cdiv(2L * h, 256);
+    MxArgs x{};
+    x.sA = p.xs; x.lds_a = d / 32; x.sA_bytes = (long)R * (d / 32);
+    x.sB = p.w1s; x.sB2 = p.w3s; x.lds_b = d / 32; x.sb_es = (long)h * (d / 32); x.sB_bytes = (long)E * h * (d / 32);
+    run_mx<BM, 256, RAGGED_M, BSEL_GLU, CSEL_NONE, EPI_SWIGLU_FWD>("ggemm_mx_up_swiglu", a, x, mt_max * a.tiles_n, s);
+  }
+  // H -> rowwise MX (down GEMM) and columnwise per expert (wgrad down)
+  {
+    ProfScope ps("mx_quantize_h", s);
+    const hipError_t err = launch_mx_quantize(p.hbuf, true, h, R, h, nullptr, 1, p.offsets, p.off32, E, 0,
+                                              (R + 31 * E + 31) / 32, p.hq, p.hs, p.hqT, p.hsT, p.r32cap, s);
+    if (err != hipSuccess) return err;
+  }
+  {  // down projection: hq [R,h] x W2q [E,d,h]
+    Args a{};
+    a.A = (const uint16_t*)p.hq; a.lda = h;
+    a.B = (const uint16_t*)p.w2q; a.ldb = h; a.b_es = (long)d * h;
+    a.C = p.yp; a.ldc = d;
+    a.N = d; a.K = h;
+    a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.tiles_n = cdiv(d, 256);
+    MxArgs x{};
+    x.sA = p.hs; x.lds_a = h / 32; x.sA_bytes = (long)R * (h / 32);
+    x.sB = p.w2s; x.lds_b = h / 32; x.sb_es = (long)d * (h / 32); x.sB_bytes = (long)E * d * (h / 32);
+    run_mx<BM, 256, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_mx_down", a, x, mt_max * a.tiles_n, s);
+  }
+  return hipGetLastError();
+}
+
+// MX tiles are 128 x 256: a 256-row fp8 tile would need more than a wave's
+// 256 registers, and at one byte per value a 128-row tile moves the same bytes
+// per flop as the 256-row bf16 tile.
+hipError_t launch_ggemm_fwd_mx(const MxFwd& p, hipStream_t s) {
+  int* tile_off = (int*)p.ws;  // [0, E]: 128-row tile prefix
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, tile_off);
+  return mx_fwd_bm<128>(p, tile_off, s);
+}
+
+template <int BM>
+static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, hipStream_t s) {
+  const int E = p.E, R = p.R, d = p.d, h = p.h;
+  const int mt_max = cdiv(R, BM) + E;
+  {  // dgrad down + SwiGLU backward: dyq [R,d] x W2 blocked along d ([h, E*d])
+    Args a{};
+    a.A = (const uint16_t*)p.dyq; a.lda = d;
+    a.B = (const uint16_t*)p.w2tq; a.ldb = (long)E * d; a.b_es = d;
+    a.C = p.dgu; a.ldc = 2L * h;
+    a.G = (const uint16_t*)p.g; a.U = (const uint16_t*)p.u; a.ldgu = h;
+    a.N = h; a.K = d; a.split = h;
+    a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.tiles_n = cdiv(h, 256);
+    MxArgs x{};
+    x.sA = p.dys; x.lds_a = d / 32; x.sA_bytes = (long)R * (d / 32);
+    x.sB = p.w2ts; x.lds_b = (long)E * d / 32; x.sb_es = d / 32; x.sB_bytes = (long)h * E * d / 32;
+    run_mx<BM, 256, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_SWIGLU_BWD>("ggemm_mx_dgrad_down_swiglu", a, x,
+                                                                    mt_max * a.tiles_n, s);
+  }
+  {
+    ProfScope ps("mx_quantize_dgu", s);
+    const hipError_t err = launch_mx_quantize(p.dgu, true, 2L * h, R, 2 * h, nullptr, 1, p.offsets, p.off32, E, 0,
+                                              (R + 31 * E + 31) / 32, p.dguq, p.dgus, p.dguqT, p.dgusT, p.r32cap, s);
+    if (err != hipSuccess) return err;
+  }
+  {  // dgrad up: dguq [R,2h] x (W1 | W3) blocked along h ([d, E*h] each)
+    Args a{};
+    a.A = (const uint16_t*)p.dguq; a.lda = 2L * h;
+    a.B = (const uint16_t*)p.w1tq; a.B2 = (const uint16_t*)p.w3tq; a.ldb = (long)E * h; a.b_es = h;
+    a.C = p.dxp; a.ldc = d;
+    a.N = d; a.K = 2 * h; a.split = h;
+    a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.tiles_n = cdiv(d, 256);
+    MxArgs x{};
+    x.sA = p.dgus; x.lds_a = 2 * h / 32; x.sA_bytes = (long)R * (2 * h / 32);
+    x.sB = p.w1ts; x.sB2 = p.w3ts; x.lds_b = (long)E * h / 32; x.sb_es = h / 32; x.sB_bytes = (long)d * E * h / 32;
+    run_mx<BM, 256, RAGGED_M, BSEL_KSPLIT, CSEL_NONE, EPI_BF16>("ggemm_mx_dgrad_up", a, x, mt_max * a.tiles_n, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
+  const int E = p.E, R = p.R, d = p.d, h = p.h;
+  int* tile_off = (int*)p.ws;
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, E, tile_off);
+  {  // dYp -> rowwise (dgrad down) and columnwise per expert (wgrad down)
+    ProfScope ps("mx_quantize_dy", s);
+    const hipError_t err = launch_mx_quantize(p.dyp, true, d, R, d, nullptr, 1, p.offsets, p.off32, E, 0,
+                                              (R + 31 * E + 31) / 32, p.dyq, p.dys, p.dyqT, p.dysT, p.r32cap, s);
+    if (err != hipSuccess) return err;
+  }
+  {
+    const hipError_t err = mx_dgrad_bm<128>(p, tile_off, s);
+    if (err != hipSuccess) return err;
+  }
+  const long sc = p.r32cap / 32;
+  {  // wgrad down: dW2[e] = dYp_e^T H_e over the expert's padded segment
+    Args a{};
+    a.A = (const uint16_t*)p.dyqT; a.lda = p.r32cap;
+    a.B = (const uint16_t*)p.hqT; a.ldb = p.r32cap;
+    a.C = p.dw2; a.ldc = h; a.c_es = (long)d * h;
+    a.M = d; a.N = h;
+    a.offsets = p.off32; a.E = E; a.R = R;
+    a.tiles_m = cdiv(d, 128); a.tiles_n = cdiv(h, 256);
+    MxArgs x{};
+    x.sA = p.dysT; x.lds_a = sc; x.sA_bytes = (long)d * sc;
+    x.sB = p.hsT; x.lds_b = sc; x.sB_bytes = (long)h * sc;
+    run_mx<128, 256, RAGGED_K, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_mx_wgrad_down", a, x, E * a.tiles_m * a.tiles_n,
+                                                               s);
+  }
+  {  // wgrad up: [dW1; dW3][e] = [dG | dU]_e^T Xp_e
+    Args a{};
+    a.A = (const uint16_t*)p.dguqT; a.lda = p.r32cap;
+    a.B = (const uint16_t*)p.xqT; a.ldb = p.r32cap;
+    a.C = p.dw1; a.C2 = p.dw3; a.ldc = d; a.c_es = (long)h * d;
+    a.M = 2 * h; a.N = d; a.split = h;
+    a.offsets = p.off32; a.E = E; a.R = R;
+    a.tiles_m = cdiv(2L * h, 128); a.tiles_n = cdiv(d, 256);
+    MxArgs x{};
+    x.sA = p.dgusT; x.lds_a = sc; x.sA_bytes = (long)2 * h * sc;
+    x.sB = p.xsT; x.lds_b = sc; x.sB_bytes = (long)d * sc;
+    run_mx<128, 256, RAGGED_K, BSEL_NONE, CSEL_MSPLIT, EPI_BF16>("ggemm_mx_wgrad_up", a, x,
+                                                                 E * a.tiles_m * a.tiles_n, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace trg

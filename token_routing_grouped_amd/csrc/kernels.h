@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/moe.h"
+
 namespace trg {
 
 // routing
@@ -55,5 +57,15 @@ hipError_t launch_ggemm_bwd_f32(const float* dyp, const float* xp, const float* 
                                 const float* w1, const float* w3, const float* w2, const int* offsets, int E, int R,
                                 int d, int h, float* dgu, float* dxp, float* dw1, float* dw3, float* dw2,
                                 hipStream_t s);
+
+// MXFP8
+hipError_t launch_mx_quantize(const void* in, bool bf16, long ld_in, int rows, int cols, const int* src, int gk,
+                              const int* seg_off, const int* seg_off32, int nseg, int seg_rows, int max_blocks32,
+                              uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, long ldc,
+                              hipStream_t s);
+typedef moe_mx_fwd_args MxFwd;
+typedef moe_mx_bwd_args MxBwd;
+hipError_t launch_ggemm_fwd_mx(const MxFwd& p, hipStream_t s);
+hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s);
 
 }  // namespace trg

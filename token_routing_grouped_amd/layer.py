@@ -23,12 +23,21 @@ from . import _abi
 
 
 class MoELayerGPU:
-    """Buffers for one layer shape.  Weights are the caller's tensors."""
+    """Buffers for one layer shape.  Weights are the caller's tensors.
 
-    def __init__(self, T: int, d: int, E: int, k: int, h: int, dtype: torch.dtype, device="cuda"):
+    mx=True runs the six grouped GEMMs in MXFP8 (E4M3 + E8M0 per 32 values,
+    each operand blocked along its own GEMM's K): the routed rows of x are
+    quantised straight from x (dispatch and quantisation in one pass), the
+    weights are quantised in both layouts every step, and H, dYp and dG|dU are
+    quantised inside the grouped-GEMM calls.  Router, combine and all outputs
+    stay bf16.
+    """
+
+    def __init__(self, T: int, d: int, E: int, k: int, h: int, dtype: torch.dtype, device="cuda", mx: bool = False):
         self.T, self.d, self.E, self.k, self.h = T, d, E, k, h
         self.R = R = T * k
         self.dtype = dtype
+        self.mx = mx
         dev = torch.device(device)
         f32, i32 = torch.float32, torch.int32
         e = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)
@@ -60,6 +69,33 @@ class MoELayerGPU:
         self.ws_route = _abi.workspace(_abi.moe_route_workspace_size(T, E, k), dev)
         self.ws_gemm = _abi.workspace(_abi.moe_grouped_gemm_workspace_size(E, R, d, h), dev)
         self.ws_router = _abi.workspace(_abi.moe_router_bwd_workspace_size(T, d, E), dev)
+        if mx:
+            self._alloc_mx(dev)
+
+    def _alloc_mx(self, dev):
+        T, d, E, k, h, R = self.T, self.d, self.E, self.k, self.h, self.R
+        u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device=dev)
+        self.r32cap = rc = (R + 31 * E + 31) // 32 * 32
+        # routed x: rowwise (up) and columnwise per expert (wgrad up)
+        self.xq, self.xs, self.xqT, self.xsT = u8(R, d), u8(R, d // 32), u8(d, rc), u8(d, rc // 32)
+        # weights: rowwise (forward) and blocked along the other dim (dgrad)
+        self.w1q, self.w1s, self.w1tq, self.w1ts = u8(E, h, d), u8(E, h, d // 32), u8(d, E * h), u8(d, E * h // 32)
+        self.w3q, self.w3s, self.w3tq, self.w3ts = u8(E, h, d), u8(E, h, d // 32), u8(d, E * h), u8(d, E * h // 32)
+        self.w2q, self.w2s, self.w2tq, self.w2ts = u8(E, d, h), u8(E, d, h // 32), u8(h, E * d), u8(h, E * d // 32)
+        self.hq, self.hs, self.hqT, self.hsT = u8(R, h), u8(R, h // 32), u8(h, rc), u8(h, rc // 32)
+        self.dyq, self.dys, self.dyqT, self.dysT = u8(R, d), u8(R, d // 32), u8(d, rc), u8(d, rc // 32)
+        self.dguq, self.dgus = u8(R, 2 * h), u8(R, 2 * h // 32)
+        self.dguqT, self.dgusT = u8(2 * h, rc), u8(2 * h, rc // 32)
+
+    def quantize_weights(self, w1, w3, w2):
+        """Both MX layouts of every expert weight (one pass per matrix)."""
+        E, d, h = self.E, self.d, self.h
+        _abi.mx_quantize(w1.view(E * h, d), E * h, self.w1q.view(E * h, d), self.w1s.view(E * h, d // 32), self.w1tq,
+                         self.w1ts, seg_rows=h)
+        _abi.mx_quantize(w3.view(E * h, d), E * h, self.w3q.view(E * h, d), self.w3s.view(E * h, d // 32), self.w3tq,
+                         self.w3ts, seg_rows=h)
+        _abi.mx_quantize(w2.view(E * d, h), E * d, self.w2q.view(E * d, h), self.w2s.view(E * d, h // 32), self.w2tq,
+                         self.w2ts, seg_rows=d)
 
     # ------------------------------------------------------------------
     def forward(self, x, wr, w1, w3, w2, forced_idx=None):
@@ -67,15 +103,37 @@ class MoELayerGPU:
         _abi.moe_route(self.logits, self.k, self.probs, self.topk_idx, self.topk_w, self.counts, self.offsets,
                        self.pos, self.src, self.ws_route, off32=self.off32, forced_idx=forced_idx,
                        err_flag=self.err_flag)
-        _abi.moe_permute(x, self.pos, self.xp)
-        _abi.moe_grouped_gemm_fwd(self.xp, w1, w3, w2, self.offsets, self.g, self.u, self.hb, self.yp, self.ws_gemm)
+        if self.mx:
+            # routed rows of x straight into their experts' MX buffers
+            _abi.mx_quantize(x, self.R, self.xq, self.xs, self.xqT, self.xsT, gather_src=self.src, gather_k=self.k,
+                             seg_off=self.offsets, seg_off32=self.off32)
+            self.quantize_weights(w1, w3, w2)
+            _abi.moe_grouped_gemm_fwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, r32cap=self.r32cap,
+                                         offsets=self.offsets, off32=self.off32, xq=self.xq, xs=self.xs, w1q=self.w1q,
+                                         w1s=self.w1s, w3q=self.w3q, w3s=self.w3s, w2q=self.w2q, w2s=self.w2s,
+                                         g=self.g, u=self.u, hbuf=self.hb, hq=self.hq, hs=self.hs, hqT=self.hqT,
+                                         hsT=self.hsT, yp=self.yp, ws=self.ws_gemm, ws_bytes=self.ws_gemm.numel())
+        else:
+            _abi.moe_permute(x, self.pos, self.xp)
+            _abi.moe_grouped_gemm_fwd(self.xp, w1, w3, w2, self.offsets, self.g, self.u, self.hb, self.yp,
+                                      self.ws_gemm)
         _abi.moe_combine(self.yp, self.topk_w, self.pos, self.y)
         return self.y
 
     def backward(self, dy, x, wr, w1, w3, w2):
         _abi.moe_combine_bwd(dy, self.yp, self.topk_w, self.pos, self.dyp, self.dgate)
-        _abi.moe_grouped_gemm_bwd(self.dyp, self.xp, self.g, self.u, self.hb, w1, w3, w2, self.offsets, self.dgu,
-                                  self.dxp, self.dw1, self.dw3, self.dw2, self.ws_gemm)
+        if self.mx:
+            _abi.moe_grouped_gemm_bwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, r32cap=self.r32cap,
+                                         offsets=self.offsets, off32=self.off32, dyp=self.dyp, dyq=self.dyq,
+                                         dys=self.dys, dyqT=self.dyqT, dysT=self.dysT, g=self.g, u=self.u,
+                                         hqT=self.hqT, hsT=self.hsT, xqT=self.xqT, xsT=self.xsT, w1tq=self.w1tq,
+                                         w1ts=self.w1ts, w3tq=self.w3tq, w3ts=self.w3ts, w2tq=self.w2tq,
+                                         w2ts=self.w2ts, dgu=self.dgu, dguq=self.dguq, dgus=self.dgus,
+                                         dguqT=self.dguqT, dgusT=self.dgusT, dxp=self.dxp, dw1=self.dw1, dw3=self.dw3,
+                                         dw2=self.dw2, ws=self.ws_gemm, ws_bytes=self.ws_gemm.numel())
+        else:
+            _abi.moe_grouped_gemm_bwd(self.dyp, self.xp, self.g, self.u, self.hb, w1, w3, w2, self.offsets, self.dgu,
+                                      self.dxp, self.dw1, self.dw3, self.dw2, self.ws_gemm)
         _abi.moe_unpermute_sum(self.dxp, self.pos, self.dx)
         _abi.moe_router_bwd(self.probs, self.topk_idx, self.dgate, x, wr, self.dx, self.dwr, self.ws_router)
         return self.dx
