@@ -142,46 +142,74 @@ __global__ __launch_bounds__(256) void route_count_kernel(const int* __restrict_
     for (int e = lane; e < E; e += 64) chunk_cnt[(long)chunk * E + e] = hw[e];
 }
 
-// One block of 1024 threads.  Thread e: exclusive scan of its expert's counts
-// over chunks, then the expert offsets and the 32-padded offsets; finally the
-// chunk bases become absolute row positions.
+// One block of 1024 threads.  Thread (e, j) = tid / TPE, tid % TPE with TPE =
+// 1024 / (E rounded up to a power of two) threads per expert owns a contiguous
+// range of chunks of expert e.  Threads are ordered expert-major, so one
+// exclusive block scan of the per-thread chunk sums gives every thread the
+// absolute row of its first entry: the counts of all lower experts plus the
+// same expert's earlier chunks.  A second scan over the experts' 32-rounded
+// counts gives off32.  Finally each thread rewrites its chunks' counts as
+// absolute starting rows.
 __global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ chunk_cnt, int nchunks, int E,
                                                           int* __restrict__ counts, int* __restrict__ offsets,
                                                           int* __restrict__ off32) {
   __shared__ int tmp[1024];
-  const int e = threadIdx.x;
-  int tot = 0;
-  if (e < E) {
-    int c = 0;
-    for (; c + 8 <= nchunks; c += 8) {
-      int vals[8];
+  __shared__ int off_s[1025];
+  const int tid = threadIdx.x;
+  int epow = 1;
+  while (epow < E) epow <<= 1;
+  const int tpe = 1024 / epow;
+  const int e = tid / tpe, j = tid - e * tpe;
+  const int per = (nchunks + tpe - 1) / tpe;
+  const int cb = j * per, ce = min(nchunks, cb + per);
+  const bool mine = e < E;
+  int sum = 0;
+  if (mine) {
+    int c = cb;
+    for (; c + 8 <= ce; c += 8) {
+      int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) vals[u] = chunk_cnt[(long)(c + u) * E + e];
+      for (int u = 0; u < 8; ++u) v[u] = chunk_cnt[(long)(c + u) * E + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        chunk_cnt[(long)(c + u) * E + e] = tot;
-        tot += vals[u];
-      }
+      for (int u = 0; u < 8; ++u) sum += v[u];
     }
-    for (; c < nchunks; ++c) {
-      int val = chunk_cnt[(long)c * E + e];
-      chunk_cnt[(long)c * E + e] = tot;
-      tot += val;
-    }
+    for (; c < ce; ++c) sum += chunk_cnt[(long)c * E + e];
   }
-  int total, total32;
-  int off = block_excl_scan_1024(e < E ? tot : 0, tmp, &total);
-  int t32 = (tot + 31) & ~31;
-  int o32 = block_excl_scan_1024(e < E ? t32 : 0, tmp, &total32);
-  if (e < E) {
-    counts[e] = tot;
-    offsets[e] = off;
+  int total;
+  const int base = block_excl_scan_1024(mine ? sum : 0, tmp, &total);
+  if (mine && j == 0) off_s[e] = base;
+  if (tid == 0) off_s[E] = total;
+  __syncthreads();
+  const int cnt_e = mine ? off_s[e + 1] - off_s[e] : 0;
+  int total32;
+  const int o32 = block_excl_scan_1024((mine && j == 0) ? (cnt_e + 31) & ~31 : 0, tmp, &total32);
+  if (mine && j == 0) {
+    counts[e] = cnt_e;
+    offsets[e] = off_s[e];
     if (off32) off32[e] = o32;
-    for (int c = 0; c < nchunks; ++c) chunk_cnt[(long)c * E + e] += off;
   }
-  if (e == 0) {
+  if (tid == 0) {
     offsets[E] = total;
     if (off32) off32[E] = total32;
+  }
+  if (mine) {
+    int run = base;
+    int c = cb;
+    for (; c + 8 <= ce; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = chunk_cnt[(long)(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        chunk_cnt[(long)(c + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; c < ce; ++c) {
+      const int v = chunk_cnt[(long)c * E + e];
+      chunk_cnt[(long)c * E + e] = run;
+      run += v;
+    }
   }
 }
 

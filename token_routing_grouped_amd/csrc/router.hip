@@ -84,16 +84,27 @@ __global__ __launch_bounds__(256) void router_dl_kernel(const float* __restrict_
 
 constexpr int kDwrChunk = 256;  // tokens per dWr partial sum
 
+// dWr partial sums over one chunk of kDwrChunk tokens.  Thread layout: 32
+// column groups of CV = 64/EB consecutive columns x 8 token lanes (the token
+// lanes of a group are neighbouring lanes of one wave, reduced with shuffles),
+// so each wave load covers whole 128-byte row pieces of x and every thread has
+// several independent loads in flight.
 template <class T, int EB>
 __global__ __launch_bounds__(256) void router_dwr_partial_kernel(const float* __restrict__ dL, const T* __restrict__ x,
                                                                  int Tn, int d, int E, float* __restrict__ part) {
+  constexpr int CV = 64 / EB;  // columns per thread; EB * CV = 64 accumulators
+  struct alignas(CV * sizeof(T)) Vec { T v[CV]; };
   __shared__ float sdl[64][EB];
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int tl = threadIdx.x & 7, cg = threadIdx.x >> 3;
+  const int c0 = blockIdx.x * (32 * CV) + cg * CV;
   const int chunk = blockIdx.y;
   const int t0 = chunk * kDwrChunk, t1 = min(Tn, t0 + kDwrChunk);
-  float acc[EB];
+  float acc[EB][CV];
 #pragma unroll
-  for (int e = 0; e < EB; ++e) acc[e] = 0.f;
+  for (int e = 0; e < EB; ++e)
+#pragma unroll
+    for (int v = 0; v < CV; ++v) acc[e][v] = 0.f;
+  const bool full = c0 + CV <= d;
   for (int tb = t0; tb < t1; tb += 64) {
     const int nt = min(64, t1 - tb);
     for (int q = threadIdx.x; q < 64 * EB; q += 256) {
@@ -101,17 +112,42 @@ __global__ __launch_bounds__(256) void router_dwr_partial_kernel(const float* __
       sdl[tt][e] = (tt < nt && e < E) ? dL[(long)(tb + tt) * E + e] : 0.f;
     }
     __syncthreads();
-    if (c < d) {
-      for (int tt = 0; tt < nt; ++tt) {
-        const float xv = Elt<T>::ld(x + (long)(tb + tt) * d + c);
+#pragma unroll 4
+    for (int tt = tl; tt < 64; tt += 8) {
+      float xv[CV];
+      if (tt < nt && full) {
+        const Vec w = *(const Vec*)(x + (long)(tb + tt) * d + c0);
 #pragma unroll
-        for (int e = 0; e < EB; ++e) acc[e] = fmaf(sdl[tt][e], xv, acc[e]);
+        for (int v = 0; v < CV; ++v) xv[v] = Elt<T>::ld(&w.v[v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < CV; ++v)
+          xv[v] = (tt < nt && c0 + v < d) ? Elt<T>::ld(x + (long)(tb + tt) * d + c0 + v) : 0.f;
       }
+#pragma unroll
+      for (int e = 0; e < EB; ++e)
+#pragma unroll
+        for (int v = 0; v < CV; ++v) acc[e][v] = fmaf(sdl[tt][e], xv[v], acc[e][v]);
     }
     __syncthreads();
   }
-  if (c < d)
-    for (int e = 0; e < E; ++e) part[((long)chunk * E + e) * d + c] = acc[e];
+  // sum the 8 token lanes (fixed order)
+#pragma unroll
+  for (int e = 0; e < EB; ++e)
+#pragma unroll
+    for (int v = 0; v < CV; ++v) {
+      float a = acc[e][v];
+      a += __shfl_xor(a, 1, 64);
+      a += __shfl_xor(a, 2, 64);
+      a += __shfl_xor(a, 4, 64);
+      acc[e][v] = a;
+    }
+  if (tl == 0) {
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int v = 0; v < CV; ++v)
+        if (c0 + v < d) part[((long)chunk * E + e) * d + c0 + v] = acc[e][v];
+  }
 }
 
 template <class T>
@@ -192,7 +228,8 @@ template <class T, int EB>
 static void bwd_valu(const float* dL, const void* x, const void* wr, int Tn, int d, int E, void* dx, void* dwr,
                      float* part, hipStream_t s) {
   const int nch = (Tn + kDwrChunk - 1) / kDwrChunk;
-  dim3 grid((d + 255) / 256, nch);
+  constexpr int cols_per_block = 32 * (64 / EB);
+  dim3 grid((d + cols_per_block - 1) / cols_per_block, nch);
   router_dwr_partial_kernel<T, EB><<<grid, 256, 0, s>>>(dL, (const T*)x, Tn, d, E, part);
   const long n = (long)E * d;
   chunk_sum_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, nch, n, (T*)dwr);
