@@ -18,9 +18,10 @@
 //     l % 32, half h = l / 32) holds k [16h, 16h+16) and [32+16h, 32+16h+16);
 //     its scale register covers the 32-wide block h of its row (probed on the
 //     hardware).  Scales load straight into registers one K step ahead.
-//   * K tails (h % 128 != 0 never happens: K is a multiple of 128 on the
-//     ragged-M side; the wgrad segments are multiples of 32) are masked per
-//     32-wide block: the block's data is zeroed and its scale set to 1.
+//   * K is a multiple of 128 on the ragged-M side (the call requires d and h
+//     to be); the weight gradients' K segments are multiples of 32, and their
+//     tails are masked per 32-wide block: the block's data is zeroed and its
+//     scale set to 1.
 #include "ggemm_impl.h"
 
 namespace trg {
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
         for (int i = 0; i < TM; ++i) af[i] = frag_mx(sA, wm * WTM + i * 32, kk, lane);
 #pragma unroll
         for (int j = 0; j < TN; ++j) bfr[j] = frag_mx(sB, wn * WTN + j * 32, kk, lane);
-        if (!v1) {  // tail: zero the invalid block(s) of every fragment
+        if (MODE == RAGGED_K && !v1) {  // tail: zero the invalid block(s) of every fragment
 #pragma unroll
           for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -248,7 +249,8 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
             for (int z = 0; z < 8; ++z)
               if (z >= 4 || !v0) bfr[j][z] = 0;
         }
-        const bool lane_ok = half ? v1 : v0;  // this lane's scale block
+        // ragged-M K is a multiple of 128: only the weight gradients have tails
+        const bool lane_ok = MODE == RAGGED_M || (half ? v1 : v0);  // this lane's scale block
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -329,13 +331,15 @@ static hipError_t mx_fwd_bm(const MxFwd& p, const int* tile_off, hipStream_t s) 
   return hipGetLastError();
 }
 
-// MX tiles are 128 x 256: a 256-row fp8 tile would need more than a wave's
-// 256 registers, and at one byte per value a 128-row tile moves the same bytes
-// per flop as the 256-row bf16 tile.
+// Ragged-M MX GEMMs use 256 x 256 tiles (128-row tiles when experts average
+// fewer than 192 rows): an fp8 K step does half a bf16 step's MFMA time per
+// byte loaded, so the per-step costs need the larger tile.  The weight
+// gradients (K-tail masking, more registers) use 128 x 256.
 hipError_t launch_ggemm_fwd_mx(const MxFwd& p, hipStream_t s) {
-  int* tile_off = (int*)p.ws;  // [0, E]: 128-row tile prefix
+  int* tile_off = (int*)p.ws;  // [0, E]: 128-row prefix, [E+1, 2E+1]: 256-row prefix
   tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, tile_off);
-  return mx_fwd_bm<128>(p, tile_off, s);
+  if (small_rows(p.E, p.R)) return mx_fwd_bm<128>(p, tile_off, s);
+  return mx_fwd_bm<256>(p, tile_off + (p.E + 1), s);
 }
 
 template <int BM>
@@ -390,7 +394,8 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   {
-    const hipError_t err = mx_dgrad_bm<128>(p, tile_off, s);
+    const hipError_t err =
+        small_rows(E, R) ? mx_dgrad_bm<128>(p, tile_off, s) : mx_dgrad_bm<256>(p, tile_off + (E + 1), s);
     if (err != hipSuccess) return err;
   }
   const long sc = p.r32cap / 32;

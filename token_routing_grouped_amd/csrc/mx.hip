@@ -55,19 +55,41 @@ TRG_DEV uint32_t e4m3_code(float x) {
   return sign | code;
 }
 
-template <class T>
-TRG_DEV float ld_elem(const T* p);
-template <>
-TRG_DEV float ld_elem<float>(const float* p) { return *p; }
-template <>
-TRG_DEV float ld_elem<uint16_t>(const uint16_t* p) { return bf2f(*p); }
+constexpr int kMxRows = 128;  // padded rows per workgroup (four 32-row blocks)
+constexpr int kMxCols = 64;   // columns per workgroup
 
-constexpr int kMxCols = 256;  // columns per workgroup
-constexpr int kMxPad = 1;     // LDS row padding (floats)
+// Segment of the 32-row block starting at padded row base32: the block's first
+// source row, the segment's end row; false past the padded row space.
+TRG_DEV bool mx_block_rows(int base32, int rows, const int* seg_off, const int* seg_off32, int nseg, int seg_rows,
+                           int& r0, int& seg_hi) {
+  if (seg_off != nullptr) {
+    if (base32 >= seg_off32[nseg]) return false;
+    int lo = 0, hi = nseg;  // last e with seg_off32[e] <= base32
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seg_off32[mid] <= base32) lo = mid; else hi = mid;
+    }
+    r0 = seg_off[lo] + (base32 - seg_off32[lo]);
+    seg_hi = seg_off[lo + 1];
+  } else {
+    // fixed-size segments of seg_rows rows (rows a multiple of seg_rows, or a
+    // single segment), each padded to a multiple of 32 rows
+    const int seg32 = (seg_rows + 31) / 32 * 32;
+    const int nsegf = (rows + seg_rows - 1) / seg_rows;
+    if (base32 >= nsegf * seg32) return false;
+    const int e = base32 / seg32;
+    r0 = e * seg_rows + (base32 - e * seg32);
+    seg_hi = min(rows, e * seg_rows + seg_rows);
+  }
+  return true;
+}
 
-// One workgroup: 32 rows of one segment's padded row space x 256 columns.
-// Thread t: row t/8, 32 columns from (t%8)*32 -> its rowwise block; then
-// column t of the tile -> its columnwise block.
+// One workgroup: 128 rows of the padded row space (four 32-row blocks, each
+// inside one segment) x 64 columns.
+//   rowwise pass: thread t -> row t/2, 32 columns from (t%2)*32;
+//   columnwise pass: thread t -> column t/4, 32-row block t%4; the four
+//   blocks of a column are neighbouring lanes, so each column's 128 payload
+//   bytes and 4 scale bytes go out as one contiguous piece.
 template <class T>
 __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, long ld_in, int rows, int cols,
                                                       const int* __restrict__ src, int gk,
@@ -76,43 +98,23 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
                                                       uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                                       uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
                                                       long ldc) {
-  __shared__ float tile[32][kMxCols + kMxPad];
+  // row stride 65 plus 16 words per 32-row block: the columnwise pass reads
+  // four blocks x 16 columns per wave from 64 distinct banks
+  __shared__ float tile[kMxRows * (kMxCols + 1) + 4 * 16];
+  auto at = [&](int r, int c) -> float& { return tile[r * (kMxCols + 1) + (r >> 5) * 16 + c]; };
   const int tid = threadIdx.x;
-  const int base32 = blockIdx.x * 32;  // row of the padded (32-aligned) segment space
+  const int base = blockIdx.x * kMxRows;
   const int col0 = blockIdx.y * kMxCols;
 
-  // segment of this 32-row block, and its source row range
-  int seg_lo, seg_hi, seg_b32;
-  if (seg_off != nullptr) {
-    if (base32 >= seg_off32[nseg]) return;
-    int lo = 0, hi = nseg;  // last e with seg_off32[e] <= base32
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (seg_off32[mid] <= base32) lo = mid; else hi = mid;
-    }
-    seg_lo = seg_off[lo];
-    seg_hi = seg_off[lo + 1];
-    seg_b32 = seg_off32[lo];
-  } else {
-    // fixed-size segments of seg_rows rows (rows a multiple of seg_rows, or
-    // a single segment), each padded to a multiple of 32 rows
-    const int seg32 = (seg_rows + 31) / 32 * 32;
-    const int nsegf = (rows + seg_rows - 1) / seg_rows;
-    if (base32 >= nsegf * seg32) return;
-    const int e = base32 / seg32;
-    seg_lo = e * seg_rows;
-    seg_hi = min(rows, seg_lo + seg_rows);
-    seg_b32 = e * seg32;
-  }
-  const int r0 = seg_lo + (base32 - seg_b32);  // first source row of the block
-
-  // ---- rowwise: thread -> (row, 32-column block)
+  // ---- rowwise
   {
-    const int i = tid >> 3, cb = (tid & 7) * 32;
-    const int r = r0 + i;
+    const int i = tid >> 1, cb = (tid & 1) * 32;
+    int r0, seg_hi;
+    const bool blk_ok = mx_block_rows(base + (i & ~31), rows, seg_off, seg_off32, nseg, seg_rows, r0, seg_hi);
+    const int r = r0 + (i & 31);
     const int c = col0 + cb;
     float v[32];
-    const bool ok = r < seg_hi && c < cols;
+    const bool ok = blk_ok && r < seg_hi && c < cols;
     if (ok) {
       long srow = r;
       if (src != nullptr) srow = src[r] / gk;
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
       for (int z = 0; z < 32; ++z) v[z] = 0.f;
     }
 #pragma unroll
-    for (int z = 0; z < 32; ++z) tile[i][cb + z] = v[z];
+    for (int z = 0; z < 32; ++z) at(i, cb + z) = v[z];
     if (ok && q_row != nullptr) {
       float amax = 0.f;
 #pragma unroll
@@ -152,25 +154,28 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
   if (q_col == nullptr) return;
   __syncthreads();
 
-  // ---- columnwise: thread -> one column, 32 rows (invalid rows are zero)
+  // ---- columnwise (rows outside a segment are zero in the tile)
   {
-    const int c = col0 + tid;
-    if (c < cols) {
+    const int cc = tid >> 2, sb = tid & 3;
+    const int c = col0 + cc;
+    int r0, seg_hi;
+    const bool blk_ok = mx_block_rows(base + sb * 32, rows, seg_off, seg_off32, nseg, seg_rows, r0, seg_hi);
+    if (blk_ok && c < cols) {
       float amax = 0.f;
 #pragma unroll
-      for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(tile[z][tid]));
+      for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(at(sb * 32 + z, cc)));
       const int s = mx_scale_exp(amax);
       uint32_t w[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         w[q] = 0;
 #pragma unroll
-        for (int z = 0; z < 4; ++z) w[q] |= e4m3_code(ldexpf(tile[q * 4 + z][tid], -s)) << (8 * z);
+        for (int z = 0; z < 4; ++z) w[q] |= e4m3_code(ldexpf(at(sb * 32 + q * 4 + z, cc), -s)) << (8 * z);
       }
-      uint4* dst = (uint4*)(q_col + (long)c * ldc + base32);
+      uint4* dst = (uint4*)(q_col + (long)c * ldc + base + sb * 32);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      s_col[(long)c * (ldc / 32) + base32 / 32] = (uint8_t)(s + 127);
+      s_col[(long)c * (ldc / 32) + (base + sb * 32) / 32] = (uint8_t)(s + 127);
     }
   }
 }
@@ -180,7 +185,7 @@ hipError_t launch_mx_quantize(const void* in, bool bf16, long ld_in, int rows, i
                               uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, long ldc,
                               hipStream_t s) {
   if (rows == 0 || max_blocks32 == 0) return hipSuccess;
-  dim3 grid(max_blocks32, (cols + kMxCols - 1) / kMxCols);
+  dim3 grid((max_blocks32 + 3) / 4, (cols + kMxCols - 1) / kMxCols);
   if (bf16)
     mx_dual_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)in, ld_in, rows, cols, src, gk, seg_off,
                                                   seg_off32, nseg, seg_rows, q_row, s_row, q_col, s_col, ldc);
