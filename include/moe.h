@@ -238,7 +238,7 @@ moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32
  * as moe_grouped_gemm_fwd / _bwd, with every GEMM operand quantised along its
  * own reduction dimension and multiplied on gfx950's scaled matrix cores
  * (fp32 accumulation, bf16 outputs).  d and h must be multiples of 128; r32cap
- * (row stride of every columnwise copy) a multiple of 32 and >= R + 31*E.
+ * (row stride of every columnwise copy) a multiple of 128 and >= R + 31*E.
  * The caller quantises x (mx_quantize with gather) and the weights; the calls
  * quantise H, dYp and dG|dU themselves (both layouts, from the stored bf16
  * values).  ws: moe_grouped_gemm_workspace_size() bytes.

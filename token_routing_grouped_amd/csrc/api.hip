@@ -414,8 +414,8 @@ static moe_status_t check_mx_dims(const char* fn, int E, int R, int d, int h, in
   if (R < 0) return fail(MOE_ERR_INVALID_ARG, "%s: R must be >= 0", fn);
   if (d <= 0 || h <= 0 || d % 128 != 0 || h % 128 != 0)
     return fail(MOE_ERR_INVALID_ARG, "%s: d and h must be positive multiples of 128", fn);
-  if (r32cap % 32 != 0 || (long)r32cap < (long)R + 31L * E)
-    return fail(MOE_ERR_INVALID_ARG, "%s: r32cap must be a multiple of 32 and >= R + 31*E", fn);
+  if (r32cap % 128 != 0 || (long)r32cap < (long)R + 31L * E)
+    return fail(MOE_ERR_INVALID_ARG, "%s: r32cap must be a multiple of 128 and >= R + 31*E", fn);
   const long widest = 2L * h > d ? 2L * h : (long)d;
   if ((long)R * widest * 2 >= (1L << 31) || (long)widest * r32cap >= (1L << 31))
     return fail(MOE_ERR_UNSUPPORTED, "%s: operands larger than 2^31 bytes", fn);

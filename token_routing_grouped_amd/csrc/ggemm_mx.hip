@@ -28,6 +28,7 @@ namespace trg {
 namespace gg {
 
 typedef int v8i32_t __attribute__((ext_vector_type(8)));
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
 typedef unsigned v2u32_t __attribute__((ext_vector_type(2)));
 
 struct MxArgs {
@@ -39,23 +40,39 @@ struct MxArgs {
   long sA_bytes, sB_bytes;  // extents (bounds for the scale loads)
 };
 
-// 4 scale bytes starting at byte `off` of the resource (any alignment).
-TRG_DEV uint32_t load_scale4(__amdgpu_buffer_rsrc_t rs, int off) {
-  const v2u32_t v = __builtin_bit_cast(v2u32_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off & ~3, 0, 0));
-  return __builtin_amdgcn_alignbyte(v.y, v.x, off & 3);
-}
+// Scale words of one K step (4 blocks of 32) as loaded: on the ragged-M side
+// every scale row starts 4-byte aligned and a K step covers 4 blocks, so one
+// aligned dword; on the ragged-K side the expert's segment starts at any
+// 32-block, so the 8 bytes around it, aligned at use by a byte shift that is
+// the same for the whole tile (scale rows are 4-byte multiples).  The words
+// are kept raw until the next step's wait, so the loads stay in flight behind
+// the MFMAs.
+template <bool KTAIL>
+struct ScaleRaw;
+template <>
+struct ScaleRaw<false> {
+  uint32_t w;
+  TRG_DEV void load(__amdgpu_buffer_rsrc_t rs, int off) { w = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0); }
+  TRG_DEV uint32_t get(int) const { return w; }
+};
+template <>
+struct ScaleRaw<true> {
+  v2u32_t w;
+  TRG_DEV void load(__amdgpu_buffer_rsrc_t rs, int off) {
+    w = __builtin_bit_cast(v2u32_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off & ~3, 0, 0));
+  }
+  TRG_DEV uint32_t get(int shift) const { return __builtin_amdgcn_alignbyte(w.y, w.x, shift); }
+};
 
 // 32-byte fragment of the 64-wide k slice kk for MFMA lane `lane`.
 TRG_DEV v8i32_t frag_mx(const char* s, int base, int kk, int lane) {
   const int row = base + (lane & 31);
   const int h = lane >> 5;
   const int sw = (row >> 1) & 7;
-  const uint4 lo = *(const uint4*)(s + row * 128 + (((kk * 4 + h) ^ sw) << 4));
-  const uint4 hi = *(const uint4*)(s + row * 128 + (((kk * 4 + 2 + h) ^ sw) << 4));
-  v8i32_t r;
-  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-  return r;
+  // native vector loads: each stays one 16-byte LDS read through to codegen
+  const v4i32_t lo = *(const v4i32_t*)(s + row * 128 + (((kk * 4 + h) ^ sw) << 4));
+  const v4i32_t hi = *(const v4i32_t*)(s + row * 128 + (((kk * 4 + 2 + h) ^ sw) << 4));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <int BM, int BN, int WM, int WN, int MODE, int BSEL, int CSEL, int EPI>
@@ -167,41 +184,46 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
     }
   };
 
-  // Scales of K step kt for this lane's A and B subtiles, shifted so that
-  // byte 0 / byte 2 are the lane's blocks of slice 0 / slice 1.
-  auto load_scales = [&](const Tile& c, int kt, uint32_t (&sa)[TM], uint32_t (&sb)[TN]) {
+  // Scales of K step kt for this lane's A and B subtiles (raw words).
+  constexpr bool KTAIL = MODE == RAGGED_K;
+  typedef ScaleRaw<KTAIL> Raw;
+  auto load_scales = [&](const Tile& c, int kt, Raw (&sa)[TM], Raw (&sb)[TN]) {
     const int blk = (c.k0 + kt) >> 5;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = c.m0 + wm * WTM + i * 32 + (lane & 31);
-      sa[i] = load_scale4(rsSA, (int)(m * x.lds_a) + blk) >> (8 * half);
+      sa[i].load(rsSA, (int)(m * x.lds_a) + blk);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       if constexpr (BSEL == BSEL_GLU) {
         const int hh = c.n0 / 2 + wn * (WTN / 2) + (j % (TN / 2)) * 32 + (lane & 31);
         const int off = (int)(c.e * x.sb_es + hh * x.lds_b) + blk;
-        sb[j] = (j < TN / 2 ? load_scale4(rsSB, off) : load_scale4(rsSB2, off)) >> (8 * half);
+        sb[j].load(j < TN / 2 ? rsSB : rsSB2, off);
       } else if constexpr (BSEL == BSEL_KSPLIT) {
         const int n = c.n0 + wn * WTN + j * 32 + (lane & 31);
         const bool second = kt >= g.split;
         const int off = (int)(c.e * x.sb_es + n * x.lds_b) + ((second ? kt - g.split : kt) >> 5);
-        sb[j] = (second ? load_scale4(rsSB2, off) : load_scale4(rsSB, off)) >> (8 * half);
+        sb[j].load(second ? rsSB2 : rsSB, off);
       } else {
         const int n = c.n0 + wn * WTN + j * 32 + (lane & 31);
-        sb[j] = load_scale4(rsSB, (int)(c.e * x.sb_es + n * x.lds_b) + blk) >> (8 * half);
+        sb[j].load(rsSB, (int)(c.e * x.sb_es + n * x.lds_b) + blk);
       }
     }
   };
 
   int t = t_begin + lb;
   Tile cur;
-  uint32_t sa[2][TM], sb[2][TN];
+  // scales in flight (next K step) and in use; plain registers, taken over
+  // once per step after the wait, pre-shifted so that byte 0 / byte 2 are the
+  // lane's blocks of slice 0 / slice 1
+  Raw sa_n[TM], sb_n[TN];
+  uint32_t sa[TM], sb[TN];
   if (t < t_end) {
     cur = decode(t);
     if (num_k(cur) > 0) {
       issue(cur, 0, 0);
-      load_scales(cur, 0, sa[0], sb[0]);
+      load_scales(cur, 0, sa_n, sb_n);
     }
   }
   for (; t < t_end; t += nbx) {
@@ -218,10 +240,16 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
     for (int it = 0; it < nk; ++it) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // stage it&1 and this step's scales are in; stage (it+1)&1 is free
-      const int sc = it & 1;
+      {
+        const int shift = KTAIL ? (cur.k0 >> 5) & 3 : 0;  // K steps are 4 blocks: same for every step
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa[i] = sa_n[i].get(shift) >> (8 * half);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb[j] = sb_n[j].get(shift) >> (8 * half);
+      }
       if (it + 1 < nk) {
+        load_scales(cur, (it + 1) * BK, sa_n, sb_n);
         issue(cur, (it + 1) * BK, (it + 1) & 1);
-        load_scales(cur, (it + 1) * BK, sa[sc ^ 1], sb[sc ^ 1]);
       }
       const char* sA = smem + (it & 1) * STAGE;
       const char* sB = sA + SA;
@@ -255,8 +283,8 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const int sA_ = lane_ok ? (int)sa[sc][i] : 127 << (16 * kk);
-            const int sB_ = lane_ok ? (int)sb[sc][j] : 127 << (16 * kk);
+            const int sA_ = lane_ok ? (int)sa[i] : 127 << (16 * kk);
+            const int sB_ = lane_ok ? (int)sb[j] : 127 << (16 * kk);
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 2 * kk, sB_,
                                                                          2 * kk, sA_);
           }
@@ -270,7 +298,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
         const Tile nxt = decode(tn);
         if (num_k(nxt) > 0) {
           issue(nxt, 0, 0);
-          load_scales(nxt, 0, sa[0], sb[0]);
+          load_scales(nxt, 0, sa_n, sb_n);
         }
         cur = nxt;
       }

@@ -75,7 +75,7 @@ class MoELayerGPU:
     def _alloc_mx(self, dev):
         T, d, E, k, h, R = self.T, self.d, self.E, self.k, self.h, self.R
         u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device=dev)
-        self.r32cap = rc = (R + 31 * E + 31) // 32 * 32
+        self.r32cap = rc = (R + 31 * E + 127) // 128 * 128  # columnwise row stride
         # routed x: rowwise (up) and columnwise per expert (wgrad up)
         self.xq, self.xs, self.xqT, self.xsT = u8(R, d), u8(R, d // 32), u8(d, rc), u8(d, rc // 32)
         # weights: rowwise (forward) and blocked along the other dim (dgrad)
