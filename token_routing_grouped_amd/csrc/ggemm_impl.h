@@ -49,8 +49,24 @@ TRG_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcFlags);
 }
 
+// 16 bytes per lane from the buffer at byte voff into LDS at lds (wave-uniform
+// base; lane i lands at lds + 16 i).  Issued as inline assembly so that the
+// compiler's wait insertion does not see an LDS write: it would otherwise
+// hold every LDS read it cannot prove disjoint (the transpose reads) until all
+// in-flight stage loads are done.  The kernels order the stages themselves
+// (vmcnt(0) + barrier before a stage is read).  M0 is saved and restored.
 TRG_DEV void lds_load16(__amdgpu_buffer_rsrc_t rs, char* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)(lds_void_t*)lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(voff), "s"(rs)
+      : "memory");
 }
 
 // K-contiguous operand: BMN rows of 64 bf16 (128-byte rows).  gfx950's LDS
