@@ -20,6 +20,14 @@ enum CSel { CSEL_NONE = 0, CSEL_MSPLIT = 1 };
 enum Epi { EPI_BF16 = 0, EPI_SWIGLU_FWD = 2, EPI_SWIGLU_BWD = 3 };
 
 constexpr int BK = 64;
+constexpr int kLdsBytes = 163840;  // gfx950 LDS per workgroup
+
+// Per-wave epilogue staging area next to the two operand stages: what is
+// left of the LDS, at most 16 KiB, in whole KiB.
+constexpr int lds_epilogue_bytes(int stage, int nw) {
+  const int r = (kLdsBytes - 2 * stage) / nw;
+  return (r > 16384 ? 16384 : r) / 1024 * 1024;
+}
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
 
 struct Args {
@@ -63,6 +71,22 @@ TRG_DEV void lds_load16(__amdgpu_buffer_rsrc_t rs, char* lds, int voff) {
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(voff), "s"(rs)
+      : "memory");
+}
+
+// 4 bytes per lane from the buffer at byte voff (4-byte aligned) into LDS at
+// lds + 4 * lane, the same way.
+TRG_DEV void lds_load4(__amdgpu_buffer_rsrc_t rs, char* lds, int voff) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)(lds_void_t*)lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(base), "v"(voff), "s"(rs)
@@ -166,13 +190,19 @@ TRG_DEV bf16x8_t frag(const char* s, int base, int kk, int lane) {
 // EPI_SWIGLU_FWD treats the first TN/2 subtiles as G and the rest as U of the
 // same hidden units and writes G, U and H = silu(G) * U; EPI_SWIGLU_BWD treats
 // the tile as dH and writes dG | dU from the stored G and U.
+template <int WTN, int EPI, int WLDS>
+constexpr int epilogue_slab_rows() {  // 16 rows when they fit the wave's area, else 8
+  return (EPI == EPI_SWIGLU_BWD ? 2 * 16 * (WTN * 2 + 16) : 16 * (WTN * 2 + 16)) <= WLDS ? 16 : 8;
+}
+
 template <int WTM, int WTN, int CSEL, int EPI, int WLDS>
 TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* wl, int lane, int wm, int wn, int e,
                       int m0, int m_end, int n0) {
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int P = WTN * 2 + 16;       // staged row pitch (16-byte aligned)
   constexpr int PG = WTN + 16;          // GLU: WTN/2 columns per array
-  constexpr int SR = 16;                // slab rows: half an accumulator subtile
+  constexpr int SR = epilogue_slab_rows<WTN, EPI, WLDS>();  // slab rows: a part of an accumulator subtile
+  constexpr int NPART = 32 / SR;
   static_assert(EPI != EPI_SWIGLU_BWD || 2 * SR * P <= WLDS, "epilogue LDS");
   static_assert(EPI != EPI_SWIGLU_FWD || 3 * SR * PG <= WLDS, "epilogue LDS");
   static_assert(SR * P <= WLDS, "epilogue LDS");
@@ -190,10 +220,30 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
       if (ms + row < m_end) dst(ms + row, cc * 8, *(const uint4*)(slab + row * pitch + cc * 16));
     }
   };
-  static_for<TM * 2>([&](auto IH) {
-    constexpr int i = decltype(IH)::value / 2;
-    const int ms = mw + i * 32 + (decltype(IH)::value & 1) * SR;
-    const bool mine = (lrow / SR) == (decltype(IH)::value & 1);  // lane's row is in this half
+  // SWIGLU_BWD: G and U of one slab, GUQ 16-byte pieces per lane, in flight
+  // one slab ahead
+  constexpr int GUQ = EPI == EPI_SWIGLU_BWD ? SR * (WTN / 8) / 64 : 1;
+  static_assert(EPI != EPI_SWIGLU_BWD || SR * (WTN / 8) % 64 == 0, "slab pieces per lane");
+  uint4 gq[GUQ], uq[GUQ];
+  auto load_gu = [&](int ms) {
+#pragma unroll
+    for (int q = 0; q < GUQ; ++q) {
+      const int c = lane + 64 * q, row = c / (WTN / 8), cc = c - row * (WTN / 8);
+      const int m = ms + row, n = n0 + wn * WTN + cc * 8;
+      gq[q] = make_uint4(0, 0, 0, 0);
+      uq[q] = gq[q];
+      if (m < m_end && n < g.N) {
+        gq[q] = *(const uint4*)(g.G + (long)m * g.ldgu + n);
+        uq[q] = *(const uint4*)(g.U + (long)m * g.ldgu + n);
+      }
+    }
+  };
+  if constexpr (EPI == EPI_SWIGLU_BWD) load_gu(mw);
+  static_for<TM * NPART>([&](auto IH) {
+    constexpr int i = decltype(IH)::value / NPART;
+    constexpr int part = decltype(IH)::value % NPART;
+    const int ms = mw + i * 32 + part * SR;
+    const bool mine = (lrow / SR) == part;  // lane's row is in this part
     if (ms < m_end) {
       if constexpr (EPI == EPI_SWIGLU_FWD) {
         char* sG = wl;
@@ -229,20 +279,19 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
         store_rows(sU, PG, WTN / 2, ms, put((uint16_t*)g.C2));
         store_rows(sH, PG, WTN / 2, ms, put((uint16_t*)g.C3));
       } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        // dH = acc; G and U come in coalesced, dG and dU go out the same way.
+        // dH = acc; G and U come in coalesced (this slab's loads were issued
+        // during the previous slab), dG and dU go out the same way.
         char* sG = wl;
         char* sU = wl + SR * P;
-        const int nw = n0 + wn * WTN;
-        for (int c = lane; c < SR * (WTN / 8); c += 64) {
-          const int row = c / (WTN / 8), cc = c - row * (WTN / 8);
-          const int m = ms + row, n = nw + cc * 8;
-          uint4 gv = make_uint4(0, 0, 0, 0), uv = gv;
-          if (m < m_end && n < g.N) {
-            gv = *(const uint4*)(g.G + (long)m * g.ldgu + n);
-            uv = *(const uint4*)(g.U + (long)m * g.ldgu + n);
-          }
-          *(uint4*)(sG + row * P + cc * 16) = gv;
-          *(uint4*)(sU + row * P + cc * 16) = uv;
+#pragma unroll
+        for (int q = 0; q < GUQ; ++q) {
+          const int c = lane + 64 * q, row = c / (WTN / 8), cc = c - row * (WTN / 8);
+          *(uint4*)(sG + row * P + cc * 16) = gq[q];
+          *(uint4*)(sU + row * P + cc * 16) = uq[q];
+        }
+        if constexpr (decltype(IH)::value + 1 < TM * NPART) {
+          constexpr int ni = (decltype(IH)::value + 1) / NPART, npart = (decltype(IH)::value + 1) % NPART;
+          load_gu(mw + ni * 32 + npart * SR);
         }
         __builtin_amdgcn_wave_barrier();
         static_for<TN>([&](auto J) {
@@ -268,6 +317,7 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
           });
         });
         __builtin_amdgcn_wave_barrier();
+        const int nw = n0 + wn * WTN;
         uint16_t* D = (uint16_t*)g.C;
         store_rows(sG, P, WTN, ms, [&](int m, int c, uint4 v) {
           if (nw + c < g.N) *(uint4*)(D + (long)m * g.ldc + nw + c) = v;

@@ -17,7 +17,8 @@
 //   * A fragment is 32 bytes per lane: for a 64-wide k slice, lane l (row
 //     l % 32, half h = l / 32) holds k [16h, 16h+16) and [32+16h, 32+16h+16);
 //     its scale register covers the 32-wide block h of its row (probed on the
-//     hardware).  Scales load straight into registers one K step ahead.
+//     hardware).  Each K step's scale words are staged in LDS with its
+//     operands.
 //   * K is a multiple of 128 on the ragged-M side (the call requires d and h
 //     to be); the weight gradients' K segments are multiples of 32, and their
 //     tails are masked per 32-wide block: the block's data is zeroed and its
@@ -29,7 +30,6 @@ namespace gg {
 
 typedef int v8i32_t __attribute__((ext_vector_type(8)));
 typedef int v4i32_t __attribute__((ext_vector_type(4)));
-typedef unsigned v2u32_t __attribute__((ext_vector_type(2)));
 
 struct MxArgs {
   const uint8_t* sA;  // A scales: row r at sA + r*lds_a (+ the K block)
@@ -38,30 +38,6 @@ struct MxArgs {
   const uint8_t* sB2;
   long lds_b, sb_es;
   long sA_bytes, sB_bytes;  // extents (bounds for the scale loads)
-};
-
-// Scale words of one K step (4 blocks of 32) as loaded: on the ragged-M side
-// every scale row starts 4-byte aligned and a K step covers 4 blocks, so one
-// aligned dword; on the ragged-K side the expert's segment starts at any
-// 32-block, so the 8 bytes around it, aligned at use by a byte shift that is
-// the same for the whole tile (scale rows are 4-byte multiples).  The words
-// are kept raw until the next step's wait, so the loads stay in flight behind
-// the MFMAs.
-template <bool KTAIL>
-struct ScaleRaw;
-template <>
-struct ScaleRaw<false> {
-  uint32_t w;
-  TRG_DEV void load(__amdgpu_buffer_rsrc_t rs, int off) { w = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0); }
-  TRG_DEV uint32_t get(int) const { return w; }
-};
-template <>
-struct ScaleRaw<true> {
-  v2u32_t w;
-  TRG_DEV void load(__amdgpu_buffer_rsrc_t rs, int off) {
-    w = __builtin_bit_cast(v2u32_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off & ~3, 0, 0));
-  }
-  TRG_DEV uint32_t get(int shift) const { return __builtin_amdgcn_alignbyte(w.y, w.x, shift); }
 };
 
 // 32-byte fragment of the 64-wide k slice kk for MFMA lane `lane`.
@@ -85,7 +61,18 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
   constexpr int STAGE = SA + SB;
   static_assert(BM % 128 == 0 && BN % 128 == 0, "tile");
   static_assert(BSEL != BSEL_GLU || (TN % 2 == 0), "GLU pairs subtiles");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // Each K step's scale words are staged in LDS next to its operands: the
+  // step's four 32-blocks of every A row and every B row, loaded once per
+  // workgroup by one 64-row chunk per wave.  Ragged-M steps start on a 4-block
+  // boundary (one dword per row); ragged-K steps start at the expert's
+  // 32-block offset, so two dwords per row are staged ([low words][high
+  // words]) and aligned at read time by a byte shift that is the same for the
+  // whole tile.
+  constexpr bool KTAIL = MODE == RAGGED_K;
+  constexpr int SCW = KTAIL ? 2 : 1;
+  constexpr int SCB = (BM + BN) * 4 * SCW;
+  static_assert((BM + BN) / 64 <= WM * WN, "one scale chunk per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 2 * SCB];
 
   const uint8_t* A = (const uint8_t*)g.A;
   const uint8_t* B = (const uint8_t*)g.B;
@@ -184,46 +171,72 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
     }
   };
 
-  // Scales of K step kt for this lane's A and B subtiles (raw words).
-  constexpr bool KTAIL = MODE == RAGGED_K;
-  typedef ScaleRaw<KTAIL> Raw;
-  auto load_scales = [&](const Tile& c, int kt, Raw (&sa)[TM], Raw (&sb)[TN]) {
-    const int blk = (c.k0 + kt) >> 5;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = c.m0 + wm * WTM + i * 32 + (lane & 31);
-      sa[i].load(rsSA, (int)(m * x.lds_a) + blk);
+  // LDS scale rows of a stage: [A rows BM][B rows BN]; GLU B rows are [W1
+  // half][W3 half] (each wave chunk reads from one of them).
+  auto issue_scales = [&](const Tile& c, int kt, int stage) {
+    char* dst = smem + 2 * STAGE + stage * SCB + wave * 256;
+    const int p = wave * 64 + lane;  // scale row of this lane
+    if constexpr (KTAIL) {
+      const int blk = ((c.k0 + kt) >> 5) & ~3;  // dword holding the step's first block
+      if (wave * 64 < BM) {
+        const int off = (c.m0 + p) * (int)x.lds_a + blk;
+        lds_load4(rsSA, dst, off);
+        lds_load4(rsSA, dst + (BM + BN) * 4, off + 4);
+      } else if (wave * 64 < BM + BN) {
+        const int off = (c.n0 + p - BM) * (int)x.lds_b + blk;
+        lds_load4(rsSB, dst, off);
+        lds_load4(rsSB, dst + (BM + BN) * 4, off + 4);
+      }
+    } else {
+      if (wave * 64 < BM) {
+        lds_load4(rsSA, dst, (c.m0 + p) * (int)x.lds_a + (kt >> 5));
+      } else if (wave * 64 < BM + BN) {
+        const int q = p - BM;
+        if constexpr (BSEL == BSEL_GLU) {
+          const bool w3 = (wave * 64 - BM) >= BN / 2;
+          const int hh = c.n0 / 2 + q - (w3 ? BN / 2 : 0);
+          lds_load4(w3 ? rsSB2 : rsSB, dst, (int)(c.e * x.sb_es) + hh * (int)x.lds_b + (kt >> 5));
+        } else if constexpr (BSEL == BSEL_KSPLIT) {
+          const bool second = kt >= g.split;
+          lds_load4(second ? rsSB2 : rsSB, dst,
+                    (int)(c.e * x.sb_es) + (c.n0 + q) * (int)x.lds_b + ((second ? kt - g.split : kt) >> 5));
+        } else {
+          lds_load4(rsSB, dst, (int)(c.e * x.sb_es) + (c.n0 + q) * (int)x.lds_b + (kt >> 5));
+        }
+      }
     }
+  };
+  // this lane's scale words of the step in `stage`, pre-shifted so that byte
+  // 0 / byte 2 are the lane's blocks of slice 0 / slice 1
+  auto lds_scales = [&](int stage, int shift, uint32_t(&sa)[TM], uint32_t(&sb)[TN]) {
+    const char* sc = smem + 2 * STAGE + stage * SCB;
+    const int l32 = lane & 31;
+    auto word = [&](int row) -> uint32_t {
+      const uint32_t lo = *(const uint32_t*)(sc + row * 4);
+      if constexpr (KTAIL) return __builtin_amdgcn_alignbyte(*(const uint32_t*)(sc + (BM + BN + row) * 4), lo, shift);
+      else return lo;
+    };
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = word(wm * WTM + i * 32 + l32) >> (8 * half);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      if constexpr (BSEL == BSEL_GLU) {
-        const int hh = c.n0 / 2 + wn * (WTN / 2) + (j % (TN / 2)) * 32 + (lane & 31);
-        const int off = (int)(c.e * x.sb_es + hh * x.lds_b) + blk;
-        sb[j].load(j < TN / 2 ? rsSB : rsSB2, off);
-      } else if constexpr (BSEL == BSEL_KSPLIT) {
-        const int n = c.n0 + wn * WTN + j * 32 + (lane & 31);
-        const bool second = kt >= g.split;
-        const int off = (int)(c.e * x.sb_es + n * x.lds_b) + ((second ? kt - g.split : kt) >> 5);
-        sb[j].load(second ? rsSB2 : rsSB, off);
-      } else {
-        const int n = c.n0 + wn * WTN + j * 32 + (lane & 31);
-        sb[j].load(rsSB, (int)(c.e * x.sb_es + n * x.lds_b) + blk);
-      }
+      int row;
+      if constexpr (BSEL == BSEL_GLU)
+        row = (j < TN / 2 ? 0 : BN / 2) + wn * (WTN / 2) + (j % (TN / 2)) * 32 + l32;
+      else
+        row = wn * WTN + j * 32 + l32;
+      sb[j] = word(BM + row) >> (8 * half);
     }
   };
 
   int t = t_begin + lb;
   Tile cur;
-  // scales in flight (next K step) and in use; plain registers, taken over
-  // once per step after the wait, pre-shifted so that byte 0 / byte 2 are the
-  // lane's blocks of slice 0 / slice 1
-  Raw sa_n[TM], sb_n[TN];
-  uint32_t sa[TM], sb[TN];
+  uint32_t sa[TM], sb[TN];  // this step's scale words
   if (t < t_end) {
     cur = decode(t);
     if (num_k(cur) > 0) {
       issue(cur, 0, 0);
-      load_scales(cur, 0, sa_n, sb_n);
+      issue_scales(cur, 0, 0);
     }
   }
   for (; t < t_end; t += nbx) {
@@ -240,54 +253,65 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
     for (int it = 0; it < nk; ++it) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // stage it&1 and this step's scales are in; stage (it+1)&1 is free
-      {
-        const int shift = KTAIL ? (cur.k0 >> 5) & 3 : 0;  // K steps are 4 blocks: same for every step
-#pragma unroll
-        for (int i = 0; i < TM; ++i) sa[i] = sa_n[i].get(shift) >> (8 * half);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) sb[j] = sb_n[j].get(shift) >> (8 * half);
-      }
+      lds_scales(it & 1, KTAIL ? (cur.k0 >> 5) & 3 : 0, sa, sb);  // K steps are 4 blocks: same shift throughout
       if (it + 1 < nk) {
-        load_scales(cur, (it + 1) * BK, sa_n, sb_n);
+        issue_scales(cur, (it + 1) * BK, (it + 1) & 1);
         issue(cur, (it + 1) * BK, (it + 1) & 1);
       }
       const char* sA = smem + (it & 1) * STAGE;
       const char* sB = sA + SA;
       const int kt = it * BK;
+      // Slice 0's fragments are read here; slice 1's are read under slice 0's
+      // MFMAs, A fragment i as soon as row i's MFMAs are issued, B fragment j
+      // after the last row's MFMA j (the registers of one slice, renamed a
+      // little by the compiler, is all that fits next to the accumulators).
+      v8i32_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = frag_mx(sA, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = frag_mx(sB, wn * WTN + j * 32, 0, lane);
       static_for<BK / 64>([&](auto KK) {
         constexpr int kk = decltype(KK)::value;
-        __builtin_amdgcn_sched_barrier(0);  // one slice's fragments live at a time
+        constexpr bool last = kk + 1 == BK / 64;
+        __builtin_amdgcn_sched_barrier(0);
         const int kb = kt + kk * 64;  // first k of the slice
         // block validity of the slice's two 32-wide blocks (uniform)
         const bool v0 = kb < cur.klen, v1 = kb + 32 < cur.klen;
-        v8i32_t af[TM], bfr[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = frag_mx(sA, wm * WTM + i * 32, kk, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[j] = frag_mx(sB, wn * WTN + j * 32, kk, lane);
-        if (MODE == RAGGED_K && !v1) {  // tail: zero the invalid block(s) of every fragment
+        if constexpr (MODE == RAGGED_K) {  // K tail: zero the invalid block(s) of every fragment
+          // (branch-free: a conditional rewrite would keep two copies of the
+          // fragments alive)
+          const int m0v = v0 ? -1 : 0, m1v = v1 ? -1 : 0;
 #pragma unroll
           for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int z = 0; z < 8; ++z)
-              if (z >= 4 || !v0) af[i][z] = 0;
+            for (int z = 0; z < 8; ++z) af[i][z] &= z < 4 ? m0v : m1v;
 #pragma unroll
           for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int z = 0; z < 8; ++z)
-              if (z >= 4 || !v0) bfr[j][z] = 0;
+            for (int z = 0; z < 8; ++z) bfr[j][z] &= z < 4 ? m0v : m1v;
         }
         // ragged-M K is a multiple of 128: only the weight gradients have tails
         const bool lane_ok = MODE == RAGGED_M || (half ? v1 : v0);  // this lane's scale block
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
+        static_for<TM>([&](auto I) {
+          constexpr int i = decltype(I)::value;
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
             const int sA_ = lane_ok ? (int)sa[i] : 127 << (16 * kk);
             const int sB_ = lane_ok ? (int)sb[j] : 127 << (16 * kk);
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 2 * kk, sB_,
                                                                          2 * kk, sA_);
+            if constexpr (!last && i == TM - 1) {
+              __builtin_amdgcn_sched_barrier(0);
+              bfr[j] = frag_mx(sB, wn * WTN + j * 32, kk + 1, lane);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
+          if constexpr (!last) {
+            __builtin_amdgcn_sched_barrier(0);
+            af[i] = frag_mx(sA, wm * WTM + i * 32, kk + 1, lane);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        });
       });
     }
 
@@ -298,7 +322,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
         const Tile nxt = decode(tn);
         if (num_k(nxt) > 0) {
           issue(nxt, 0, 0);
-          load_scales(nxt, 0, sa_n, sb_n);
+          issue_scales(nxt, 0, 0);
         }
         cur = nxt;
       }
@@ -434,11 +458,11 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
     a.C = p.dw2; a.ldc = h; a.c_es = (long)d * h;
     a.M = d; a.N = h;
     a.offsets = p.off32; a.E = E; a.R = R;
-    a.tiles_m = cdiv(d, 128); a.tiles_n = cdiv(h, 256);
+    a.tiles_m = cdiv(d, 256); a.tiles_n = cdiv(h, 256);
     MxArgs x{};
     x.sA = p.dysT; x.lds_a = sc; x.sA_bytes = (long)d * sc;
     x.sB = p.hsT; x.lds_b = sc; x.sB_bytes = (long)h * sc;
-    run_mx<128, 256, RAGGED_K, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_mx_wgrad_down", a, x, E * a.tiles_m * a.tiles_n,
+    run_mx<256, 256, RAGGED_K, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_mx_wgrad_down", a, x, E * a.tiles_m * a.tiles_n,
                                                                s);
   }
   {  // wgrad up: [dW1; dW3][e] = [dG | dU]_e^T Xp_e
@@ -448,11 +472,11 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
     a.C = p.dw1; a.C2 = p.dw3; a.ldc = d; a.c_es = (long)h * d;
     a.M = 2 * h; a.N = d; a.split = h;
     a.offsets = p.off32; a.E = E; a.R = R;
-    a.tiles_m = cdiv(2L * h, 128); a.tiles_n = cdiv(d, 256);
+    a.tiles_m = cdiv(2L * h, 256); a.tiles_n = cdiv(d, 256);
     MxArgs x{};
     x.sA = p.dgusT; x.lds_a = sc; x.sA_bytes = (long)2 * h * sc;
     x.sB = p.xsT; x.lds_b = sc; x.sB_bytes = (long)d * sc;
-    run_mx<128, 256, RAGGED_K, BSEL_NONE, CSEL_MSPLIT, EPI_BF16>("ggemm_mx_wgrad_up", a, x,
+    run_mx<256, 256, RAGGED_K, BSEL_NONE, CSEL_MSPLIT, EPI_BF16>("ggemm_mx_wgrad_up", a, x,
                                                                  E * a.tiles_m * a.tiles_n, s);
   }
   return hipGetLastError();

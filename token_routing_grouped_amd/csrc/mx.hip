@@ -38,22 +38,19 @@ TRG_DEV int mx_scale_exp(float amax) {
   return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
 
-// E4M3FN code of x (already divided by the block scale; |x| < 512),
-// nearest-even, saturating to 448, signed zero kept.
-TRG_DEV uint32_t e4m3_code(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  uint32_t code;
-  if (a < 0.015625f) {  // below 2^-6: subnormal spacing 2^-9; 8 -> smallest normal
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    const int e = ilog2_floor(a);                                   // -6 .. 8
-    const float m = __builtin_rintf(ldexpf(a, 3 - e));              // 8 .. 16, exact scaling
-    code = (uint32_t)(((e + 7) << 3) + ((int)m - 8));               // m == 16 carries into e
-  }
-  if (code > 0x7Eu) code = 0x7Eu;  // 0x7F is NaN in E4M3FN: saturate to 448
-  return sign | code;
+// E4M3FN codes of four values already divided by the block scale (|x| <
+// 512): clamped to +-448 (the saturating rule; the sign of zero survives the
+// clamp), then gfx950's OCP fp8 conversion, which rounds to nearest even and
+// keeps subnormals.  Byte z of the result is the code of the z-th value.
+TRG_DEV float sat448(float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); }
+TRG_DEV uint32_t e4m3_x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+  return (uint32_t)w;
 }
+
+TRG_DEV float to_f32(float v) { return v; }
+TRG_DEV float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 constexpr int kMxRows = 128;  // padded rows per workgroup (four 32-row blocks)
 constexpr int kMxCols = 64;   // columns per workgroup
@@ -98,13 +95,21 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
                                                       uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                                       uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
                                                       long ldc) {
-  // row stride 65 plus 16 words per 32-row block: the columnwise pass reads
-  // four blocks x 16 columns per wave from 64 distinct banks
-  __shared__ float tile[kMxRows * (kMxCols + 1) + 4 * 16];
-  auto at = [&](int r, int c) -> float& { return tile[r * (kMxCols + 1) + (r >> 5) * 16 + c]; };
+  // The tile keeps the source values in their own type (bf16: 17 KiB, so
+  // that enough workgroups are resident to keep HBM busy).  Row pitch
+  // kMxCols + PAD elements plus 64 bytes per 32-row block: the columnwise pass
+  // reads four blocks x 16 columns per wave from distinct banks.
+  constexpr int PAD = sizeof(T) == 2 ? 2 : 1;
+  constexpr int PITCH = kMxCols + PAD;
+  constexpr int BLKSKIP = 64 / sizeof(T);
+  __shared__ __attribute__((aligned(16))) T tile[kMxRows * PITCH + 4 * BLKSKIP];
+  auto at = [&](int r, int c) -> T& { return tile[r * PITCH + (r >> 5) * BLKSKIP + c]; };
   const int tid = threadIdx.x;
-  const int base = blockIdx.x * kMxRows;
-  const int col0 = blockIdx.y * kMxCols;
+  // workgroups walk the column blocks of a row band first: neighbouring
+  // workgroups read neighbouring pieces of the same source rows
+  const int ncb = (cols + kMxCols - 1) / kMxCols;
+  const int base = (int)(blockIdx.x / ncb) * kMxRows;
+  const int col0 = (int)(blockIdx.x % ncb) * kMxCols;
 
   // ---- rowwise
   {
@@ -115,24 +120,29 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
     const int c = col0 + cb;
     float v[32];
     const bool ok = blk_ok && r < seg_hi && c < cols;
+    constexpr int V = 16 / sizeof(T);
+    uint4 raw[32 / V];
     if (ok) {
       long srow = r;
       if (src != nullptr) srow = src[r] / gk;
       const T* p = in + srow * ld_in + c;
-      constexpr int V = 16 / sizeof(T);
 #pragma unroll
-      for (int q = 0; q < 32 / V; ++q) {
-        float f[V];
-        unpack16<T>(((const uint4*)p)[q], f);
-#pragma unroll
-        for (int z = 0; z < V; ++z) v[q * V + z] = f[z];
-      }
+      for (int q = 0; q < 32 / V; ++q) raw[q] = ((const uint4*)p)[q];
     } else {
 #pragma unroll
-      for (int z = 0; z < 32; ++z) v[z] = 0.f;
+      for (int q = 0; q < 32 / V; ++q) raw[q] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int z = 0; z < 32; ++z) at(i, cb + z) = v[z];
+    for (int q = 0; q < 32 / V; ++q) {
+      float f[V];
+      unpack16<T>(raw[q], f);
+#pragma unroll
+      for (int z = 0; z < V; ++z) v[q * V + z] = f[z];
+    }
+    // the source bits go to the tile as they are (16-byte stores when the row
+    // offset allows, else element stores)
+#pragma unroll
+    for (int z = 0; z < 32; ++z) at(i, cb + z) = ((const T*)raw)[z];
     if (ok && q_row != nullptr) {
       float amax = 0.f;
 #pragma unroll
@@ -140,11 +150,9 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
       const int s = mx_scale_exp(amax);
       uint32_t w[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        w[q] = 0;
-#pragma unroll
-        for (int z = 0; z < 4; ++z) w[q] |= e4m3_code(ldexpf(v[q * 4 + z], -s)) << (8 * z);
-      }
+      for (int q = 0; q < 8; ++q)
+        w[q] = e4m3_x4(ldexpf(v[q * 4], -s), ldexpf(v[q * 4 + 1], -s), ldexpf(v[q * 4 + 2], -s),
+                       ldexpf(v[q * 4 + 3], -s));
       uint4* dst = (uint4*)(q_row + (long)r * cols + c);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -163,14 +171,15 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
     if (blk_ok && c < cols) {
       float amax = 0.f;
 #pragma unroll
-      for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(at(sb * 32 + z, cc)));
+      for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(to_f32(at(sb * 32 + z, cc))));
       const int s = mx_scale_exp(amax);
       uint32_t w[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        w[q] = 0;
+        float x[4];
 #pragma unroll
-        for (int z = 0; z < 4; ++z) w[q] |= e4m3_code(ldexpf(at(sb * 32 + q * 4 + z, cc), -s)) << (8 * z);
+        for (int z = 0; z < 4; ++z) x[z] = ldexpf(to_f32(at(sb * 32 + q * 4 + z, cc)), -s);
+        w[q] = e4m3_x4(x[0], x[1], x[2], x[3]);
       }
       uint4* dst = (uint4*)(q_col + (long)c * ldc + base + sb * 32);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -185,7 +194,9 @@ hipError_t launch_mx_quantize(const void* in, bool bf16, long ld_in, int rows, i
                               uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, long ldc,
                               hipStream_t s) {
   if (rows == 0 || max_blocks32 == 0) return hipSuccess;
-  dim3 grid((max_blocks32 + 3) / 4, (cols + kMxCols - 1) / kMxCols);
+  const long nblk = (long)((max_blocks32 + 3) / 4) * ((cols + kMxCols - 1) / kMxCols);
+  if (nblk > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)nblk;
   if (bf16)
     mx_dual_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)in, ld_in, rows, cols, src, gk, seg_off,
                                                   seg_off32, nseg, seg_rows, q_row, s_row, q_col, s_col, ldc);
