@@ -53,7 +53,13 @@ TRG_DEV float to_f32(float v) { return v; }
 TRG_DEV float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 constexpr int kMxRows = 128;  // padded rows per workgroup (four 32-row blocks)
-constexpr int kMxCols = 64;   // columns per workgroup
+constexpr int kMxCols = 128;  // columns per workgroup
+
+// OR of v over the four lanes 4q .. 4q+3 (all of them take part).
+TRG_DEV uint32_t or4(uint32_t v) {
+  v |= __shfl_xor(v, 1);
+  return v | __shfl_xor(v, 2);
+}
 
 // Segment of the 32-row block starting at padded row base32: the block's first
 // source row, the segment's end row; false past the padded row space.
@@ -82,11 +88,12 @@ TRG_DEV bool mx_block_rows(int base32, int rows, const int* seg_off, const int* 
 }
 
 // One workgroup: 128 rows of the padded row space (four 32-row blocks, each
-// inside one segment) x 64 columns.
-//   rowwise pass: thread t -> row t/2, 32 columns from (t%2)*32;
-//   columnwise pass: thread t -> column t/4, 32-row block t%4; the four
-//   blocks of a column are neighbouring lanes, so each column's 128 payload
-//   bytes and 4 scale bytes go out as one contiguous piece.
+// inside one segment) x 128 columns; every thread takes two units per pass.
+//   rowwise pass: unit u -> row u/4, 32 columns from (u%4)*32: the four units
+//   of a row are neighbouring lanes, so each row's 128 payload bytes go out as
+//   one piece and its 4 scale bytes as one dword;
+//   columnwise pass: unit u -> column u/4, 32-row block u%4: likewise 128
+//   payload bytes and one scale dword per column.
 template <class T>
 __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, long ld_in, int rows, int cols,
                                                       const int* __restrict__ src, int gk,
@@ -95,96 +102,120 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
                                                       uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                                       uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
                                                       long ldc) {
-  // The tile keeps the source values in their own type (bf16: 17 KiB, so
-  // that enough workgroups are resident to keep HBM busy).  Row pitch
-  // kMxCols + PAD elements plus 64 bytes per 32-row block: the columnwise pass
-  // reads four blocks x 16 columns per wave from distinct banks.
+  // The tile keeps the source values in their own type (bf16: 33 KiB).  Row
+  // pitch kMxCols + PAD elements plus 64 bytes per 32-row block: the
+  // columnwise pass reads four blocks x 16 columns per wave from distinct
+  // banks.
   constexpr int PAD = sizeof(T) == 2 ? 2 : 1;
   constexpr int PITCH = kMxCols + PAD;
   constexpr int BLKSKIP = 64 / sizeof(T);
+  constexpr int V = 16 / sizeof(T);  // values per 16-byte load
   __shared__ __attribute__((aligned(16))) T tile[kMxRows * PITCH + 4 * BLKSKIP];
   auto at = [&](int r, int c) -> T& { return tile[r * PITCH + (r >> 5) * BLKSKIP + c]; };
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, q4 = tid & 3;
   // workgroups walk the column blocks of a row band first: neighbouring
   // workgroups read neighbouring pieces of the same source rows
   const int ncb = (cols + kMxCols - 1) / kMxCols;
   const int base = (int)(blockIdx.x / ncb) * kMxRows;
   const int col0 = (int)(blockIdx.x % ncb) * kMxCols;
+  // whole scale dwords: the row's (column's) four blocks are all in range and
+  // 4-byte aligned
+  const bool row_dw = cols % 128 == 0 && ((uintptr_t)s_row & 3) == 0;
+  const bool col_dw = ldc % 128 == 0 && ((uintptr_t)s_col & 3) == 0;
 
-  // ---- rowwise
-  {
-    const int i = tid >> 1, cb = (tid & 1) * 32;
+  // ---- rowwise: both units' loads first
+  uint4 raw[2][32 / V];
+  int rr[2];
+  bool rok[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = (tid >> 2) + 64 * k;
     int r0, seg_hi;
     const bool blk_ok = mx_block_rows(base + (i & ~31), rows, seg_off, seg_off32, nseg, seg_rows, r0, seg_hi);
-    const int r = r0 + (i & 31);
-    const int c = col0 + cb;
-    float v[32];
-    const bool ok = blk_ok && r < seg_hi && c < cols;
-    constexpr int V = 16 / sizeof(T);
-    uint4 raw[32 / V];
-    if (ok) {
-      long srow = r;
-      if (src != nullptr) srow = src[r] / gk;
-      const T* p = in + srow * ld_in + c;
+    rr[k] = r0 + (i & 31);
+    const int c = col0 + q4 * 32;
+    rok[k] = blk_ok && rr[k] < seg_hi && c < cols;
+    if (rok[k]) {
+      long srow = rr[k];
+      if (src != nullptr) srow = src[rr[k]] / gk;
+      const uint4* p = (const uint4*)(in + srow * ld_in + c);
 #pragma unroll
-      for (int q = 0; q < 32 / V; ++q) raw[q] = ((const uint4*)p)[q];
+      for (int q = 0; q < 32 / V; ++q) raw[k][q] = p[q];
     } else {
 #pragma unroll
-      for (int q = 0; q < 32 / V; ++q) raw[q] = make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < 32 / V; ++q) raw[k][q] = make_uint4(0, 0, 0, 0);
     }
+  }
 #pragma unroll
-    for (int q = 0; q < 32 / V; ++q) {
-      float f[V];
-      unpack16<T>(raw[q], f);
+  for (int k = 0; k < 2; ++k) {
+    const int i = (tid >> 2) + 64 * k;
+    const int c = col0 + q4 * 32;
+    // the source bits go to the tile as they are
 #pragma unroll
-      for (int z = 0; z < V; ++z) v[q * V + z] = f[z];
-    }
-    // the source bits go to the tile as they are (16-byte stores when the row
-    // offset allows, else element stores)
+    for (int z = 0; z < 32; ++z) at(i, q4 * 32 + z) = ((const T*)raw[k])[z];
+    if (q_row != nullptr) {
+      float v[32];
 #pragma unroll
-    for (int z = 0; z < 32; ++z) at(i, cb + z) = ((const T*)raw)[z];
-    if (ok && q_row != nullptr) {
+      for (int q = 0; q < 32 / V; ++q) unpack16<T>(raw[k][q], v + q * V);
       float amax = 0.f;
 #pragma unroll
       for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(v[z]));
       const int s = mx_scale_exp(amax);
-      uint32_t w[8];
+      const uint32_t all = or4((rok[k] ? 1u : 0u) << q4);
+      const uint32_t sw = or4((uint32_t)(s + 127) << (8 * q4));
+      if (rok[k]) {
+        uint32_t w[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        w[q] = e4m3_x4(ldexpf(v[q * 4], -s), ldexpf(v[q * 4 + 1], -s), ldexpf(v[q * 4 + 2], -s),
-                       ldexpf(v[q * 4 + 3], -s));
-      uint4* dst = (uint4*)(q_row + (long)r * cols + c);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      s_row[(long)r * (cols / 32) + c / 32] = (uint8_t)(s + 127);
+        for (int q = 0; q < 8; ++q)
+          w[q] = e4m3_x4(ldexpf(v[q * 4], -s), ldexpf(v[q * 4 + 1], -s), ldexpf(v[q * 4 + 2], -s),
+                         ldexpf(v[q * 4 + 3], -s));
+        uint4* dst = (uint4*)(q_row + (long)rr[k] * cols + c);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        uint8_t* sp = s_row + (long)rr[k] * (cols / 32) + c / 32;
+        if (row_dw && all == 15u) {
+          if (q4 == 0) *(uint32_t*)sp = sw;
+        } else {
+          *sp = (uint8_t)(s + 127);
+        }
+      }
     }
   }
   if (q_col == nullptr) return;
   __syncthreads();
 
   // ---- columnwise (rows outside a segment are zero in the tile)
-  {
-    const int cc = tid >> 2, sb = tid & 3;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int cc = (tid >> 2) + 64 * k, sb = q4;
     const int c = col0 + cc;
     int r0, seg_hi;
     const bool blk_ok = mx_block_rows(base + sb * 32, rows, seg_off, seg_off32, nseg, seg_rows, r0, seg_hi);
-    if (blk_ok && c < cols) {
-      float amax = 0.f;
+    const bool ok = blk_ok && c < cols;
+    float x[32];
 #pragma unroll
-      for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(to_f32(at(sb * 32 + z, cc))));
-      const int s = mx_scale_exp(amax);
+    for (int z = 0; z < 32; ++z) x[z] = to_f32(at(sb * 32 + z, cc));
+    float amax = 0.f;
+#pragma unroll
+    for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(x[z]));
+    const int s = mx_scale_exp(amax);
+    const uint32_t all = or4((ok ? 1u : 0u) << q4);
+    const uint32_t sw = or4((uint32_t)(s + 127) << (8 * q4));
+    if (ok) {
       uint32_t w[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        float x[4];
-#pragma unroll
-        for (int z = 0; z < 4; ++z) x[z] = ldexpf(to_f32(at(sb * 32 + q * 4 + z, cc)), -s);
-        w[q] = e4m3_x4(x[0], x[1], x[2], x[3]);
-      }
+      for (int q = 0; q < 8; ++q)
+        w[q] = e4m3_x4(ldexpf(x[q * 4], -s), ldexpf(x[q * 4 + 1], -s), ldexpf(x[q * 4 + 2], -s),
+                       ldexpf(x[q * 4 + 3], -s));
       uint4* dst = (uint4*)(q_col + (long)c * ldc + base + sb * 32);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      s_col[(long)c * (ldc / 32) + (base + sb * 32) / 32] = (uint8_t)(s + 127);
+      uint8_t* sp = s_col + (long)c * (ldc / 32) + (base + sb * 32) / 32;
+      if (col_dw && all == 15u) {
+        if (sb == 0) *(uint32_t*)sp = sw;
+      } else {
+        *sp = (uint8_t)(s + 127);
+      }
     }
   }
 }
