@@ -40,6 +40,45 @@ GEMM_KERNELS = {
 GEMM_KERNELS.update({n.replace("ggemm_", "ggemm_mx_"): m for n, m in list(GEMM_KERNELS.items())})
 
 
+# HBM traffic of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# runs (profiles/hbm_traffic.txt).  A line counts only while the kernel's
+# sources are unchanged since the counters were taken (their sha256 is part of
+# the line); otherwise the traffic is reported as null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCES = {
+    "ggemm_mx_": ["ggemm_mx.hip", "ggemm_impl.h", "common.h", "kernels.h"],
+    "ggemm_": ["ggemm.hip", "ggemm_impl.h", "common.h", "kernels.h"],
+}
+
+
+def kernel_sources_sha(kernel):
+    import hashlib
+
+    for prefix, files in KERNEL_SOURCES.items():
+        if kernel.startswith(prefix):
+            h = hashlib.sha256()
+            for f in files:
+                with open(os.path.join(ROOT, "token_routing_grouped_amd", "csrc", f), "rb") as fh:
+                    h.update(fh.read())
+            return h.hexdigest()
+    return None
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch recorded for (kernel, workload), or None."""
+    sha = kernel_sources_sha(kernel)
+    if sha is None or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("#") or "|" not in line:
+                continue
+            parts = [p.strip() for p in line.split("|")]
+            if len(parts) >= 8 and parts[0] == kernel and parts[1] == workload and parts[2] == sha:
+                return float(parts[7])
+    return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -222,7 +261,8 @@ def main():
         "ggemm_frac_own_peak": gemm_flops / (gemm_us * 1e-6) / 1e12 / gemm_peak,
         "ms_per_step_no_events": 1000.0 * elapsed_clean / a.steps,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": gemm_peak,
-                     "unit": "TFLOP/s", "frac": achieved / gemm_peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / gemm_peak,
+                     "traffic": measured_traffic(dom, f"{cfg.slug}/{mode}"),
                      "algorithmic_per_launch": f"{GEMM_KERNELS[dom]}*R*d*h = {dom_flops:.4g} flop"},
         "kernels_avg_us": {n: round(v["avg_us"], 2) for n, v in sorted(kern.items())},
         "expert_load": {"max": int(counts.max()), "mean": float(counts.mean()), "min": int(counts.min())},
