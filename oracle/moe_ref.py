@@ -236,16 +236,19 @@ def combine_backward(dy, yp, w, pos, dtype=F):
     return dyp, dgate
 
 
-def router_backward(probs, idx, dgate, x, wr, dtype=F):
+def router_backward(probs, idx, dgate, x, wr, dtype=F, aux_g=None):
     """Gradient through gates w = probs[idx] into the logits, Wr and x.
 
-    g[t, e] = dgate[t, j] where e = idx[t, j], else 0;
+    g[t, e] = dgate[t, j] where e = idx[t, j], else 0;  plus aux_g[e] for every
+    t when the balance loss is on (see oracle/balance_ref.py);
     dL = p * (g - sum_e p g)  (softmax Jacobian);  dWr = dL^T x;  dx_r = dL Wr.
     """
     p = np.asarray(probs, dtype)
     T, E = p.shape
     g = np.zeros((T, E), dtype)
     np.put_along_axis(g, np.asarray(idx), np.asarray(dgate, dtype), axis=1)
+    if aux_g is not None:
+        g = g + np.asarray(aux_g, dtype)[None, :]
     dL = p * (g - np.sum(p * g, axis=1, keepdims=True))
     dwr = dL.T @ np.asarray(x, dtype)
     dx_r = dL @ np.asarray(wr, dtype)
@@ -267,11 +270,17 @@ def layer_forward(x, wr, w1, w3, w2, k, forced_idx=None, logits=None, dtype=F):
     return dict(logits=L, **rt, xp=xp, G=G, U=U, H=H, yp=yp, y=y)
 
 
-def layer_backward(fwd, dy, x, wr, w1, w3, w2, dtype=F):
-    """Backward of ``layer_forward`` for upstream gradient dy."""
+def layer_backward(fwd, dy, x, wr, w1, w3, w2, dtype=F, aux_alpha=0.0):
+    """Backward of ``layer_forward`` for upstream gradient dy.  With aux_alpha
+    > 0 the loss also holds the balance term alpha * score
+    (oracle/balance_ref.py), whose gradient enters the router backward."""
     dyp, dgate = combine_backward(dy, fwd["yp"], fwd["w"], fwd["pos"], dtype)
     eb = experts_backward(dyp, fwd["xp"], fwd["G"], fwd["U"], fwd["H"], fwd["offsets"],
                           w1, w3, w2, dtype)
     dx_e = unpermute_sum(eb["dxp"], fwd["pos"], dtype)
-    dL, dwr, dx_r = router_backward(fwd["probs"], fwd["idx"], dgate, x, wr, dtype)
+    aux_g = None
+    if aux_alpha:
+        from oracle import balance_ref
+        aux_g = balance_ref.balance(fwd["probs"], fwd["counts"], fwd["idx"].shape[1], aux_alpha, dtype)["g"]
+    dL, dwr, dx_r = router_backward(fwd["probs"], fwd["idx"], dgate, x, wr, dtype, aux_g=aux_g)
     return dict(dyp=dyp, dgate=dgate, dlogits=dL, dx_e=dx_e, dx=dx_e + dx_r, dwr=dwr, **eb)
