@@ -154,6 +154,8 @@ def main():
     ap.add_argument("--mode", default=None, help="router | uniform | zipf (default: the config's first mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--aux-alpha", type=float, default=0.0,
+                    help="include the router balance loss (weight alpha) in every timed step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
@@ -184,7 +186,7 @@ def main():
     if mode != "router":
         forced = torch.from_numpy(inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)).to(dev)
     del inp
-    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, dev, mx=cfg.mx)
+    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, dev, mx=cfg.mx, aux_alpha=a.aux_alpha)
     args = (t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])
 
     for _ in range(a.warmup):
@@ -235,6 +237,9 @@ def main():
     gemm_peak = FP8_PEAK_TFLOPS if cfg.mx else BF16_PEAK_TFLOPS
 
     counts = layer.counts.cpu().numpy()
+    # router balance report of the same routing (after the timed region): the
+    # balance score next to the actual load of the busiest expert
+    bstats = layer.balance(alpha=a.aux_alpha).cpu().numpy()
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -266,6 +271,8 @@ def main():
                      "algorithmic_per_launch": f"{GEMM_KERNELS[dom]}*R*d*h = {dom_flops:.4g} flop"},
         "kernels_avg_us": {n: round(v["avg_us"], 2) for n, v in sorted(kern.items())},
         "expert_load": {"max": int(counts.max()), "mean": float(counts.mean()), "min": int(counts.min())},
+        "balance": {"score": float(bstats[0]), "max_over_mean": float(bstats[2]), "min_over_mean": float(bstats[3]),
+                    "aux_alpha": a.aux_alpha, "aux_loss": float(bstats[1])},
         "peak_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
     }
     if not a.no_cpu_baseline:

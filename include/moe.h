@@ -201,6 +201,35 @@ moe_status_t moe_router_bwd(const float* probs, const int32_t* topk_idx, const f
                             void* dx, void* dwr, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Router balance step.  The pages warn that a routing balance score can
+ * improve while the actual workload balance gets worse (token gerrymandering:
+ * Olmo-core 3 overview, "Empirical findings beyond raw speed") but define no
+ * score and no balance loss; the plain reading taken here:
+ *   f_e = counts[e] / (T k),  P_e = (1/T) sum_t probs[t,e]
+ *   score = E sum_e f_e P_e                 (1 when both are uniform)
+ *   loss  = alpha * score                   (auxiliary load-balance loss)
+ *   actual balance = max_e counts[e] / (T k / E)
+ *   aux_g[e] = d loss / d probs[t,e] = alpha E f_e / T   (every t)
+ *
+ * moe_balance: probs [T,E] f32 and counts [E] i32 as written by moe_route;
+ *   0 <= alpha (finite).  Writes stats[4] f32 = {score, loss, max/mean load,
+ *   min/mean load}; aux_g [E] f32 and mean_probs [E] f32 (= P) if non-null.
+ *   Deterministic (fixed-order sums).  ws: moe_balance_workspace_size(T, E)
+ *   bytes.  Everything stays on the device.
+ * moe_router_bwd_aux: moe_router_bwd with the balance loss: aux_g[e] (from
+ *   moe_balance) is added to every token's gate-gradient row before the
+ *   softmax backward, so dlogits, dwr and dx carry both terms.
+ */
+size_t moe_balance_workspace_size(int T, int E);
+moe_status_t moe_balance(const float* probs, const int32_t* counts, int T, int E, int k, float alpha,
+                         float* stats, float* aux_g, float* mean_probs, void* ws, size_t ws_bytes,
+                         void* stream);
+moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, const float* dgate,
+                                const float* aux_g, const void* x, const void* wr, int T, int d, int E,
+                                int k, int dt, void* dx, void* dwr, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
  * ---------------------------------------------------------------------------
  * MXFP8 path ("Precision optimisation with MXFP8": MXFP8 cuts both compute and
  * the traffic between experts).  Encoding (OCP microscaling): E4M3FN elements

@@ -45,6 +45,9 @@ _SIGS = {
                               _P], _I),
     "moe_router_bwd_workspace_size": ([_I, _I, _I], _Z),
     "moe_router_bwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "moe_router_bwd_aux": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "moe_balance_workspace_size": ([_I, _I], _Z),
+    "moe_balance": ([_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _Z, _P], _I),
     "mx_quantize": ([_P, _I, _I, _I, _P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P], _I),
     "moe_grouped_gemm_fwd_mx": ([_P, _P], _I),
     "moe_grouped_gemm_bwd_mx": ([_P, _P], _I),
@@ -169,6 +172,10 @@ def moe_router_bwd_workspace_size(T: int, d: int, E: int) -> int:
     return int(lib().moe_router_bwd_workspace_size(T, d, E))
 
 
+def moe_balance_workspace_size(T: int, E: int) -> int:
+    return int(lib().moe_balance_workspace_size(T, E))
+
+
 def workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
@@ -258,6 +265,32 @@ def moe_router_bwd(probs, topk_idx, dgate, x, wr, dx, dwr, ws):
     _expect(dwr, x.dtype, "dwr")
     _check(lib().moe_router_bwd(_p(probs), _p(topk_idx), _p(dgate), _p(x), _p(wr), T, d, E, k, _dt(x), _p(dx), _p(dwr),
                                 _p(ws), ws.numel(), _stream()), "moe_router_bwd")
+
+
+def moe_router_bwd_aux(probs, topk_idx, dgate, aux_g, x, wr, dx, dwr, ws):
+    """moe_router_bwd plus the balance loss's per-expert gradient aux_g [E] f32."""
+    T, d = x.shape
+    E = wr.shape[0]
+    k = topk_idx.shape[1]
+    _expect(dx, x.dtype, "dx")
+    _expect(dwr, x.dtype, "dwr")
+    _expect(aux_g, torch.float32, "aux_g")
+    _check(lib().moe_router_bwd_aux(_p(probs), _p(topk_idx), _p(dgate), _p(aux_g), _p(x), _p(wr), T, d, E, k, _dt(x),
+                                    _p(dx), _p(dwr), _p(ws), ws.numel(), _stream()), "moe_router_bwd_aux")
+
+
+def moe_balance(probs, counts, k, alpha, stats, ws, aux_g=None, mean_probs=None):
+    """Balance score, aux loss, max/min load over mean into stats [4] f32; the
+    loss's probability gradient into aux_g [E] and P into mean_probs [E]."""
+    T, E = probs.shape
+    _expect(probs, torch.float32, "probs")
+    _expect(counts, torch.int32, "counts")
+    _expect(stats, torch.float32, "stats")
+    for t, n in ((aux_g, "aux_g"), (mean_probs, "mean_probs")):
+        if t is not None:
+            _expect(t, torch.float32, n)
+    _check(lib().moe_balance(_p(probs), _p(counts), T, E, k, float(alpha), _p(stats), _p(aux_g), _p(mean_probs), _p(ws),
+                             ws.numel(), _stream()), "moe_balance")
 
 
 # ---------------------------------------------------------------------------

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libtrg_moe.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "router.hip", "gemm_bf16.hip", "ggemm.hip", "ggemm_mx.hip", "mx.hip", "gemm_f32.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "router.hip", "gemm_bf16.hip", "ggemm.hip", "ggemm_mx.hip", "mx.hip", "gemm_f32.hip", "balance.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -347,10 +347,9 @@ size_t moe_router_bwd_workspace_size(int T, int d, int E) {
   return trg::router_bwd_ws_bytes(T, d, E);
 }
 
-moe_status_t moe_router_bwd(const float* probs, const int32_t* topk_idx, const float* dgate, const void* x,
-                            const void* wr, int T, int d, int E, int k, int dt, void* dx, void* dwr, void* ws,
-                            size_t ws_bytes, void* stream) {
-  const char* fn = "moe_router_bwd";
+static moe_status_t router_bwd_impl(const char* fn, const float* probs, const int32_t* topk_idx, const float* dgate,
+                                    const float* aux_g, const void* x, const void* wr, int T, int d, int E, int k,
+                                    int dt, void* dx, void* dwr, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_dt(fn, dt));
   TRY(check_tk(fn, T, k));
   if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
@@ -367,8 +366,46 @@ moe_status_t moe_router_bwd(const float* probs, const int32_t* topk_idx, const f
   if (!aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
   TRY(check_device());
   trg::ProfScope ps(fn, (hipStream_t)stream);
-  return hip_status(fn, trg::launch_router_bwd(probs, topk_idx, dgate, x, wr, T, d, E, k, dt == MOE_BF16, dx, dwr, ws,
-                                               (hipStream_t)stream));
+  return hip_status(fn, trg::launch_router_bwd(probs, topk_idx, dgate, aux_g, x, wr, T, d, E, k, dt == MOE_BF16, dx,
+                                               dwr, ws, (hipStream_t)stream));
+}
+
+moe_status_t moe_router_bwd(const float* probs, const int32_t* topk_idx, const float* dgate, const void* x,
+                            const void* wr, int T, int d, int E, int k, int dt, void* dx, void* dwr, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return router_bwd_impl("moe_router_bwd", probs, topk_idx, dgate, nullptr, x, wr, T, d, E, k, dt, dx, dwr, ws,
+                         ws_bytes, stream);
+}
+
+moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, const float* dgate, const float* aux_g,
+                                const void* x, const void* wr, int T, int d, int E, int k, int dt, void* dx, void* dwr,
+                                void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_router_bwd_aux";
+  if (T > 0) TRY(check_ptrs(fn, {{"aux_g", aux_g}}));
+  return router_bwd_impl(fn, probs, topk_idx, dgate, aux_g, x, wr, T, d, E, k, dt, dx, dwr, ws, ws_bytes, stream);
+}
+
+size_t moe_balance_workspace_size(int T, int E) {
+  if (T < 0 || E < 1) return 0;
+  return trg::balance_ws_bytes(T, E);
+}
+
+moe_status_t moe_balance(const float* probs, const int32_t* counts, int T, int E, int k, float alpha, float* stats,
+                         float* aux_g, float* mean_probs, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_balance";
+  TRY(check_tk(fn, T, k));
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "%s: k (%d) > E (%d)", fn, k, E);
+  if (!(alpha >= 0.0f) || alpha > 1e30f) return fail(MOE_ERR_INVALID_ARG, "%s: alpha must be finite and >= 0", fn);
+  TRY(check_ptrs(fn, {{"counts", counts}, {"stats", stats}}));
+  if (T > 0) TRY(check_ptrs(fn, {{"probs", probs}}));
+  const size_t need = trg::balance_ws_bytes(T, E);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  TRY(check_device());
+  trg::ProfScope ps(fn, (hipStream_t)stream);
+  return hip_status(fn, trg::launch_balance(probs, counts, T, E, k, alpha, stats, aux_g, mean_probs, ws,
+                                            (hipStream_t)stream));
 }
 
 moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32_t* gather_src, int gather_k,

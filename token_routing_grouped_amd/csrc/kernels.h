@@ -27,8 +27,12 @@ hipError_t launch_combine_bwd(const void* dy, const void* yp, const float* w, co
 size_t router_bwd_ws_bytes(int T, int d, int E);
 hipError_t launch_router_logits(const void* x, bool bf16, const void* wr, int T, int d, int E, float* logits,
                                 hipStream_t s);
-hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dgate, const void* x, const void* wr,
-                             int T, int d, int E, int k, bool bf16, void* dx, void* dwr, void* ws, hipStream_t s);
+hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dgate, const float* aux_g,
+                             const void* x, const void* wr, int T, int d, int E, int k, bool bf16, void* dx, void* dwr,
+                             void* ws, hipStream_t s);
+size_t balance_ws_bytes(int T, int E);
+hipError_t launch_balance(const float* probs, const int* counts, int T, int E, int k, float alpha, float* stats,
+                          float* aux_g, float* mean_probs, void* ws, hipStream_t s);
 
 // grouped GEMMs
 size_t ggemm_ws_bytes(int E, int R, int d, int h);

@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void router_logits_valu_kernel(const T* __rest
 // Softmax backward through the gates.  One wave per token.
 template <int EPL>
 __global__ __launch_bounds__(256) void router_dl_kernel(const float* __restrict__ probs, const int* __restrict__ idx,
-                                                        const float* __restrict__ dgate, int Tn, int E, int k,
+                                                        const float* __restrict__ dgate,
+                                                        const float* __restrict__ aux_g, int Tn, int E, int k,
                                                         float* __restrict__ dL, uint16_t* __restrict__ dLb) {
   const int lane = threadIdx.x & 63;
   const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
@@ -60,6 +61,11 @@ __global__ __launch_bounds__(256) void router_dl_kernel(const float* __restrict_
     p[i] = e < E ? probs[(long)t * E + e] : 0.f;
     gh[i] = 0.f;
   }
+  // the balance loss's probability gradient (the same for every token), added
+  // before the gates' own (disjoint slots are written below)
+  float ga[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) ga[i] = (aux_g != nullptr && lane + 64 * i < E) ? aux_g[lane + 64 * i] : 0.f;
   for (int j = 0; j < k; ++j) {
     const int ej = idx[(long)t * k + j];
     const float gj = dgate[(long)t * k + j];
@@ -67,6 +73,8 @@ __global__ __launch_bounds__(256) void router_dl_kernel(const float* __restrict_
     for (int i = 0; i < EPL; ++i)
       if (lane + 64 * i == ej) gh[i] = gj;
   }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) gh[i] += ga[i];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) s = fmaf(p[i], gh[i], s);
@@ -245,8 +253,9 @@ static void bwd_valu_any(const float* dL, const void* x, const void* wr, int Tn,
   else bwd_valu<T, 64>(dL, x, wr, Tn, d, E, dx, dwr, part, s);
 }
 
-hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dgate, const void* x, const void* wr,
-                             int T, int d, int E, int k, bool bf16, void* dx, void* dwr, void* ws, hipStream_t s) {
+hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dgate, const float* aux_g,
+                             const void* x, const void* wr, int T, int d, int E, int k, bool bf16, void* dx, void* dwr,
+                             void* ws, hipStream_t s) {
   const bool mf = router_uses_mfma(bf16, E);
   if (!mf && E > 64) return hipErrorInvalidValue;
   char* p = (char*)ws;
@@ -263,11 +272,11 @@ hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dg
   }
   const dim3 gw((T + 3) / 4);
   uint16_t* dlb_out = mf ? dLb : nullptr;
-  if (E <= 64) router_dl_kernel<1><<<gw, 256, 0, s>>>(probs, idx, dgate, T, E, k, dL, dlb_out);
-  else if (E <= 128) router_dl_kernel<2><<<gw, 256, 0, s>>>(probs, idx, dgate, T, E, k, dL, dlb_out);
-  else if (E <= 256) router_dl_kernel<4><<<gw, 256, 0, s>>>(probs, idx, dgate, T, E, k, dL, dlb_out);
-  else if (E <= 512) router_dl_kernel<8><<<gw, 256, 0, s>>>(probs, idx, dgate, T, E, k, dL, dlb_out);
-  else router_dl_kernel<16><<<gw, 256, 0, s>>>(probs, idx, dgate, T, E, k, dL, dlb_out);
+  if (E <= 64) router_dl_kernel<1><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
+  else if (E <= 128) router_dl_kernel<2><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
+  else if (E <= 256) router_dl_kernel<4><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
+  else if (E <= 512) router_dl_kernel<8><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
+  else router_dl_kernel<16><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
   if (mf) {
     hipError_t err = launch_router_dwr_mfma(dLb, (const uint16_t*)x, (uint16_t*)dwr, part, T, d, E, s);
     if (err != hipSuccess) return err;

@@ -10,6 +10,9 @@ Backward:
 
   moe_combine_bwd -> moe_grouped_gemm_bwd -> moe_unpermute_sum -> moe_router_bwd
 
+With aux_alpha > 0 the router balance step runs after routing (moe_balance)
+and its loss's gradient enters the router backward (moe_router_bwd_aux).
+
 Every call is enqueued on torch's current stream; nothing is copied to the
 host in between (routing metadata stays on the GPU: Olmo-core 3 overview,
 "Routing and compute optimisation").
@@ -33,8 +36,10 @@ class MoELayerGPU:
     stay bf16.
     """
 
-    def __init__(self, T: int, d: int, E: int, k: int, h: int, dtype: torch.dtype, device="cuda", mx: bool = False):
+    def __init__(self, T: int, d: int, E: int, k: int, h: int, dtype: torch.dtype, device="cuda", mx: bool = False,
+                 aux_alpha: float = 0.0):
         self.T, self.d, self.E, self.k, self.h = T, d, E, k, h
+        self.aux_alpha = float(aux_alpha)
         self.R = R = T * k
         self.dtype = dtype
         self.mx = mx
@@ -69,6 +74,12 @@ class MoELayerGPU:
         self.ws_route = _abi.workspace(_abi.moe_route_workspace_size(T, E, k), dev)
         self.ws_gemm = _abi.workspace(_abi.moe_grouped_gemm_workspace_size(E, R, d, h), dev)
         self.ws_router = _abi.workspace(_abi.moe_router_bwd_workspace_size(T, d, E), dev)
+        # router balance step: {score, aux loss, max/mean load, min/mean load},
+        # the aux loss's per-expert probability gradient and mean probabilities
+        self.balance_stats = e(4, dt=f32)
+        self.aux_g = e(E, dt=f32)
+        self.mean_probs = e(E, dt=f32)
+        self.ws_balance = _abi.workspace(_abi.moe_balance_workspace_size(T, E), dev)
         if mx:
             self._alloc_mx(dev)
 
@@ -103,6 +114,8 @@ class MoELayerGPU:
         _abi.moe_route(self.logits, self.k, self.probs, self.topk_idx, self.topk_w, self.counts, self.offsets,
                        self.pos, self.src, self.ws_route, off32=self.off32, forced_idx=forced_idx,
                        err_flag=self.err_flag)
+        if self.aux_alpha > 0.0:
+            self.balance()
         if self.mx:
             # routed rows of x straight into their experts' MX buffers
             _abi.mx_quantize(x, self.R, self.xq, self.xs, self.xqT, self.xsT, gather_src=self.src, gather_k=self.k,
@@ -135,8 +148,20 @@ class MoELayerGPU:
             _abi.moe_grouped_gemm_bwd(self.dyp, self.xp, self.g, self.u, self.hb, w1, w3, w2, self.offsets, self.dgu,
                                       self.dxp, self.dw1, self.dw3, self.dw2, self.ws_gemm)
         _abi.moe_unpermute_sum(self.dxp, self.pos, self.dx)
-        _abi.moe_router_bwd(self.probs, self.topk_idx, self.dgate, x, wr, self.dx, self.dwr, self.ws_router)
+        if self.aux_alpha > 0.0:
+            _abi.moe_router_bwd_aux(self.probs, self.topk_idx, self.dgate, self.aux_g, x, wr, self.dx, self.dwr,
+                                    self.ws_router)
+        else:
+            _abi.moe_router_bwd(self.probs, self.topk_idx, self.dgate, x, wr, self.dx, self.dwr, self.ws_router)
         return self.dx
+
+    def balance(self, alpha=None):
+        """Router balance step on the current routing: balance score, aux loss,
+        actual max/min load over the mean, and the aux loss's gradient (all on
+        the device)."""
+        _abi.moe_balance(self.probs, self.counts, self.k, self.aux_alpha if alpha is None else alpha,
+                         self.balance_stats, self.ws_balance, aux_g=self.aux_g, mean_probs=self.mean_probs)
+        return self.balance_stats
 
     def step(self, x, wr, w1, w3, w2, dy, forced_idx=None):
         self.forward(x, wr, w1, w3, w2, forced_idx)
