@@ -188,8 +188,9 @@ TRG_DEV bf16x8_t frag(const char* s, int base, int kk, int lane) {
 // and, per 32-column subtile j and group q, columns j*32 + q*8 + lgrp + {0..3}.
 // EPI_BF16 writes C (rows >= split go to C2 under CSEL_MSPLIT, plus e*c_es);
 // EPI_SWIGLU_FWD treats the first TN/2 subtiles as G and the rest as U of the
-// same hidden units and writes G, U and H = silu(G) * U; EPI_SWIGLU_BWD treats
-// the tile as dH and writes dG | dU from the stored G and U.
+// same hidden units and writes G, U and H = silu(G) * U (directly from the
+// accumulators, see below); EPI_SWIGLU_BWD treats the tile as dH and writes
+// dG | dU from the stored G and U.
 template <int WTN, int EPI, int WLDS>
 constexpr int epilogue_slab_rows() {  // 16 rows when they fit the wave's area, else 8
   return (EPI == EPI_SWIGLU_BWD ? 2 * 16 * (WTN * 2 + 16) : 16 * (WTN * 2 + 16)) <= WLDS ? 16 : 8;
@@ -200,11 +201,41 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
                       int m0, int m_end, int n0) {
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int P = WTN * 2 + 16;       // staged row pitch (16-byte aligned)
-  constexpr int PG = WTN + 16;          // GLU: WTN/2 columns per array
   constexpr int SR = epilogue_slab_rows<WTN, EPI, WLDS>();  // slab rows: a part of an accumulator subtile
   constexpr int NPART = 32 / SR;
   static_assert(EPI != EPI_SWIGLU_BWD || 2 * SR * P <= WLDS, "epilogue LDS");
-  static_assert(EPI != EPI_SWIGLU_FWD || 3 * SR * PG <= WLDS, "epilogue LDS");
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    // G, U and H go out straight from the accumulators (8-byte pieces, merged
+    // into whole lines by L2): measured faster than staging three arrays
+    // through LDS.
+    const int lrow = lane & 31, lgrp = (lane >> 5) * 4;
+    const int hh0 = n0 / 2 + wn * (WTN / 2);
+    static_for<TM>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const int m = m0 + wm * WTM + i * 32 + lrow;
+      if (m >= m_end) return;
+      static_for<TN / 2>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        static_for<4>([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          const int c = hh0 + j * 32 + q * 8 + lgrp;
+          if (c >= g.split) return;
+          float gv[4], uv[4], hv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            gv[r] = acc[i][j][q * 4 + r];
+            uv[r] = acc[i][j + TN / 2][q * 4 + r];
+            hv[r] = silu_f(gv[r]) * uv[r];
+          }
+          const long off = (long)m * g.ldc + c;
+          *(uint2*)((uint16_t*)g.C + off) = make_uint2(pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3]));
+          *(uint2*)((uint16_t*)g.C2 + off) = make_uint2(pack_bf2(uv[0], uv[1]), pack_bf2(uv[2], uv[3]));
+          *(uint2*)((uint16_t*)g.C3 + off) = make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
+        });
+      });
+    });
+    return;
+  }
   static_assert(SR * P <= WLDS, "epilogue LDS");
   const int lrow = lane & 31, lgrp = (lane >> 5) * 4;
   const int mw = m0 + wm * WTM;
@@ -245,40 +276,7 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
     const int ms = mw + i * 32 + part * SR;
     const bool mine = (lrow / SR) == part;  // lane's row is in this part
     if (ms < m_end) {
-      if constexpr (EPI == EPI_SWIGLU_FWD) {
-        char* sG = wl;
-        char* sU = wl + SR * PG;
-        char* sH = wl + 2 * SR * PG;
-        static_for<TN / 2>([&](auto J) {
-          constexpr int j = decltype(J)::value;
-          static_for<4>([&](auto Q) {
-            constexpr int q = decltype(Q)::value;
-            float gv[4], uv[4], hv[4];
-            static_for<4>([&](auto Rr) {
-              constexpr int r = decltype(Rr)::value;
-              gv[r] = acc[i][j][q * 4 + r];
-              uv[r] = acc[i][j + TN / 2][q * 4 + r];
-              hv[r] = silu_f(gv[r]) * uv[r];
-            });
-            const int col = j * 32 + q * 8 + lgrp;
-            if (mine) {
-              stage4(sG, PG, col, gv[0], gv[1], gv[2], gv[3]);
-              stage4(sU, PG, col, uv[0], uv[1], uv[2], uv[3]);
-              stage4(sH, PG, col, hv[0], hv[1], hv[2], hv[3]);
-            }
-          });
-        });
-        __builtin_amdgcn_wave_barrier();
-        const int hh0 = n0 / 2 + wn * (WTN / 2);
-        auto put = [&](uint16_t* base) {
-          return [&, base](int m, int c, uint4 v) {
-            if (hh0 + c < g.split) *(uint4*)(base + (long)m * g.ldc + hh0 + c) = v;
-          };
-        };
-        store_rows(sG, PG, WTN / 2, ms, put((uint16_t*)g.C));
-        store_rows(sU, PG, WTN / 2, ms, put((uint16_t*)g.C2));
-        store_rows(sH, PG, WTN / 2, ms, put((uint16_t*)g.C3));
-      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+      if constexpr (EPI == EPI_SWIGLU_BWD) {
         // dH = acc; G and U come in coalesced (this slab's loads were issued
         // during the previous slab), dG and dU go out the same way.
         char* sG = wl;
