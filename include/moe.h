@@ -164,6 +164,10 @@ moe_status_t moe_unpermute_sum(const void* dxp, const int32_t* pos, int T, int d
  * and a second launch yp = hbuf w2[e]^T.  The tile map is derived on the
  * device from offsets.  ws: moe_grouped_gemm_workspace_size() bytes.
  * bf16 needs d and h to be multiples of 64 and R * max(d, 2h) * 2 < 2^31.
+ * Memory-lean forward (bf16): g and/or u may be null, then they are not
+ * stored; the backward recomputes them with moe_grouped_gemm_recompute_gu
+ * (bit-identical to what this call would have stored), so only xp, hbuf and
+ * yp have to live from the forward to the backward.
  */
 size_t moe_grouped_gemm_workspace_size(int E, int R, int d, int h);
 moe_status_t moe_grouped_gemm_fwd(const void* xp, const void* w1, const void* w3, const void* w2,
@@ -181,6 +185,17 @@ moe_status_t moe_grouped_gemm_fwd(const void* xp, const void* w1, const void* w3
  * Weight gradients are accumulated in fp32 over the whole segment and rounded
  * once; an expert with no rows gets zero gradients.
  */
+/*
+ * moe_grouped_gemm_recompute_gu: the up projection of moe_grouped_gemm_fwd
+ * alone, writing g = xp w1[e]^T and u = xp w3[e]^T (bf16, [R,h] each) and not
+ * hbuf: the recompute of the memory-lean backward, which trades activation
+ * memory for one more up projection.  Same arguments, layouts and workspace
+ * as moe_grouped_gemm_fwd.
+ */
+moe_status_t moe_grouped_gemm_recompute_gu(const void* xp, const void* w1, const void* w3,
+                                           const int32_t* offsets, int E, int R, int d, int h, int dt,
+                                           void* g, void* u, void* ws, size_t ws_bytes, void* stream);
+
 moe_status_t moe_grouped_gemm_bwd(const void* dyp, const void* xp, const void* g, const void* u,
                                   const void* hbuf, const void* w1, const void* w3,
                                   const void* w2, const int32_t* offsets, int E, int R, int d,
@@ -310,6 +325,13 @@ typedef struct {
 
 moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* args, void* stream);
 moe_status_t moe_grouped_gemm_bwd_mx(const moe_mx_bwd_args* args, void* stream);
+/*
+ * Memory-lean MXFP8: moe_grouped_gemm_fwd_mx accepts g = u = null (not
+ * stored); moe_grouped_gemm_recompute_gu_mx then runs the MX up projection
+ * alone from xq/xs and the weights' forward copies, writing g and u only, so
+ * the forward-to-backward state is the fp8 copies (xq, xqT, hqT) and yp.
+ */
+moe_status_t moe_grouped_gemm_recompute_gu_mx(const moe_mx_fwd_args* args, void* stream);
 
 #ifdef __cplusplus
 }

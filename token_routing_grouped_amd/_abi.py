@@ -41,6 +41,8 @@ _SIGS = {
     "moe_unpermute_sum": ([_P, _P, _I, _I, _I, _I, _P, _P], _I),
     "moe_grouped_gemm_workspace_size": ([_I, _I, _I, _I], _Z),
     "moe_grouped_gemm_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "moe_grouped_gemm_recompute_gu": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "moe_grouped_gemm_recompute_gu_mx": ([_P, _P], _I),
     "moe_grouped_gemm_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z,
                               _P], _I),
     "moe_router_bwd_workspace_size": ([_I, _I, _I], _Z),
@@ -246,6 +248,16 @@ def moe_grouped_gemm_fwd(xp, w1, w3, w2, offsets, g, u, hbuf, yp, ws):
                                       _p(hbuf), _p(yp), _p(ws), ws.numel(), _stream()), "moe_grouped_gemm_fwd")
 
 
+def moe_grouped_gemm_recompute_gu(xp, w1, w3, offsets, g, u, ws):
+    """The up projection alone, writing G and U (memory-lean backward)."""
+    R, d = xp.shape
+    E, h, _ = w1.shape
+    for t, n in ((w1, "w1"), (w3, "w3"), (g, "g"), (u, "u")):
+        _expect(t, xp.dtype, n)
+    _check(lib().moe_grouped_gemm_recompute_gu(_p(xp), _p(w1), _p(w3), _p(offsets), E, R, d, h, _dt(xp), _p(g), _p(u),
+                                               _p(ws), ws.numel(), _stream()), "moe_grouped_gemm_recompute_gu")
+
+
 def moe_grouped_gemm_bwd(dyp, xp, g, u, hbuf, w1, w3, w2, offsets, dgu, dxp, dw1, dw3, dw2, ws):
     R, d = xp.shape
     E, h, _ = w1.shape
@@ -326,6 +338,12 @@ def moe_grouped_gemm_fwd_mx(**kw):
     """Keyword arguments are the fields of moe_mx_fwd_args (tensors or ints)."""
     a = _fill(MxFwdArgs(), **kw)
     _check(lib().moe_grouped_gemm_fwd_mx(ctypes.byref(a), _stream()), "moe_grouped_gemm_fwd_mx")
+
+
+def moe_grouped_gemm_recompute_gu_mx(**kw):
+    """The MX up projection alone, writing g and u (fields of moe_mx_fwd_args)."""
+    a = _fill(MxFwdArgs(), **kw)
+    _check(lib().moe_grouped_gemm_recompute_gu_mx(ctypes.byref(a), _stream()), "moe_grouped_gemm_recompute_gu_mx")
 
 
 def moe_grouped_gemm_bwd_mx(**kw):

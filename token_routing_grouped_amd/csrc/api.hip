@@ -312,8 +312,10 @@ moe_status_t moe_grouped_gemm_fwd(const void* xp, const void* w1, const void* w3
   const char* fn = "moe_grouped_gemm_fwd";
   TRY(check_ggemm_dims(fn, E, R, d, h, dt));
   TRY(check_ptrs(fn, {{"w1", w1}, {"w3", w3}, {"w2", w2}, {"offsets", offsets}}));
+  if ((g == nullptr || u == nullptr) && dt != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: the memory-lean forward (g or u null) needs bf16", fn);
   if (R == 0) return ok();
-  TRY(check_ptrs(fn, {{"xp", xp}, {"g", g}, {"u", u}, {"hbuf", hbuf}, {"yp", yp}}));
+  TRY(check_ptrs(fn, {{"xp", xp}, {"hbuf", hbuf}, {"yp", yp}}));
   const size_t need = trg::ggemm_ws_bytes(E, R, d, h);
   if (ws == nullptr || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
@@ -321,6 +323,23 @@ moe_status_t moe_grouped_gemm_fwd(const void* xp, const void* w1, const void* w3
   TRY(check_device());
   return hip_status(fn, trg::launch_ggemm_fwd(xp, w1, w3, w2, offsets, E, R, d, h, dt == MOE_BF16, g, u, hbuf, yp, ws,
                                               (hipStream_t)stream));
+}
+
+moe_status_t moe_grouped_gemm_recompute_gu(const void* xp, const void* w1, const void* w3, const int32_t* offsets,
+                                           int E, int R, int d, int h, int dt, void* g, void* u, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_gemm_recompute_gu";
+  TRY(check_ggemm_dims(fn, E, R, d, h, dt));
+  if (dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: needs bf16", fn);
+  TRY(check_ptrs(fn, {{"w1", w1}, {"w3", w3}, {"offsets", offsets}}));
+  if (R == 0) return ok();
+  TRY(check_ptrs(fn, {{"xp", xp}, {"g", g}, {"u", u}}));
+  const size_t need = trg::ggemm_ws_bytes(E, R, d, h);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
+  if (!aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+  TRY(check_device());
+  return hip_status(fn, trg::launch_ggemm_recompute_gu(xp, w1, w3, offsets, E, R, d, h, g, u, ws, (hipStream_t)stream));
 }
 
 moe_status_t moe_grouped_gemm_bwd(const void* dyp, const void* xp, const void* g, const void* u, const void* hbuf,
@@ -470,10 +489,21 @@ moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* a, void* stream) {
   TRY(check_ptrs(fn, {{"offsets", a->offsets}, {"off32", a->off32}, {"w1q", a->w1q}, {"w1s", a->w1s},
                       {"w3q", a->w3q}, {"w3s", a->w3s}, {"w2q", a->w2q}, {"w2s", a->w2s}}));
   if (a->R == 0) return ok();
-  TRY(check_ptrs(fn, {{"xq", a->xq}, {"xs", a->xs}, {"g", a->g}, {"u", a->u}, {"hbuf", a->hbuf}, {"hq", a->hq},
-                      {"hs", a->hs}, {"hqT", a->hqT}, {"hsT", a->hsT}, {"yp", a->yp}}));
+  TRY(check_ptrs(fn, {{"xq", a->xq}, {"xs", a->xs}, {"hbuf", a->hbuf}, {"hq", a->hq}, {"hs", a->hs},
+                      {"hqT", a->hqT}, {"hsT", a->hsT}, {"yp", a->yp}}));
   TRY(check_device());
   return hip_status(fn, trg::launch_ggemm_fwd_mx(*a, (hipStream_t)stream));
+}
+
+moe_status_t moe_grouped_gemm_recompute_gu_mx(const moe_mx_fwd_args* a, void* stream) {
+  const char* fn = "moe_grouped_gemm_recompute_gu_mx";
+  if (!a) return fail(MOE_ERR_INVALID_ARG, "%s: args is null", fn);
+  TRY(check_mx_dims(fn, a->E, a->R, a->d, a->h, a->r32cap, a->ws, a->ws_bytes));
+  TRY(check_ptrs(fn, {{"offsets", a->offsets}, {"w1q", a->w1q}, {"w1s", a->w1s}, {"w3q", a->w3q}, {"w3s", a->w3s}}));
+  if (a->R == 0) return ok();
+  TRY(check_ptrs(fn, {{"xq", a->xq}, {"xs", a->xs}, {"g", a->g}, {"u", a->u}}));
+  TRY(check_device());
+  return hip_status(fn, trg::launch_ggemm_recompute_gu_mx(*a, (hipStream_t)stream));
 }
 
 moe_status_t moe_grouped_gemm_bwd_mx(const moe_mx_bwd_args* a, void* stream) {

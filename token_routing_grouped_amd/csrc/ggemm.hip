@@ -273,20 +273,27 @@ size_t ggemm_ws_bytes(int E, int R, int d, int h) {
 
 using namespace gg;
 
+// Up projection with the SwiGLU epilogue (N covers W1 and W3 rows); any of
+// G, U, H may be null (not stored).
+template <int BM>
+static void up_bm(const char* name, const void* xp, const void* w1, const void* w3, const int* offsets, int E, int R,
+                  int d, int h, void* gq, void* u, void* hb, const int* tile_off, hipStream_t s) {
+  const int mt_max = cdiv(R, BM) + E;
+  Args a{};
+  a.A = (const uint16_t*)xp; a.lda = d;
+  a.B = (const uint16_t*)w1; a.B2 = (const uint16_t*)w3; a.ldb = d; a.b_es = (long)h * d;
+  a.C = gq; a.C2 = u; a.C3 = hb; a.ldc = h;
+  a.N = 2 * h; a.K = d; a.split = h;
+  a.offsets = offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+  a.tiles_n = cdiv(2L * h, 256);
+  run<BM, 256, true, true, RAGGED_M, BSEL_GLU, CSEL_NONE, EPI_SWIGLU_FWD>(name, a, mt_max * a.tiles_n, s);
+}
+
 template <int BM>
 static void fwd_bm(const void* xp, const void* w1, const void* w3, const void* w2, const int* offsets, int E, int R,
                    int d, int h, void* gq, void* u, void* hb, void* yp, const int* tile_off, hipStream_t s) {
   const int mt_max = cdiv(R, BM) + E;
-  {  // up projection with the SwiGLU epilogue: N covers W1 and W3 rows
-    Args a{};
-    a.A = (const uint16_t*)xp; a.lda = d;
-    a.B = (const uint16_t*)w1; a.B2 = (const uint16_t*)w3; a.ldb = d; a.b_es = (long)h * d;
-    a.C = gq; a.C2 = u; a.C3 = hb; a.ldc = h;
-    a.N = 2 * h; a.K = d; a.split = h;
-    a.offsets = offsets; a.tile_off = tile_off; a.E = E; a.R = R;
-    a.tiles_n = cdiv(2L * h, 256);
-    run<BM, 256, true, true, RAGGED_M, BSEL_GLU, CSEL_NONE, EPI_SWIGLU_FWD>("ggemm_up_swiglu", a, mt_max * a.tiles_n, s);
-  }
+  up_bm<BM>("ggemm_up_swiglu", xp, w1, w3, offsets, E, R, d, h, gq, u, hb, tile_off, s);
   {  // down projection
     Args a{};
     a.A = (const uint16_t*)hb; a.lda = h;
@@ -311,6 +318,17 @@ hipError_t launch_ggemm_fwd(const void* xp, const void* w1, const void* w3, cons
     fwd_bm<128>(xp, w1, w3, w2, offsets, E, R, d, h, g, u, hb, yp, tile_off, s);
   else
     fwd_bm<256>(xp, w1, w3, w2, offsets, E, R, d, h, g, u, hb, yp, tile_off + (E + 1), s);
+  return hipGetLastError();
+}
+
+hipError_t launch_ggemm_recompute_gu(const void* xp, const void* w1, const void* w3, const int* offsets, int E, int R,
+                                     int d, int h, void* g, void* u, void* ws, hipStream_t s) {
+  int* tile_off = (int*)ws;
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off);
+  if (small_rows(E, R))
+    up_bm<128>("ggemm_recompute_gu", xp, w1, w3, offsets, E, R, d, h, g, u, nullptr, tile_off, s);
+  else
+    up_bm<256>("ggemm_recompute_gu", xp, w1, w3, offsets, E, R, d, h, g, u, nullptr, tile_off + (E + 1), s);
   return hipGetLastError();
 }
 

@@ -227,10 +227,12 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
             uv[r] = acc[i][j + TN / 2][q * 4 + r];
             hv[r] = silu_f(gv[r]) * uv[r];
           }
+          // any of G, U, H may be absent: a memory-lean forward stores H only,
+          // the backward's recompute G and U only (uniform branches)
           const long off = (long)m * g.ldc + c;
-          *(uint2*)((uint16_t*)g.C + off) = make_uint2(pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3]));
-          *(uint2*)((uint16_t*)g.C2 + off) = make_uint2(pack_bf2(uv[0], uv[1]), pack_bf2(uv[2], uv[3]));
-          *(uint2*)((uint16_t*)g.C3 + off) = make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
+          if (g.C) *(uint2*)((uint16_t*)g.C + off) = make_uint2(pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3]));
+          if (g.C2) *(uint2*)((uint16_t*)g.C2 + off) = make_uint2(pack_bf2(uv[0], uv[1]), pack_bf2(uv[2], uv[3]));
+          if (g.C3) *(uint2*)((uint16_t*)g.C3 + off) = make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
         });
       });
     });

@@ -343,23 +343,39 @@ static void run_mx(const char* name, const Args& a, const MxArgs& x, int max_til
 
 using namespace gg;
 
+// Up projection + SwiGLU: xq [R,d] x (W1q | W3q) [E,h,d]; any of G, U, H may
+// be null (not stored).
+template <int BM>
+static void mx_up_bm(const char* name, const MxFwd& p, void* gq, void* u, void* hb, const int* tile_off,
+                     hipStream_t s) {
+  const int E = p.E, R = p.R, d = p.d, h = p.h;
+  const int mt_max = cdiv(R, BM) + E;
+  Args a{};
+  a.A = (const uint16_t*)p.xq; a.lda = d;
+  a.B = (const uint16_t*)p.w1q; a.B2 = (const uint16_t*)p.w3q; a.ldb = d; a.b_es = (long)h * d;
+  a.C = gq; a.C2 = u; a.C3 = hb; a.ldc = h;
+  a.N = 2 * h; a.K = d; a.split = h;
+  a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+  a.tiles_n = cdiv(2L * h, 256);
+  MxArgs x{};
+  x.sA = p.xs; x.lds_a = d / 32; x.sA_bytes = (long)R * (d / 32);
+  x.sB = p.w1s; x.sB2 = p.w3s; x.lds_b = d / 32; x.sb_es = (long)h * (d / 32); x.sB_bytes = (long)E * h * (d / 32);
+  run_mx<BM, 256, RAGGED_M, BSEL_GLU, CSEL_NONE, EPI_SWIGLU_FWD>(name, a, x, mt_max * a.tiles_n, s);
+}
+
+hipError_t launch_ggemm_recompute_gu_mx(const MxFwd& p, hipStream_t s) {
+  int* tile_off = (int*)p.ws;
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, tile_off);
+  if (small_rows(p.E, p.R)) mx_up_bm<128>("ggemm_mx_recompute_gu", p, p.g, p.u, nullptr, tile_off, s);
+  else mx_up_bm<256>("ggemm_mx_recompute_gu", p, p.g, p.u, nullptr, tile_off + (p.E + 1), s);
+  return hipGetLastError();
+}
+
 template <int BM>
 static hipError_t mx_fwd_bm(const MxFwd& p, const int* tile_off, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
   const int mt_max = cdiv(R, BM) + E;
-  {  // up projection + SwiGLU: xq [R,d] x (W1q | W3q) [E,h,d]
-    Args a{};
-    a.A = (const uint16_t*)p.xq; a.lda = d;
-    a.B = (const uint16_t*)p.w1q; a.B2 = (const uint16_t*)p.w3q; a.ldb = d; a.b_es = (long)h * d;
-    a.C = p.g; a.C2 = p.u; a.C3 = p.hbuf; a.ldc = h;
-    a.N = 2 * h; a.K = d; a.split = h;
-    a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
-    a.tiles_n = cdiv(2L * h, 256);
-    MxArgs x{};
-    x.sA = p.xs; x.lds_a = d / 32; x.sA_bytes = (long)R * (d / 32);
-    x.sB = p.w1s; x.sB2 = p.w3s; x.lds_b = d / 32; x.sb_es = (long)h * (d / 32); x.sB_bytes = (long)E * h * (d / 32);
-    run_mx<BM, 256, RAGGED_M, BSEL_GLU, CSEL_NONE, EPI_SWIGLU_FWD>("ggemm_mx_up_swiglu", a, x, mt_max * a.tiles_n, s);
-  }
+  mx_up_bm<BM>("ggemm_mx_up_swiglu", p, p.g, p.u, p.hbuf, tile_off, s);
   // H -> rowwise MX (down GEMM) and columnwise per expert (wgrad down)
   {
     ProfScope ps("mx_quantize_h", s);

@@ -69,6 +69,9 @@ hipError_t launch_mx_quantize(const void* in, bool bf16, long ld_in, int rows, i
                               hipStream_t s);
 typedef moe_mx_fwd_args MxFwd;
 typedef moe_mx_bwd_args MxBwd;
+hipError_t launch_ggemm_recompute_gu(const void* xp, const void* w1, const void* w3, const int* offsets, int E, int R,
+                                     int d, int h, void* g, void* u, void* ws, hipStream_t s);
+hipError_t launch_ggemm_recompute_gu_mx(const MxFwd& p, hipStream_t s);
 hipError_t launch_ggemm_fwd_mx(const MxFwd& p, hipStream_t s);
 hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s);
 

@@ -12,6 +12,8 @@ Backward:
 
 With aux_alpha > 0 the router balance step runs after routing (moe_balance)
 and its loss's gradient enters the router backward (moe_router_bwd_aux).
+With lean=True the forward does not store G and U and the backward recomputes
+them (moe_grouped_gemm_recompute_gu[_mx]) before moe_grouped_gemm_bwd[_mx].
 
 Every call is enqueued on torch's current stream; nothing is copied to the
 host in between (routing metadata stays on the GPU: Olmo-core 3 overview,
@@ -37,9 +39,13 @@ class MoELayerGPU:
     """
 
     def __init__(self, T: int, d: int, E: int, k: int, h: int, dtype: torch.dtype, device="cuda", mx: bool = False,
-                 aux_alpha: float = 0.0):
+                 aux_alpha: float = 0.0, lean: bool = False):
         self.T, self.d, self.E, self.k, self.h = T, d, E, k, h
         self.aux_alpha = float(aux_alpha)
+        # memory-lean: the forward does not store G and U; the backward
+        # recomputes them (one more up projection) into g / u, which then act
+        # as backward scratch
+        self.lean = bool(lean)
         self.R = R = T * k
         self.dtype = dtype
         self.mx = mx
@@ -124,17 +130,31 @@ class MoELayerGPU:
             _abi.moe_grouped_gemm_fwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, r32cap=self.r32cap,
                                          offsets=self.offsets, off32=self.off32, xq=self.xq, xs=self.xs, w1q=self.w1q,
                                          w1s=self.w1s, w3q=self.w3q, w3s=self.w3s, w2q=self.w2q, w2s=self.w2s,
-                                         g=self.g, u=self.u, hbuf=self.hb, hq=self.hq, hs=self.hs, hqT=self.hqT,
+                                         g=None if self.lean else self.g, u=None if self.lean else self.u,
+                                         hbuf=self.hb, hq=self.hq, hs=self.hs, hqT=self.hqT,
                                          hsT=self.hsT, yp=self.yp, ws=self.ws_gemm, ws_bytes=self.ws_gemm.numel())
         else:
             _abi.moe_permute(x, self.pos, self.xp)
-            _abi.moe_grouped_gemm_fwd(self.xp, w1, w3, w2, self.offsets, self.g, self.u, self.hb, self.yp,
-                                      self.ws_gemm)
+            _abi.moe_grouped_gemm_fwd(self.xp, w1, w3, w2, self.offsets, None if self.lean else self.g,
+                                      None if self.lean else self.u, self.hb, self.yp, self.ws_gemm)
         _abi.moe_combine(self.yp, self.topk_w, self.pos, self.y)
         return self.y
 
+    def recompute_gu(self, w1, w3):
+        """G and U of the current routing, bit-identical to what the forward
+        would have stored (memory-lean backward)."""
+        if self.mx:
+            _abi.moe_grouped_gemm_recompute_gu_mx(E=self.E, R=self.R, d=self.d, h=self.h, r32cap=self.r32cap,
+                                                  offsets=self.offsets, off32=self.off32, xq=self.xq, xs=self.xs,
+                                                  w1q=self.w1q, w1s=self.w1s, w3q=self.w3q, w3s=self.w3s, g=self.g,
+                                                  u=self.u, ws=self.ws_gemm, ws_bytes=self.ws_gemm.numel())
+        else:
+            _abi.moe_grouped_gemm_recompute_gu(self.xp, w1, w3, self.offsets, self.g, self.u, self.ws_gemm)
+
     def backward(self, dy, x, wr, w1, w3, w2):
         _abi.moe_combine_bwd(dy, self.yp, self.topk_w, self.pos, self.dyp, self.dgate)
+        if self.lean:
+            self.recompute_gu(w1, w3)
         if self.mx:
             _abi.moe_grouped_gemm_bwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, r32cap=self.r32cap,
                                          offsets=self.offsets, off32=self.off32, dyp=self.dyp, dyq=self.dyq,
@@ -162,6 +182,23 @@ class MoELayerGPU:
         _abi.moe_balance(self.probs, self.counts, self.k, self.aux_alpha if alpha is None else alpha,
                          self.balance_stats, self.ws_balance, aux_g=self.aux_g, mean_probs=self.mean_probs)
         return self.balance_stats
+
+    def saved_tensors(self):
+        """The layer's own buffers that must live from the forward to the
+        backward (routing metadata excluded: it is the same in every mode;
+        the caller's inputs and weights excluded)."""
+        keep = [self.yp]  # combine backward: dgate = <dy, Yp>
+        if self.mx:
+            keep += [self.xqT, self.xsT, self.hqT, self.hsT]  # weight gradients
+            keep += [self.xq, self.xs] if self.lean else [self.g, self.u]
+        else:
+            keep += [self.xp, self.hb]  # weight gradients (and the recompute's input)
+            if not self.lean:
+                keep += [self.g, self.u]
+        return keep
+
+    def saved_bytes(self):
+        return sum(t.numel() * t.element_size() for t in self.saved_tensors())
 
     def step(self, x, wr, w1, w3, w2, dy, forced_idx=None):
         self.forward(x, wr, w1, w3, w2, forced_idx)
