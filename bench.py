@@ -1,7 +1,7 @@
 """Benchmark of the MoE expert layer, forward + backward, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config small] [--mode router]
-                    [--no-cpu-baseline] [--lean] [--aux-alpha A]
+                    [--no-cpu-baseline] [--lean] [--overlap] [--aux-alpha A]
 
 One step = the whole hot path over one batch of synthetic input, through the C
 ABI: router logits, routing (softmax / top-k, histogram, offsets, positions),
@@ -154,6 +154,8 @@ def main():
     ap.add_argument("--mode", default=None, help="router | uniform | zipf (default: the config's first mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--overlap", action="store_true",
+                    help="run the weight-gradient GEMMs on a second stream next to the dgrad chain (bf16)")
     ap.add_argument("--lean", action="store_true",
                     help="memory-lean backward: G and U are not stored by the forward but recomputed")
     ap.add_argument("--aux-alpha", type=float, default=0.0,
@@ -188,7 +190,8 @@ def main():
     if mode != "router":
         forced = torch.from_numpy(inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)).to(dev)
     del inp
-    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, dev, mx=cfg.mx, aux_alpha=a.aux_alpha, lean=a.lean)
+    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, dev, mx=cfg.mx, aux_alpha=a.aux_alpha, lean=a.lean,
+                        overlap=a.overlap)
     args = (t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])
 
     for _ in range(a.warmup):
@@ -276,6 +279,7 @@ def main():
         "balance": {"score": float(bstats[0]), "max_over_mean": float(bstats[2]), "min_over_mean": float(bstats[3]),
                     "aux_alpha": a.aux_alpha, "aux_loss": float(bstats[1])},
         "peak_mem_gib": torch.cuda.max_memory_allocated() / 2 ** 30,
+        "streams": 2 if layer.overlap else 1,
         "memory": {"lean": a.lean, "saved_activation_bytes": layer.saved_bytes(),
                    "note": "bytes the layer keeps from the forward to the backward (routing metadata, inputs and "
                            "weights excluded)"},

@@ -203,6 +203,31 @@ moe_status_t moe_grouped_gemm_bwd(const void* dyp, const void* xp, const void* g
                                   void* dw2, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_grouped_gemm_bwd_parts: moe_grouped_gemm_bwd restricted to a subset of
+ * its four GEMMs (bf16), so that a caller can run them on two streams:
+ *   MOE_BWD_DGRAD_DOWN  dgu = SwiGLU-bwd(dyp W2[e], g, u)   needs dyp
+ *   MOE_BWD_WGRAD_DOWN  dw2 = dyp^T hbuf per expert          needs dyp
+ *   MOE_BWD_DGRAD_UP    dxp = dgu [W1; W3]                   needs dgu
+ *   MOE_BWD_WGRAD_UP    dw1 | dw3 = dgu^T xp per expert      needs dgu
+ * The pages report that overlapping streams does not always help
+ * (Olmo-core 3 overview, "Empirical findings beyond raw speed"); this call is
+ * what measures that here.  Calls that may run concurrently need separate
+ * workspaces.  Same arguments as moe_grouped_gemm_bwd otherwise.
+ */
+enum {
+  MOE_BWD_DGRAD_DOWN = 1,
+  MOE_BWD_WGRAD_DOWN = 2,
+  MOE_BWD_DGRAD_UP = 4,
+  MOE_BWD_WGRAD_UP = 8,
+  MOE_BWD_ALL = 15
+};
+moe_status_t moe_grouped_gemm_bwd_parts(const void* dyp, const void* xp, const void* g, const void* u,
+                                        const void* hbuf, const void* w1, const void* w3, const void* w2,
+                                        const int32_t* offsets, int E, int R, int d, int h, int dt, void* dgu,
+                                        void* dxp, void* dw1, void* dw3, void* dw2, unsigned parts, void* ws,
+                                        size_t ws_bytes, void* stream);
+
+/*
  * moe_router_bwd: gradient through the gates into the logits, wr and x.
  *   gh[t,e] = dgate[t,j] where e = topk_idx[t,j], else 0
  *   dlogits = probs * (gh - sum_e probs*gh)      (softmax backward)

@@ -41,6 +41,8 @@ _SIGS = {
     "moe_unpermute_sum": ([_P, _P, _I, _I, _I, _I, _P, _P], _I),
     "moe_grouped_gemm_workspace_size": ([_I, _I, _I, _I], _Z),
     "moe_grouped_gemm_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "moe_grouped_gemm_bwd_parts": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
+                                    ctypes.c_uint, _P, _Z, _P], _I),
     "moe_grouped_gemm_recompute_gu": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "moe_grouped_gemm_recompute_gu_mx": ([_P, _P], _I),
     "moe_grouped_gemm_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z,
@@ -246,6 +248,21 @@ def moe_grouped_gemm_fwd(xp, w1, w3, w2, offsets, g, u, hbuf, yp, ws):
         _expect(t, xp.dtype, n)
     _check(lib().moe_grouped_gemm_fwd(_p(xp), _p(w1), _p(w3), _p(w2), _p(offsets), E, R, d, h, _dt(xp), _p(g), _p(u),
                                       _p(hbuf), _p(yp), _p(ws), ws.numel(), _stream()), "moe_grouped_gemm_fwd")
+
+
+BWD_DGRAD_DOWN, BWD_WGRAD_DOWN, BWD_DGRAD_UP, BWD_WGRAD_UP, BWD_ALL = 1, 2, 4, 8, 15
+
+
+def moe_grouped_gemm_bwd_parts(dyp, xp, g, u, hbuf, w1, w3, w2, offsets, dgu, dxp, dw1, dw3, dw2, parts, ws):
+    """A subset (MOE_BWD_* mask) of moe_grouped_gemm_bwd's four GEMMs."""
+    R, d = xp.shape
+    E, h, _ = w1.shape
+    for t, n in ((dyp, "dyp"), (g, "g"), (u, "u"), (hbuf, "hbuf"), (w1, "w1"), (w3, "w3"), (w2, "w2"), (dgu, "dgu"),
+                 (dxp, "dxp"), (dw1, "dw1"), (dw3, "dw3"), (dw2, "dw2")):
+        _expect(t, xp.dtype, n)
+    _check(lib().moe_grouped_gemm_bwd_parts(_p(dyp), _p(xp), _p(g), _p(u), _p(hbuf), _p(w1), _p(w3), _p(w2),
+                                            _p(offsets), E, R, d, h, _dt(xp), _p(dgu), _p(dxp), _p(dw1), _p(dw3),
+                                            _p(dw2), parts, _p(ws), ws.numel(), _stream()), "moe_grouped_gemm_bwd_parts")
 
 
 def moe_grouped_gemm_recompute_gu(xp, w1, w3, offsets, g, u, ws):

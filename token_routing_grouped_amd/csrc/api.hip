@@ -342,12 +342,16 @@ moe_status_t moe_grouped_gemm_recompute_gu(const void* xp, const void* w1, const
   return hip_status(fn, trg::launch_ggemm_recompute_gu(xp, w1, w3, offsets, E, R, d, h, g, u, ws, (hipStream_t)stream));
 }
 
-moe_status_t moe_grouped_gemm_bwd(const void* dyp, const void* xp, const void* g, const void* u, const void* hbuf,
-                                  const void* w1, const void* w3, const void* w2, const int32_t* offsets, int E, int R,
-                                  int d, int h, int dt, void* dgu, void* dxp, void* dw1, void* dw3, void* dw2,
-                                  void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "moe_grouped_gemm_bwd";
+static moe_status_t ggemm_bwd_impl(const char* fn, const void* dyp, const void* xp, const void* g, const void* u,
+                                   const void* hbuf, const void* w1, const void* w3, const void* w2,
+                                   const int32_t* offsets, int E, int R, int d, int h, int dt, void* dgu, void* dxp,
+                                   void* dw1, void* dw3, void* dw2, unsigned parts, void* ws, size_t ws_bytes,
+                                   void* stream) {
   TRY(check_ggemm_dims(fn, E, R, d, h, dt));
+  if (parts == 0 || (parts & ~(unsigned)MOE_BWD_ALL) != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: parts must be a non-empty subset of MOE_BWD_ALL", fn);
+  if (dt != MOE_BF16 && parts != MOE_BWD_ALL)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: a subset of the backward GEMMs needs bf16", fn);
   TRY(check_ptrs(fn, {{"w1", w1}, {"w3", w3}, {"w2", w2}, {"offsets", offsets}, {"dw1", dw1}, {"dw3", dw3},
                       {"dw2", dw2}}));
   if (R > 0)
@@ -358,7 +362,24 @@ moe_status_t moe_grouped_gemm_bwd(const void* dyp, const void* xp, const void* g
   if (!aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
   TRY(check_device());
   return hip_status(fn, trg::launch_ggemm_bwd(dyp, xp, g, u, hbuf, w1, w3, w2, offsets, E, R, d, h, dt == MOE_BF16,
-                                              dgu, dxp, dw1, dw3, dw2, ws, (hipStream_t)stream));
+                                              dgu, dxp, dw1, dw3, dw2, ws, parts, (hipStream_t)stream));
+}
+
+moe_status_t moe_grouped_gemm_bwd(const void* dyp, const void* xp, const void* g, const void* u, const void* hbuf,
+                                  const void* w1, const void* w3, const void* w2, const int32_t* offsets, int E, int R,
+                                  int d, int h, int dt, void* dgu, void* dxp, void* dw1, void* dw3, void* dw2,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return ggemm_bwd_impl("moe_grouped_gemm_bwd", dyp, xp, g, u, hbuf, w1, w3, w2, offsets, E, R, d, h, dt, dgu, dxp,
+                        dw1, dw3, dw2, MOE_BWD_ALL, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_grouped_gemm_bwd_parts(const void* dyp, const void* xp, const void* g, const void* u,
+                                        const void* hbuf, const void* w1, const void* w3, const void* w2,
+                                        const int32_t* offsets, int E, int R, int d, int h, int dt, void* dgu,
+                                        void* dxp, void* dw1, void* dw3, void* dw2, unsigned parts, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  return ggemm_bwd_impl("moe_grouped_gemm_bwd_parts", dyp, xp, g, u, hbuf, w1, w3, w2, offsets, E, R, d, h, dt, dgu,
+                        dxp, dw1, dw3, dw2, parts, ws, ws_bytes, stream);
 }
 
 size_t moe_router_bwd_workspace_size(int T, int d, int E) {

@@ -335,9 +335,9 @@ hipError_t launch_ggemm_recompute_gu(const void* xp, const void* w1, const void*
 template <int BM>
 static void dgrad_bm(const void* dyp, const void* g, const void* u, const void* w1, const void* w3, const void* w2,
                      const int* offsets, int E, int R, int d, int h, void* dgu, void* dxp, const int* tile_off,
-                     hipStream_t s) {
+                     unsigned parts, hipStream_t s) {
   const int mt_max = cdiv(R, BM) + E;
-  {  // dgrad down + SwiGLU backward: dH = dYp W2[e] -> dG, dU
+  if (parts & MOE_BWD_DGRAD_DOWN) {  // dgrad down + SwiGLU backward: dH = dYp W2[e] -> dG, dU
     Args a{};
     a.A = (const uint16_t*)dyp; a.lda = d;
     a.B = (const uint16_t*)w2; a.ldb = h; a.b_es = (long)d * h;
@@ -349,7 +349,7 @@ static void dgrad_bm(const void* dyp, const void* g, const void* u, const void* 
     run<BM, 256, true, false, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_SWIGLU_BWD>("ggemm_dgrad_down_swiglu", a,
                                                                               mt_max * a.tiles_n, s);
   }
-  {  // dgrad up: dXp = [dG | dU] [W1; W3]
+  if (parts & MOE_BWD_DGRAD_UP) {  // dgrad up: dXp = [dG | dU] [W1; W3]
     Args a{};
     a.A = (const uint16_t*)dgu; a.lda = 2L * h;
     a.B = (const uint16_t*)w1; a.B2 = (const uint16_t*)w3; a.ldb = d; a.b_es = (long)h * d;
@@ -364,18 +364,20 @@ static void dgrad_bm(const void* dyp, const void* g, const void* u, const void* 
 hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, const void* u, const void* hb,
                             const void* w1, const void* w3, const void* w2, const int* offsets, int E, int R, int d,
                             int h, bool bf16, void* dgu, void* dxp, void* dw1, void* dw3, void* dw2, void* ws,
-                            hipStream_t s) {
+                            unsigned parts, hipStream_t s) {
   if (!bf16)
     return launch_ggemm_bwd_f32((const float*)dyp, (const float*)xp, (const float*)g, (const float*)u,
                                 (const float*)hb, (const float*)w1, (const float*)w3, (const float*)w2, offsets, E,
                                 R, d, h, (float*)dgu, (float*)dxp, (float*)dw1, (float*)dw3, (float*)dw2, s);
-  int* tile_off = (int*)ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off);
-  if (small_rows(E, R))
-    dgrad_bm<128>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off, s);
-  else
-    dgrad_bm<256>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off + (E + 1), s);
-  {  // wgrad down: dW2[e] = dYp_e^T H_e  (M = d, N = h, K = the expert's rows)
+  if (parts & (MOE_BWD_DGRAD_DOWN | MOE_BWD_DGRAD_UP)) {
+    int* tile_off = (int*)ws;
+    tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off);
+    if (small_rows(E, R))
+      dgrad_bm<128>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off, parts, s);
+    else
+      dgrad_bm<256>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off + (E + 1), parts, s);
+  }
+  if (parts & MOE_BWD_WGRAD_DOWN) {  // wgrad down: dW2[e] = dYp_e^T H_e  (M = d, N = h, K = the expert's rows)
     Args a{};
     a.A = (const uint16_t*)dyp; a.lda = d;
     a.B = (const uint16_t*)hb; a.ldb = h;
@@ -386,7 +388,7 @@ hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, cons
     run<256, 256, false, false, RAGGED_K, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_wgrad_down", a,
                                                                           E * a.tiles_m * a.tiles_n, s);
   }
-  {  // wgrad up: [dW1; dW3][e] = [dG | dU]_e^T Xp_e  (M = 2h, N = d)
+  if (parts & MOE_BWD_WGRAD_UP) {  // wgrad up: [dW1; dW3][e] = [dG | dU]_e^T Xp_e  (M = 2h, N = d)
     Args a{};
     a.A = (const uint16_t*)dgu; a.lda = 2L * h;
     a.B = (const uint16_t*)xp; a.ldb = d;

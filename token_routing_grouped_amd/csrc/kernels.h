@@ -41,7 +41,7 @@ hipError_t launch_ggemm_fwd(const void* xp, const void* w1, const void* w3, cons
                             hipStream_t s);
 hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, const void* u, const void* hb,
                             const void* w1, const void* w3, const void* w2, const int* offsets, int E, int R, int d,
-                            int h, bool bf16, void* dgu, void* dxp, void* dw1, void* dw3, void* dw2, void* ws,
+                            int h, bool bf16, void* dgu, void* dxp, void* dw1, void* dw3, void* dw2, void* ws, unsigned parts,
                             hipStream_t s);
 
 // bf16 MFMA dense GEMM helpers used by the router (E >= 64)

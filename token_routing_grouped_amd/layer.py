@@ -39,13 +39,16 @@ class MoELayerGPU:
     """
 
     def __init__(self, T: int, d: int, E: int, k: int, h: int, dtype: torch.dtype, device="cuda", mx: bool = False,
-                 aux_alpha: float = 0.0, lean: bool = False):
+                 aux_alpha: float = 0.0, lean: bool = False, overlap: bool = False):
         self.T, self.d, self.E, self.k, self.h = T, d, E, k, h
         self.aux_alpha = float(aux_alpha)
         # memory-lean: the forward does not store G and U; the backward
         # recomputes them (one more up projection) into g / u, which then act
         # as backward scratch
         self.lean = bool(lean)
+        # overlap (bf16): the weight-gradient GEMMs run on a second stream
+        # (default priority) next to the dgrad chain, joined by events
+        self.overlap = bool(overlap) and not mx
         self.R = R = T * k
         self.dtype = dtype
         self.mx = mx
@@ -80,6 +83,9 @@ class MoELayerGPU:
         self.ws_route = _abi.workspace(_abi.moe_route_workspace_size(T, E, k), dev)
         self.ws_gemm = _abi.workspace(_abi.moe_grouped_gemm_workspace_size(E, R, d, h), dev)
         self.ws_router = _abi.workspace(_abi.moe_router_bwd_workspace_size(T, d, E), dev)
+        if self.overlap:
+            self.side_stream = torch.cuda.Stream(device=dev)
+            self.ws_gemm2 = _abi.workspace(_abi.moe_grouped_gemm_workspace_size(E, R, d, h), dev)
         # router balance step: {score, aux loss, max/mean load, min/mean load},
         # the aux loss's per-expert probability gradient and mean probabilities
         self.balance_stats = e(4, dt=f32)
@@ -164,10 +170,14 @@ class MoELayerGPU:
                                          w2ts=self.w2ts, dgu=self.dgu, dguq=self.dguq, dgus=self.dgus,
                                          dguqT=self.dguqT, dgusT=self.dgusT, dxp=self.dxp, dw1=self.dw1, dw3=self.dw3,
                                          dw2=self.dw2, ws=self.ws_gemm, ws_bytes=self.ws_gemm.numel())
+        elif self.overlap:
+            self._backward_gemms_two_streams(w1, w3, w2)
         else:
             _abi.moe_grouped_gemm_bwd(self.dyp, self.xp, self.g, self.u, self.hb, w1, w3, w2, self.offsets, self.dgu,
                                       self.dxp, self.dw1, self.dw3, self.dw2, self.ws_gemm)
         _abi.moe_unpermute_sum(self.dxp, self.pos, self.dx)
+        if self.overlap and not self.mx:
+            torch.cuda.current_stream().wait_event(self._ev_side_done)
         if self.aux_alpha > 0.0:
             _abi.moe_router_bwd_aux(self.probs, self.topk_idx, self.dgate, self.aux_g, x, wr, self.dx, self.dwr,
                                     self.ws_router)
@@ -182,6 +192,27 @@ class MoELayerGPU:
         _abi.moe_balance(self.probs, self.counts, self.k, self.aux_alpha if alpha is None else alpha,
                          self.balance_stats, self.ws_balance, aux_g=self.aux_g, mean_probs=self.mean_probs)
         return self.balance_stats
+
+    def _backward_gemms_two_streams(self, w1, w3, w2):
+        """dgrad chain on the current stream, weight gradients on the side
+        stream: wgrad-down as soon as dYp exists, wgrad-up once dG|dU does."""
+        main, side = torch.cuda.current_stream(), self.side_stream
+        args = (self.dyp, self.xp, self.g, self.u, self.hb, w1, w3, w2, self.offsets, self.dgu, self.dxp, self.dw1,
+                self.dw3, self.dw2)
+        ev_dyp = torch.cuda.Event()
+        ev_dyp.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(ev_dyp)
+            _abi.moe_grouped_gemm_bwd_parts(*args, _abi.BWD_WGRAD_DOWN, self.ws_gemm2)
+        _abi.moe_grouped_gemm_bwd_parts(*args, _abi.BWD_DGRAD_DOWN, self.ws_gemm)
+        ev_dgu = torch.cuda.Event()
+        ev_dgu.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(ev_dgu)
+            _abi.moe_grouped_gemm_bwd_parts(*args, _abi.BWD_WGRAD_UP, self.ws_gemm2)
+            self._ev_side_done = torch.cuda.Event()
+            self._ev_side_done.record(side)
+        _abi.moe_grouped_gemm_bwd_parts(*args, _abi.BWD_DGRAD_UP, self.ws_gemm)
 
     def saved_tensors(self):
         """The layer's own buffers that must live from the forward to the
