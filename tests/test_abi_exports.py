@@ -121,3 +121,26 @@ def test_mx_host_side_validation_without_gpu():
     a = _abi.MxFwdArgs(E=2, R=8, d=128, h=128, r32cap=96)
     assert lib.moe_grouped_gemm_fwd_mx(ctypes.byref(a), None) == 1
     assert b"multiple of 128" in lib.moe_last_error_string()
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_host_validation_of_the_next_rows():
+    """Argument checks of the balance, lean and two-stream entry points (no GPU)."""
+    from token_routing_grouped_amd import _abi
+
+    lib = _abi.lib()
+    c = ctypes.c_void_p(16)
+    # balance: negative alpha, k > E
+    assert lib.moe_balance(c, c, 8, 4, 2, -1.0, c, None, None, c, 1 << 20, None) == 1
+    assert b"alpha" in lib.moe_last_error_string()
+    assert lib.moe_balance(c, c, 8, 4, 5, 0.01, c, None, None, c, 1 << 20, None) == 1
+    # lean forward (g, u null) is bf16 only
+    st = lib.moe_grouped_gemm_fwd(c, c, c, c, c, 2, 8, 64, 64, 0, None, None, c, c, c, 1 << 20, None)
+    assert st == 2 and b"memory-lean" in lib.moe_last_error_string()
+    # recompute needs bf16
+    assert lib.moe_grouped_gemm_recompute_gu(c, c, c, c, 2, 8, 64, 64, 0, c, c, c, 1 << 20, None) == 2
+    # backward parts: empty and out-of-range masks
+    args = [c] * 9 + [2, 8, 64, 64, 1] + [c] * 5
+    assert lib.moe_grouped_gemm_bwd_parts(*args, 0, c, 1 << 20, None) == 1
+    assert lib.moe_grouped_gemm_bwd_parts(*args, 16, c, 1 << 20, None) == 1
+    assert b"parts" in lib.moe_last_error_string()
