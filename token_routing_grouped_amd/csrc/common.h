@@ -33,15 +33,14 @@ TRG_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 TRG_DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Round to nearest even; NaN stays NaN.
-TRG_DEV uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even (gfx950's v_cvt_pk_bf16_f32; NaN stays
+// a quiet NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 TRG_DEV uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+TRG_DEV uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Element access for the two storage types.
 template <class T> struct Elt;
@@ -105,7 +104,11 @@ TRG_DEV int block_excl_scan_1024(int v, int* tmp /* 1024 */, int* total) {
   return incl - v;
 }
 
-TRG_DEV float silu_f(float g) { return g / (1.0f + __expf(-g)); }
-TRG_DEV float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// The epilogues' activation functions with the hardware reciprocal (1 ulp;
+// the results are stored in bf16): an IEEE division costs about ten
+// instructions more per element.  Limits: g -> -inf gives -0 and 0, g -> +inf
+// gives g and 1.
+TRG_DEV float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+TRG_DEV float silu_f(float g) { return g * sigmoid_f(g); }
 
 }  // namespace trg
