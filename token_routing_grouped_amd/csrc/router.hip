@@ -26,13 +26,23 @@ __global__ __launch_bounds__(256) void router_logits_valu_kernel(const T* __rest
   for (int v = lane; v < nv; v += 64) {
     float f[V];
     unpack16<T>(xr[v], f);
+    // Groups of 8 expert rows: the loads are issued unconditionally (row
+    // index clamped to a valid row) so they are all in flight together; only
+    // the FMAs depend on e < E.
 #pragma unroll
-    for (int e = 0; e < EB; ++e) {
-      if (e < E) {
-        float w[V];
-        unpack16<T>(((const uint4*)(wr + (long)e * d))[v], w);
+    for (int e0 = 0; e0 < EB; e0 += 8) {
+      if (e0 >= E) break;
+      uint4 wv[8];
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[e] = fmaf(f[i], w[i], acc[e]);
+      for (int q = 0; q < 8; ++q) wv[q] = ((const uint4*)(wr + (long)min(e0 + q, E - 1) * d))[v];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (e0 + q < E) {
+          float w[V];
+          unpack16<T>(wv[q], w);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[e0 + q] = fmaf(f[i], w[i], acc[e0 + q]);
+        }
       }
     }
   }
@@ -90,56 +100,94 @@ __global__ __launch_bounds__(256) void router_dl_kernel(const float* __restrict_
   }
 }
 
-constexpr int kDwrChunk = 256;  // tokens per dWr partial sum
+constexpr int kDwrChunk = 128;  // tokens per dWr partial sum
 
 // dWr partial sums over one chunk of kDwrChunk tokens.  Thread layout: 32
 // column groups of CV = 64/EB consecutive columns x 8 token lanes (the token
 // lanes of a group are neighbouring lanes of one wave, reduced with shuffles),
-// so each wave load covers whole 128-byte row pieces of x and every thread has
-// several independent loads in flight.
-template <class T, int EB>
+// so each wave load covers whole 128-byte row pieces of x.  The op is bound by
+// HBM, so a workgroup issues every load of its chunk (the chunk's dlogits and
+// each thread's NT rows of x) before the first wait; with 128-token chunks a
+// typical shape has several workgroups per CU in flight.
+template <class T, int EB, bool ELEM>
 __global__ __launch_bounds__(256) void router_dwr_partial_kernel(const float* __restrict__ dL, const T* __restrict__ x,
                                                                  int Tn, int d, int E, float* __restrict__ part) {
-  constexpr int CV = 64 / EB;  // columns per thread; EB * CV = 64 accumulators
+  constexpr int CV = 64 / EB;           // columns per thread; EB * CV = 64 accumulators
+  constexpr int NT = kDwrChunk / 8;     // rows per thread
   struct alignas(CV * sizeof(T)) Vec { T v[CV]; };
-  __shared__ float sdl[64][EB];
+  __shared__ float sdl[kDwrChunk][EB];
   const int tl = threadIdx.x & 7, cg = threadIdx.x >> 3;
   const int c0 = blockIdx.x * (32 * CV) + cg * CV;
   const int chunk = blockIdx.y;
-  const int t0 = chunk * kDwrChunk, t1 = min(Tn, t0 + kDwrChunk);
+  const int t0 = chunk * kDwrChunk;
+  const int nt = min(kDwrChunk, Tn - t0);
+  // Raw rows, converted at the FMAs.  No branch around the loads (a branch
+  // makes the compiler wait for each load before the next is issued): rows
+  // past the chunk and column groups past d load a valid address and are
+  // zeroed by a select.  ELEM (a column group may straddle d: fp32 with
+  // d % CV != 0) loads element by element instead.
+  Vec xr[NT];
+  if constexpr (!ELEM) {
+    const bool col_ok = c0 + CV <= d;
+    const int cl = col_ok ? c0 : 0;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int tt = tl + 8 * j;
+      xr[j] = *(const Vec*)(x + (long)(t0 + min(tt, nt - 1)) * d + cl);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int tt = tl + 8 * j;
+#pragma unroll
+      for (int v = 0; v < CV; ++v) xr[j].v[v] = (tt < nt && c0 + v < d) ? x[(long)(t0 + tt) * d + c0 + v] : T(0);
+    }
+  }
+  // dlogits of the chunk -> LDS (zero past the chunk's end and for e >= E;
+  // loaded from a clamped valid index, then selected, again without a branch)
+  float dv[kDwrChunk * EB / 256];
+#pragma unroll
+  for (int q = 0; q < kDwrChunk * EB / 256; ++q) {
+    const int i = threadIdx.x + 256 * q, tt = i / EB, e = i % EB;
+    dv[q] = dL[(long)(t0 + min(tt, nt - 1)) * E + min(e, E - 1)];
+  }
+#pragma unroll
+  for (int q = 0; q < kDwrChunk * EB / 256; ++q) {
+    const int i = threadIdx.x + 256 * q;
+    if (!(i / EB < nt && i % EB < E)) dv[q] = 0.f;
+  }
+  if constexpr (!ELEM) {
+    const bool col_ok = c0 + CV <= d;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      if (!(col_ok && tl + 8 * j < nt))
+#pragma unroll
+        for (int v = 0; v < CV; ++v) xr[j].v[v] = T(0);
+  }
+#pragma unroll
+  for (int q = 0; q < kDwrChunk * EB / 256; ++q) {
+    const int i = threadIdx.x + 256 * q;
+    sdl[i / EB][i % EB] = dv[q];
+  }
+  __syncthreads();
   float acc[EB][CV];
 #pragma unroll
   for (int e = 0; e < EB; ++e)
 #pragma unroll
     for (int v = 0; v < CV; ++v) acc[e][v] = 0.f;
-  const bool full = c0 + CV <= d;
-  for (int tb = t0; tb < t1; tb += 64) {
-    const int nt = min(64, t1 - tb);
-    for (int q = threadIdx.x; q < 64 * EB; q += 256) {
-      const int tt = q / EB, e = q % EB;
-      sdl[tt][e] = (tt < nt && e < E) ? dL[(long)(tb + tt) * E + e] : 0.f;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int tt = tl + 8 * j;
+#pragma unroll
+    for (int v = 0; v < CV; ++v) {
+      const float xv = Elt<T>::ld(&xr[j].v[v]);
+#pragma unroll
+      for (int e = 0; e < EB; ++e) acc[e][v] = fmaf(sdl[tt][e], xv, acc[e][v]);
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int tt = tl; tt < 64; tt += 8) {
-      float xv[CV];
-      if (tt < nt && full) {
-        const Vec w = *(const Vec*)(x + (long)(tb + tt) * d + c0);
-#pragma unroll
-        for (int v = 0; v < CV; ++v) xv[v] = Elt<T>::ld(&w.v[v]);
-      } else {
-#pragma unroll
-        for (int v = 0; v < CV; ++v)
-          xv[v] = (tt < nt && c0 + v < d) ? Elt<T>::ld(x + (long)(tb + tt) * d + c0 + v) : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < EB; ++e)
-#pragma unroll
-        for (int v = 0; v < CV; ++v) acc[e][v] = fmaf(sdl[tt][e], xv[v], acc[e][v]);
-    }
-    __syncthreads();
   }
-  // sum the 8 token lanes (fixed order)
+  // sum the 8 token lanes (fixed order; every lane of the group ends with the
+  // same sums), then lane tl writes experts tl, tl + 8, ...: CV contiguous
+  // floats per expert row
 #pragma unroll
   for (int e = 0; e < EB; ++e)
 #pragma unroll
@@ -150,21 +198,43 @@ __global__ __launch_bounds__(256) void router_dwr_partial_kernel(const float* __
       a += __shfl_xor(a, 4, 64);
       acc[e][v] = a;
     }
-  if (tl == 0) {
-    for (int e = 0; e < E; ++e)
+  const bool cols_full = c0 + CV <= d;
+#pragma unroll
+  for (int e = 0; e < EB; ++e) {
+    if ((e & 7) != tl || e >= E) continue;
+    float* dst = part + ((long)chunk * E + e) * d + c0;
+    if (cols_full) {
+      if constexpr (CV % 4 == 0) {
+#pragma unroll
+        for (int v = 0; v < CV; v += 4) *(float4*)(dst + v) = make_float4(acc[e][v], acc[e][v + 1], acc[e][v + 2], acc[e][v + 3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < CV; ++v) dst[v] = acc[e][v];
+      }
+    } else {
 #pragma unroll
       for (int v = 0; v < CV; ++v)
-        if (c0 + v < d) part[((long)chunk * E + e) * d + c0 + v] = acc[e][v];
+        if (c0 + v < d) dst[v] = acc[e][v];
+    }
   }
 }
 
+// out[i] = sum over the nch chunk partials in chunk order (8 loads in flight).
 template <class T>
 __global__ __launch_bounds__(256) void chunk_sum_kernel(const float* __restrict__ part, int nch, long n,
                                                         T* __restrict__ out) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  float s = part[i];
-  for (int c = 1; c < nch; ++c) s += part[(long)c * n + i];
+  float s = 0.f;
+  int c = 0;
+  for (; c + 8 <= nch; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = part[(long)(c + q) * n + i];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s += v[q];
+  }
+  for (; c < nch; ++c) s += part[(long)c * n + i];
   Elt<T>::st(out + i, s);
 }
 
@@ -179,14 +249,32 @@ __global__ __launch_bounds__(256) void router_dx_valu_kernel(const float* __rest
   const int nv = d / V;
   uint4* row = (uint4*)(dx + (long)t * d);
   for (int v = threadIdx.x; v < nv; v += 256) {
+    const uint4 rv = row[v];  // the expert-path gradient, added after the router term
     float acc[V];
-    unpack16<T>(row[v], acc);
-    for (int e = 0; e < E; ++e) {
-      float w[V];
-      unpack16<T>(((const uint4*)(wr + (long)e * d))[v], w);
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = fmaf(sdl[e], w[i], acc[i]);
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    // groups of 8 expert rows, loaded unconditionally (clamped row index) so
+    // that they are in flight together; the FMAs depend on e < E
+#pragma unroll
+    for (int e0 = 0; e0 < EB; e0 += 8) {
+      if (e0 >= E) break;
+      uint4 wv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wv[q] = ((const uint4*)(wr + (long)min(e0 + q, E - 1) * d))[v];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (e0 + q < E) {
+          float w[V];
+          unpack16<T>(wv[q], w);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] = fmaf(sdl[e0 + q], w[i], acc[i]);
+        }
+      }
     }
+    float g[V];
+    unpack16<T>(rv, g);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] += g[i];
     row[v] = pack16<T>(acc);
   }
 }
@@ -236,9 +324,11 @@ template <class T, int EB>
 static void bwd_valu(const float* dL, const void* x, const void* wr, int Tn, int d, int E, void* dx, void* dwr,
                      float* part, hipStream_t s) {
   const int nch = (Tn + kDwrChunk - 1) / kDwrChunk;
-  constexpr int cols_per_block = 32 * (64 / EB);
+  constexpr int CV = 64 / EB;
+  constexpr int cols_per_block = 32 * CV;
   dim3 grid((d + cols_per_block - 1) / cols_per_block, nch);
-  router_dwr_partial_kernel<T, EB><<<grid, 256, 0, s>>>(dL, (const T*)x, Tn, d, E, part);
+  if (d % CV == 0) router_dwr_partial_kernel<T, EB, false><<<grid, 256, 0, s>>>(dL, (const T*)x, Tn, d, E, part);
+  else router_dwr_partial_kernel<T, EB, true><<<grid, 256, 0, s>>>(dL, (const T*)x, Tn, d, E, part);
   const long n = (long)E * d;
   chunk_sum_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, nch, n, (T*)dwr);
   router_dx_valu_kernel<T, EB><<<Tn, 256, 0, s>>>(dL, (const T*)wr, d, E, (T*)dx);
