@@ -238,21 +238,33 @@ __global__ __launch_bounds__(256) void chunk_sum_kernel(const float* __restrict_
   Elt<T>::st(out + i, s);
 }
 
+// dx[t] += sum_e dL[t, e] Wr[e] for TPB = 4 tokens per workgroup: the Wr
+// row pieces a thread loads serve all TPB token rows.
+constexpr int kDxTokens = 4;
 template <class T, int EB>
 __global__ __launch_bounds__(256) void router_dx_valu_kernel(const float* __restrict__ dL, const T* __restrict__ wr,
-                                                             int d, int E, T* __restrict__ dx) {
+                                                             int Tn, int d, int E, T* __restrict__ dx) {
   constexpr int V = Elt<T>::kVec;
-  __shared__ float sdl[EB];
-  const int t = blockIdx.x;
-  if (threadIdx.x < EB) sdl[threadIdx.x] = threadIdx.x < E ? dL[(long)t * E + threadIdx.x] : 0.f;
+  constexpr int TPB = kDxTokens;
+  __shared__ float sdl[TPB][EB];
+  const int t0 = blockIdx.x * TPB;
+  for (int i = threadIdx.x; i < TPB * EB; i += 256) {
+    const int u = i / EB, e = i % EB;
+    sdl[u][e] = (t0 + u < Tn && e < E) ? dL[(long)(t0 + u) * E + e] : 0.f;
+  }
   __syncthreads();
   const int nv = d / V;
-  uint4* row = (uint4*)(dx + (long)t * d);
   for (int v = threadIdx.x; v < nv; v += 256) {
-    const uint4 rv = row[v];  // the expert-path gradient, added after the router term
-    float acc[V];
+    // the expert-path gradient rows (rows past Tn read row Tn - 1 and are
+    // never written), added after the router term
+    uint4 rv[TPB];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int u = 0; u < TPB; ++u) rv[u] = ((const uint4*)(dx + (long)min(t0 + u, Tn - 1) * d))[v];
+    float acc[TPB][V];
+#pragma unroll
+    for (int u = 0; u < TPB; ++u)
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[u][i] = 0.f;
     // groups of 8 expert rows, loaded unconditionally (clamped row index) so
     // that they are in flight together; the FMAs depend on e < E
 #pragma unroll
@@ -267,15 +279,22 @@ __global__ __launch_bounds__(256) void router_dx_valu_kernel(const float* __rest
           float w[V];
           unpack16<T>(wv[q], w);
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] = fmaf(sdl[e0 + q], w[i], acc[i]);
+          for (int u = 0; u < TPB; ++u)
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[u][i] = fmaf(sdl[u][e0 + q], w[i], acc[u][i]);
         }
       }
     }
-    float g[V];
-    unpack16<T>(rv, g);
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] += g[i];
-    row[v] = pack16<T>(acc);
+    for (int u = 0; u < TPB; ++u) {
+      if (t0 + u < Tn) {
+        float g[V];
+        unpack16<T>(rv[u], g);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[u][i] += g[i];
+        ((uint4*)(dx + (long)(t0 + u) * d))[v] = pack16<T>(acc[u]);
+      }
+    }
   }
 }
 
@@ -331,7 +350,7 @@ static void bwd_valu(const float* dL, const void* x, const void* wr, int Tn, int
   else router_dwr_partial_kernel<T, EB, true><<<grid, 256, 0, s>>>(dL, (const T*)x, Tn, d, E, part);
   const long n = (long)E * d;
   chunk_sum_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, nch, n, (T*)dwr);
-  router_dx_valu_kernel<T, EB><<<Tn, 256, 0, s>>>(dL, (const T*)wr, d, E, (T*)dx);
+  router_dx_valu_kernel<T, EB><<<(Tn + kDxTokens - 1) / kDxTokens, 256, 0, s>>>(dL, (const T*)wr, Tn, d, E, (T*)dx);
 }
 
 template <class T>
