@@ -145,6 +145,10 @@ def copy_probe(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": reps}), flush=True)
 
 
+# Expert weight banks above this many fp32 bytes are drawn on the device.
+HOST_WEIGHT_BYTES = 8 << 30
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,8 +188,26 @@ def main():
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     log(f"bench: {cfg.slug} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} h={cfg.h} {cfg.dtype} mode={mode}")
-    inp = inputs.layer_inputs(cfg)
-    t = {n: torch.from_numpy(v).to(dev).to(dt) for n, v in inp.items()}
+    wbytes = 3 * cfg.E * cfg.h * cfg.d * 4
+    if wbytes <= HOST_WEIGHT_BYTES:
+        inp = inputs.layer_inputs(cfg)
+        t = {n: torch.from_numpy(v).to(dev).to(dt) for n, v in inp.items()}
+        weights_on = "host"
+    else:
+        # weight banks too large to draw on the host in reasonable time (the
+        # trillion shape's are 58 GB in fp32): x, wr and dy as usual, the expert
+        # weights from a seeded device generator, same distribution
+        inp = inputs.layer_inputs(cfg, experts=[0])
+        t = {n: torch.from_numpy(v).to(dev).to(dt) for n, v in inp.items() if n in ("x", "wr", "dy")}
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 + cfg.seed)
+        for n, shape in (("w1", (cfg.E, cfg.h, cfg.d)), ("w3", (cfg.E, cfg.h, cfg.d)), ("w2", (cfg.E, cfg.d, cfg.h))):
+            w = torch.empty(shape, device=dev, dtype=dt)
+            for e in range(cfg.E):  # one expert at a time: no fp32 copy of a whole bank
+                w[e] = (torch.randn(shape[1:], device=dev, generator=gen) * cfg.w_std).to(dt)
+            t[n] = w
+            log(f"bench: {n} generated on the device")
+        weights_on = "device"
     forced = None
     if mode != "router":
         forced = torch.from_numpy(inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)).to(dev)
@@ -218,13 +240,39 @@ def main():
         kern[name] = {"launches": n, "avg_us": 1000.0 * ms / max(n, 1)}
     _abi.prof_reset()
 
-    # one clean step without events (events add a little host/GPU overhead)
+    # the same steps again without the library's per-kernel events (they add
+    # a little host/GPU overhead)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(a.steps):
         layer.step(*args, forced_idx=forced)
     torch.cuda.synchronize()
     elapsed_clean = time.perf_counter() - t1
+
+    # Per-step distribution: one event pair per step on torch's current stream
+    # (where the layer launches), back to back, then with the 256 MB Infinity
+    # Cache flushed before each step by writing a 1 GiB scratch buffer outside
+    # the events.
+    def step_distribution(flush):
+        pairs = []
+        for _ in range(a.steps):
+            if flush is not None:
+                flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            layer.step(*args, forced_idx=forced)
+            e1.record()
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = np.array([x.elapsed_time(y) for x, y in pairs])
+        return {"median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
+                "p90": float(np.percentile(ms, 90))}
+
+    dist = step_distribution(None)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dist_flushed = step_distribution(scratch)
+    del scratch
+    log("bench: per-step distributions done")
 
     ms_step = 1000.0 * elapsed / a.steps
     tokens_per_s = cfg.T * a.steps / elapsed
@@ -262,7 +310,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "mxfp8" if cfg.mx else cfg.dtype,
-        "data": "synthetic (seeded: x~N(0,1), weights~N(0,0.02^2), dy~N(0,1); values fixed across steps)",
+        "data": "synthetic (seeded: x~N(0,1), weights~N(0,0.02^2), dy~N(0,1); values fixed across steps"
+                + ("; expert weights drawn on the device)" if weights_on == "device" else ")"),
         "config": {"workload": f"{cfg.slug}: MoE expert layer fwd+bwd, T={cfg.T} d_model={cfg.d} experts={cfg.E} "
                                f"top-{cfg.k} SwiGLU hidden={cfg.h} "
                                f"{'MXFP8 grouped GEMMs (bf16 router/combine)' if cfg.mx else cfg.dtype}, "
@@ -275,6 +324,8 @@ def main():
         "ggemm_frac_bf16_peak": gemm_flops / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
         "ggemm_frac_own_peak": gemm_flops / (gemm_us * 1e-6) / 1e12 / gemm_peak,
         "ms_per_step_no_events": 1000.0 * elapsed_clean / a.steps,
+        "step_ms": dist,
+        "step_ms_cache_flushed": dist_flushed,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": gemm_peak,
                      "unit": "TFLOP/s", "frac": achieved / gemm_peak,
                      "traffic": measured_traffic(dom, f"{cfg.slug}/{mode}"),
