@@ -28,6 +28,14 @@ TRG_DEV void static_for(F&& f) {
 }
 
 // ---- bfloat16 <-> float (storage is raw uint16_t) ---------------------------
+// A 16-byte store with the non-temporal hint, for output rows that the
+// writing kernel does not read again and that go out as whole lines.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+TRG_DEV void store_nt16(void* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (u32x4_t*)p);
+}
+
 TRG_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 TRG_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 TRG_DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

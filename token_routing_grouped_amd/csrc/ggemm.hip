@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
       }
     }
     constexpr int WLDS = STAGE / NW;  // LDS bytes per wave, inside stage 1
-    epilogue<WTM, WTN, CSEL, EPI, WLDS>(g, acc, smem + STAGE + wave * WLDS, lane, wm, wn, e, m0, m_end, n0);
+    epilogue<WTM, WTN, CSEL, EPI, WLDS, MODE == RAGGED_M>(g, acc, smem + STAGE + wave * WLDS, lane, wm, wn, e, m0, m_end, n0);
   }
 }
 

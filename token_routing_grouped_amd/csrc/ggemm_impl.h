@@ -52,6 +52,16 @@ struct Args {
   int tiles_m, tiles_n;
 };
 
+// Staged epilogue rows go out with store_nt16 when NT (the ragged-M GEMMs:
+// 2-6% faster on dgrad-down and down at the small shape; the weight gradients
+// measured no better, or slower, with it).  The SwiGLU-forward epilogue's
+// direct 8-byte stores keep the default policy: as partial lines they rely on
+// L2 merging them, and with the hint that kernel took twice as long.
+TRG_DEV void store_row16(bool nt, void* p, uint4 v) {
+  if (nt) store_nt16(p, v);
+  else *(uint4*)p = v;
+}
+
 TRG_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
   const unsigned n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFL ? 0xFFFFFFFFu : (unsigned)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcFlags);
@@ -196,7 +206,7 @@ constexpr int epilogue_slab_rows() {  // 16 rows when they fit the wave's area, 
   return (EPI == EPI_SWIGLU_BWD ? 2 * 16 * (WTN * 2 + 16) : 16 * (WTN * 2 + 16)) <= WLDS ? 16 : 8;
 }
 
-template <int WTM, int WTN, int CSEL, int EPI, int WLDS>
+template <int WTM, int WTN, int CSEL, int EPI, int WLDS, bool NT>
 TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* wl, int lane, int wm, int wn, int e,
                       int m0, int m_end, int n0) {
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -320,10 +330,10 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
         const int nw = n0 + wn * WTN;
         uint16_t* D = (uint16_t*)g.C;
         store_rows(sG, P, WTN, ms, [&](int m, int c, uint4 v) {
-          if (nw + c < g.N) *(uint4*)(D + (long)m * g.ldc + nw + c) = v;
+          if (nw + c < g.N) store_row16(NT, D + (long)m * g.ldc + nw + c, v);
         });
         store_rows(sU, P, WTN, ms, [&](int m, int c, uint4 v) {
-          if (nw + c < g.N) *(uint4*)(D + (long)m * g.ldc + g.split + nw + c) = v;
+          if (nw + c < g.N) store_row16(NT, D + (long)m * g.ldc + g.split + nw + c, v);
         });
       } else {
         char* sC = wl;
@@ -348,7 +358,7 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
                 mr = m - g.split;
               }
             }
-            *(uint4*)(Cb + (long)e * g.c_es + (long)mr * g.ldc + nw + c) = v;
+            store_row16(NT, Cb + (long)e * g.c_es + (long)mr * g.ldc + nw + c, v);
           }
         });
       }

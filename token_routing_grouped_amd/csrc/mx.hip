@@ -170,8 +170,8 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
           w[q] = e4m3_x4(ldexpf(v[q * 4], -s), ldexpf(v[q * 4 + 1], -s), ldexpf(v[q * 4 + 2], -s),
                          ldexpf(v[q * 4 + 3], -s));
         uint4* dst = (uint4*)(q_row + (long)rr[k] * cols + c);
-        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        store_nt16(dst, make_uint4(w[0], w[1], w[2], w[3]));
+        store_nt16(dst + 1, make_uint4(w[4], w[5], w[6], w[7]));
         uint8_t* sp = s_row + (long)rr[k] * (cols / 32) + c / 32;
         if (row_dw && all == 15u) {
           if (q4 == 0) *(uint32_t*)sp = sw;
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
         w[q] = e4m3_x4(ldexpf(x[q * 4], -s), ldexpf(x[q * 4 + 1], -s), ldexpf(x[q * 4 + 2], -s),
                        ldexpf(x[q * 4 + 3], -s));
       uint4* dst = (uint4*)(q_col + (long)c * ldc + base + sb * 32);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      store_nt16(dst, make_uint4(w[0], w[1], w[2], w[3]));
+      store_nt16(dst + 1, make_uint4(w[4], w[5], w[6], w[7]));
       uint8_t* sp = s_col + (long)c * (ldc / 32) + (base + sb * 32) / 32;
       if (col_dw && all == 15u) {
         if (sb == 0) *(uint32_t*)sp = sw;

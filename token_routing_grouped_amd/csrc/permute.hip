@@ -27,7 +27,9 @@ __global__ __launch_bounds__(256) void permute_kernel(const T* __restrict__ x, i
 
 // y[t] = sum_j w[t,j] * yp[pos[t,j]] (w == nullptr: weights of one), fp32
 // accumulation in slot order, one rounding.
-template <class T>
+// NT: the output rows go out with the non-temporal hint (measured faster for
+// the backward's unpermute-sum, slower for the forward's combine).
+template <class T, bool NT>
 __global__ __launch_bounds__(256) void gather_sum_kernel(const T* __restrict__ yp, const float* __restrict__ w,
                                                          const int* __restrict__ pos, int d, int k,
                                                          T* __restrict__ y) {
@@ -46,7 +48,8 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const T* __restrict__ y
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
     }
-    ((uint4*)(y + (long)t * d))[v] = pack16<T>(acc);
+    if constexpr (NT) store_nt16((uint4*)(y + (long)t * d) + v, pack16<T>(acc));
+    else ((uint4*)(y + (long)t * d))[v] = pack16<T>(acc);
   }
 }
 
@@ -110,10 +113,14 @@ hipError_t launch_permute(const void* x, bool bf16, int T, int d, int k, const i
 hipError_t launch_gather_sum(const void* yp, const float* w, const int* pos, int T, int d, int k, bool bf16,
                              void* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (bf16)
-    gather_sum_kernel<uint16_t><<<T, 256, 0, s>>>((const uint16_t*)yp, w, pos, d, k, (uint16_t*)y);
-  else
-    gather_sum_kernel<float><<<T, 256, 0, s>>>((const float*)yp, w, pos, d, k, (float*)y);
+  const bool nt = w == nullptr;  // the unpermute-sum (no gate weights)
+  if (bf16) {
+    if (nt) gather_sum_kernel<uint16_t, true><<<T, 256, 0, s>>>((const uint16_t*)yp, w, pos, d, k, (uint16_t*)y);
+    else gather_sum_kernel<uint16_t, false><<<T, 256, 0, s>>>((const uint16_t*)yp, w, pos, d, k, (uint16_t*)y);
+  } else {
+    if (nt) gather_sum_kernel<float, true><<<T, 256, 0, s>>>((const float*)yp, w, pos, d, k, (float*)y);
+    else gather_sum_kernel<float, false><<<T, 256, 0, s>>>((const float*)yp, w, pos, d, k, (float*)y);
+  }
   return hipGetLastError();
 }
 
