@@ -31,7 +31,7 @@
  *  - Tensors are contiguous and row-major.  Shapes:
  *      x, y, dx [T,d]; wr, dwr [E,d]; logits, probs [T,E] f32;
  *      topk_idx, pos [T,k] i32; topk_w, dgate [T,k] f32;
- *      counts [E], offsets [E+1], off32 [E+1], src [R] i32;
+ *      counts [E], offsets [E+1], off128 [E+1], src [R] i32;
  *      xp, yp, dyp, dxp [R,d]; g, u, hbuf [R,h]; dgu [R,2h] (dG | dU);
  *      w1, w3, dw1, dw3 [E,h,d]; w2, dw2 [E,d,h]   (output-major, K last).
  *  - dt selects the storage type of activations, weights and gradients:
@@ -110,8 +110,9 @@ moe_status_t moe_router_logits(const void* x, int dt, const void* wr, int T, int
  *                 clamped and flagged, duplicates flagged.
  *   topk_w[t,j] = probs[t, topk_idx[t,j]]  (not renormalised)
  *   counts[e]   = number of (t,j) routed to e; offsets = exclusive prefix sum
- *                 (offsets[E] = T*k); off32 (nullable) = prefix sum of counts
- *                 rounded up to multiples of 32 (MX column blocks).
+ *                 (offsets[E] = T*k); off128 (nullable) = prefix sum of counts
+ *                 rounded up to multiples of 128 (MX column segments: each
+ *                 starts on a 128-byte line of the columnwise copies).
  *   pos[t,j]    = row of (t,j) in the expert-contiguous buffer: offsets[e]
  *                 plus the number of entries (t',j') < (t,j) in (token, slot)
  *                 order routed to the same e.  src[pos[t,j]] = t*k + j.
@@ -121,7 +122,7 @@ moe_status_t moe_router_logits(const void* x, int dt, const void* wr, int T, int
 size_t moe_route_workspace_size(int T, int E, int k);
 moe_status_t moe_route(const float* logits, int T, int E, int k, const int32_t* forced_idx,
                        float* probs, int32_t* topk_idx, float* topk_w, int32_t* counts,
-                       int32_t* offsets, int32_t* pos, int32_t* src, int32_t* off32,
+                       int32_t* offsets, int32_t* pos, int32_t* src, int32_t* off128,
                        int32_t* err_flag, void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -281,7 +282,7 @@ moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, con
  *   rowwise      q [rows, cols] u8, s [rows, cols/32] u8 (blocks along cols)
  *   columnwise   q [cols, ldc] u8, s [cols, ldc/32] u8: blocks of 32
  *                consecutive rows inside each row segment, the last block of
- *                a segment zero-padded; segment e starts at column off32[e]
+ *                a segment zero-padded; segment e starts at column off128[e]
  *                (the transpose of the rowwise form of each padded segment)
  * ---------------------------------------------------------------------------
  *
@@ -290,59 +291,60 @@ moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, con
  *   gather_src (nullable): logical row r is in[gather_src[r] / gather_k]
  *     (pass moe_route's src and k to quantise the routed rows of x straight
  *     from x: the rowwise dispatch and the quantisation in one step).
- *   seg_off / seg_off32 (nullable, [nseg+1]): row segments and their 32-padded
- *     starts (moe_route's offsets / off32); if null, segments of seg_rows rows
+ *   seg_off / seg_off128 (nullable, [nseg+1]): row segments and their padded
+ *     starts: multiples of 32, each padded segment at least as long as its
+ *     segment and at most 127 rows longer (moe_route's offsets / off128); if null, segments of seg_rows rows
  *     (rows a multiple of seg_rows, or seg_rows = rows), each padded to 32.
  *   q_row/s_row (nullable): rowwise output.  q_col/s_col (nullable): columnwise
  *     output with row stride ldc (a multiple of 32, at least the padded row
- *     count: rows + 31*nseg with seg_off, else segments x round32(seg_rows)).
+ *     count: rows + 127*nseg with seg_off, else segments x round32(seg_rows)).
  * cols must be a multiple of 32.  Bit-exact and deterministic.
  */
 moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32_t* gather_src, int gather_k,
-                         const int32_t* seg_off, const int32_t* seg_off32, int nseg, int seg_rows, uint8_t* q_row,
+                         const int32_t* seg_off, const int32_t* seg_off128, int nseg, int seg_rows, uint8_t* q_row,
                          uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, int ldc, void* stream);
 
 /*
  * MXFP8 grouped GEMMs of the expert FFNs: the same SwiGLU forward and backward
  * as moe_grouped_gemm_fwd / _bwd, with every GEMM operand quantised along its
  * own reduction dimension and multiplied on gfx950's scaled matrix cores
- * (fp32 accumulation, bf16 outputs).  d and h must be multiples of 128; r32cap
- * (row stride of every columnwise copy) a multiple of 128 and >= R + 31*E.
+ * (fp32 accumulation, bf16 outputs).  d and h must be multiples of 128; rcap
+ * (row stride of every columnwise copy) a multiple of 128 and >= R + 127*E.
  * The caller quantises x (mx_quantize with gather) and the weights; the calls
  * quantise H, dYp and dG|dU themselves (both layouts, from the stored bf16
  * values).  ws: moe_grouped_gemm_workspace_size() bytes.
  */
 typedef struct {
-  int E, R, d, h, r32cap;
+  int E, R, d, h, rcap;
   const int32_t* offsets;                 /* [E+1] expert row offsets          */
-  const int32_t* off32;                   /* [E+1] 32-padded segment starts    */
+  const int32_t* off128;                   /* [E+1] 128-padded segment starts   */
   const uint8_t* xq; const uint8_t* xs;   /* [R,d], [R,d/32] routed x, rowwise */
   const uint8_t* w1q; const uint8_t* w1s; /* [E,h,d], [E,h,d/32] rowwise       */
   const uint8_t* w3q; const uint8_t* w3s; /* [E,h,d], [E,h,d/32] rowwise       */
   const uint8_t* w2q; const uint8_t* w2s; /* [E,d,h], [E,d,h/32] rowwise       */
   void* g; void* u; void* hbuf;           /* out: [R,h] bf16                   */
   uint8_t* hq; uint8_t* hs;               /* out: [R,h], [R,h/32] rowwise H    */
-  uint8_t* hqT; uint8_t* hsT;             /* out: [h,r32cap], [h,r32cap/32]    */
+  uint8_t* hqT; uint8_t* hsT;             /* out: [h,rcap], [h,rcap/32]    */
   void* yp;                               /* out: [R,d] bf16                   */
   void* ws; size_t ws_bytes;
 } moe_mx_fwd_args;
 
 typedef struct {
-  int E, R, d, h, r32cap;
+  int E, R, d, h, rcap;
   const int32_t* offsets;
-  const int32_t* off32;
+  const int32_t* off128;
   const void* dyp;                          /* [R,d] bf16 (moe_combine_bwd)         */
   uint8_t* dyq; uint8_t* dys;               /* out: [R,d], [R,d/32] rowwise dYp     */
-  uint8_t* dyqT; uint8_t* dysT;             /* out: [d,r32cap], [d,r32cap/32]       */
+  uint8_t* dyqT; uint8_t* dysT;             /* out: [d,rcap], [d,rcap/32]       */
   const void* g; const void* u;             /* [R,h] bf16 from the forward          */
   const uint8_t* hqT; const uint8_t* hsT;   /* columnwise H from the forward        */
-  const uint8_t* xqT; const uint8_t* xsT;   /* [d,r32cap] columnwise routed x       */
+  const uint8_t* xqT; const uint8_t* xsT;   /* [d,rcap] columnwise routed x       */
   const uint8_t* w1tq; const uint8_t* w1ts; /* [d,E*h], [d,E*h/32]: W1 blocked on h */
   const uint8_t* w3tq; const uint8_t* w3ts; /* same for W3                          */
   const uint8_t* w2tq; const uint8_t* w2ts; /* [h,E*d], [h,E*d/32]: W2 blocked on d */
   void* dgu;                                /* out: [R,2h] bf16 (dG | dU)           */
   uint8_t* dguq; uint8_t* dgus;             /* out: [R,2h], [R,2h/32]               */
-  uint8_t* dguqT; uint8_t* dgusT;           /* out: [2h,r32cap], [2h,r32cap/32]     */
+  uint8_t* dguqT; uint8_t* dgusT;           /* out: [2h,rcap], [2h,rcap/32]     */
   void* dxp;                                /* out: [R,d] bf16                      */
   void* dw1; void* dw3; void* dw2;          /* out: weight gradients, bf16          */
   void* ws; size_t ws_bytes;

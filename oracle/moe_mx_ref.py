@@ -68,7 +68,7 @@ def layer_forward_mx(x, wr, w1, w3, w2, k, forced_idx=None, logits=None):
 
 
 def layer_backward_mx(fwd, dy, x, wr, w1, w3, w2):
-    offsets, off32, pos = fwd["offsets"], fwd["off32"], fwd["pos"]
+    offsets, off128, pos = fwd["offsets"], fwd["off128"], fwd["pos"]
     E = len(offsets) - 1
     dyp, dgate = ref.combine_backward(dy, fwd["yp"], fwd["w"], pos)
     dyp = bf16_value(dyp)
@@ -81,11 +81,11 @@ def layer_backward_mx(fwd, dy, x, wr, w1, w3, w2):
             dH[a:b] = dyq_r[a:b] @ mx.qdq_cols(w2[e])
     dG, dU = ref.swiglu_backward(dH, fwd["G"], fwd["U"])
     dG, dU = bf16_value(dG), bf16_value(dU)
-    dyq_c = mx.qdq_cols_segmented(dyp, offsets, off32)
-    hq_c = mx.qdq_cols_segmented(fwd["H"], offsets, off32)
-    dgq_c = mx.qdq_cols_segmented(dG, offsets, off32)
-    duq_c = mx.qdq_cols_segmented(dU, offsets, off32)
-    xq_c = mx.qdq_cols_segmented(fwd["xp"], offsets, off32)
+    dyq_c = mx.qdq_cols_segmented(dyp, offsets, off128)
+    hq_c = mx.qdq_cols_segmented(fwd["H"], offsets, off128)
+    dgq_c = mx.qdq_cols_segmented(dG, offsets, off128)
+    duq_c = mx.qdq_cols_segmented(dU, offsets, off128)
+    xq_c = mx.qdq_cols_segmented(fwd["xp"], offsets, off128)
     dgq_r, duq_r = mx.qdq_rows(dG), mx.qdq_rows(dU)
     dxp = np.zeros((R, d))
     dw1 = np.zeros((E, h, d))

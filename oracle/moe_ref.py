@@ -30,8 +30,9 @@ Readings taken where the pages are silent (plainest reading):
   * dropless: every routed row is kept; sum(counts) = T*k.
   * offsets are the exclusive prefix sum of counts (length E+1, unpadded);
     within an expert, rows are in ascending token order (a stable counting
-    sort; unique because a token never picks an expert twice).  ``off32`` is
-    the same prefix sum over counts rounded up to 32 (MX column blocks).
+    sort; unique because a token never picks an expert twice).  ``off128`` is
+    the same prefix sum over counts rounded up to 128 (starts of the MX
+    column segments; a layout choice, the pages fix none).
   * expert FFN: SwiGLU without biases, silu on the W1 branch:
     G = Xp W1^T, U = Xp W3^T, H = silu(G) * U, Yp = H W2^T.
     Weight layouts: w1, w3 [E, h, d]; w2 [E, d, h] (output, input).
@@ -84,7 +85,7 @@ def route(logits, k, forced_idx=None, dtype=F):
       counts [E], offsets [E+1]        -- histogram and its exclusive prefix sum
       pos [T,k]  -- row of (t, j) in the expert-contiguous buffer
       src [R]    -- inverse map: src[pos[t, j]] = t*k + j
-      off32 [E+1] -- prefix sum of counts rounded up to multiples of 32
+      off128 [E+1] -- prefix sum of counts rounded up to multiples of 128
     """
     L = np.asarray(logits)
     T, E = L.shape
@@ -100,10 +101,10 @@ def route(logits, k, forced_idx=None, dtype=F):
     pos = np.empty(T * k, np.int64)
     pos[src] = np.arange(T * k)
     pos = pos.reshape(T, k)
-    c32 = (counts + 31) // 32 * 32
-    off32 = np.concatenate([[0], np.cumsum(c32)]).astype(np.int64)
+    c128 = (counts + 127) // 128 * 128
+    off128 = np.concatenate([[0], np.cumsum(c128)]).astype(np.int64)
     return dict(probs=probs, idx=idx, w=w, counts=counts, offsets=offsets, pos=pos,
-                src=src, off32=off32)
+                src=src, off128=off128)
 
 
 # ----------------------------------------------------------------------------

@@ -26,7 +26,7 @@ Layouts:
                   [off_e, off_{e+1}) of an [R, K] matrix; a partial last block
                   is zero-padded; blocks never straddle experts.  Stored as the
                   rowwise form of the transpose: qT [K, R32], sT [K, R32/32]
-                  with segment e starting at column off32[e].
+                  with segment e starting at column off128[e].
 """
 
 from __future__ import annotations
@@ -103,18 +103,18 @@ def dequantize_rows(q, scales):
     return v.reshape(M, K)
 
 
-def quantize_cols_segmented(a, offsets, off32):
+def quantize_cols_segmented(a, offsets, off128):
     """Column-per-segment MX quantisation of [R, K] -> (qT [K, R32], sT [K, R32/32])."""
     a = np.asarray(a, np.float64)
     R, K = a.shape
     E = len(offsets) - 1
-    R32 = int(off32[E])
+    R32 = int(off128[E])
     qT = np.zeros((K, R32), np.uint8)
     sT = np.zeros((K, R32 // BLOCK), np.uint8)
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        base = int(off32[e])
-        n32 = int(off32[e + 1]) - base
+        base = int(off128[e])
+        n32 = int(off128[e + 1]) - base
         if n32 == 0:
             continue
         seg = np.zeros((n32, K))
@@ -125,7 +125,7 @@ def quantize_cols_segmented(a, offsets, off32):
     return qT, sT
 
 
-def dequantize_cols_segmented(qT, sT, offsets, off32):
+def dequantize_cols_segmented(qT, sT, offsets, off128):
     """Inverse layout of ``quantize_cols_segmented`` back to [R, K]."""
     K = qT.shape[0]
     E = len(offsets) - 1
@@ -134,7 +134,7 @@ def dequantize_cols_segmented(qT, sT, offsets, off32):
     full = dequantize_rows(qT, sT)
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        base = int(off32[e])
+        base = int(off128[e])
         out[lo:hi] = full[:, base:base + hi - lo].T
     return out
 
@@ -143,8 +143,8 @@ def qdq_rows(a):
     return dequantize_rows(*quantize_rows(a))
 
 
-def qdq_cols_segmented(a, offsets, off32):
-    return dequantize_cols_segmented(*quantize_cols_segmented(a, offsets, off32), offsets, off32)
+def qdq_cols_segmented(a, offsets, off128):
+    return dequantize_cols_segmented(*quantize_cols_segmented(a, offsets, off128), offsets, off128)
 
 
 def qdq_cols(a):

@@ -112,13 +112,13 @@ def test_mx_host_side_validation_without_gpu():
     st = lib.mx_quantize(None, 1, 4, 64, None, 1, None, None, 0, 4, None, None, None, None, 0, None)
     assert st == 1 and b"nothing to write" in lib.moe_last_error_string()
     # MX grouped GEMM needs d, h multiples of 128
-    a = _abi.MxFwdArgs(E=2, R=8, d=192, h=128, r32cap=128)
+    a = _abi.MxFwdArgs(E=2, R=8, d=192, h=128, rcap=128)
     assert lib.moe_grouped_gemm_fwd_mx(ctypes.byref(a), None) == 1
-    # r32cap below R + 31*E
-    a = _abi.MxFwdArgs(E=4, R=8, d=128, h=128, r32cap=128)
+    # rcap below R + 127*E
+    a = _abi.MxFwdArgs(E=4, R=8, d=128, h=128, rcap=128)
     assert lib.moe_grouped_gemm_fwd_mx(ctypes.byref(a), None) == 1
-    # r32cap not a multiple of 128
-    a = _abi.MxFwdArgs(E=2, R=8, d=128, h=128, r32cap=96)
+    # rcap not a multiple of 128
+    a = _abi.MxFwdArgs(E=2, R=8, d=128, h=128, rcap=96)
     assert lib.moe_grouped_gemm_fwd_mx(ctypes.byref(a), None) == 1
     assert b"multiple of 128" in lib.moe_last_error_string()
 

@@ -83,7 +83,7 @@ def test_layer_parity(case):
     b = ref.layer_backward(f, dy, x, wr, w1, w3, w2)
 
     for n, g in (("counts", layer.counts), ("offsets", layer.offsets), ("pos", layer.pos), ("src", layer.src),
-                 ("off32", layer.off32)):
+                 ("off128", layer.off128)):
         assert (to_np(g) == f[n]).all(), n
     assert (to_np(layer.topk_idx) == f["idx"]).all()
     assert np.allclose(to_np(layer.topk_w), f["w"], rtol=1e-4, atol=1e-7)

@@ -113,17 +113,17 @@ def test_mx_quantize_gather_both_layouts(T, E, k, cols, mode):
     rt = _routing(T, E, k, T + E, mode)
     x = _special_matrix(T, cols, 3 * T)
     R = T * k
-    rc = (R + 31 * E + 31) // 32 * 32
+    rc = (R + 127 * E + 127) // 128 * 128
     q, s, qT, sT = _u8(R, cols), _u8(R, cols // 32), _u8(cols, rc), _u8(cols, rc // 32)
     i32 = lambda a: _dev(np.asarray(a, np.int32), torch.int32)
     _abi.mx_quantize(_dev(x, torch.bfloat16), R, q, s, qT, sT, gather_src=i32(rt["src"]), gather_k=k,
-                     seg_off=i32(rt["offsets"]), seg_off32=i32(rt["off32"]))
+                     seg_off=i32(rt["offsets"]), seg_off128=i32(rt["off128"]))
     torch.cuda.synchronize()
     xp = ref.permute(x, rt["pos"])
     rq, rs = mx.quantize_rows(xp)
     assert (q.cpu().numpy() == rq).all() and (s.cpu().numpy() == rs).all()
-    cq, cs = mx.quantize_cols_segmented(xp, rt["offsets"], rt["off32"])
-    R32 = int(rt["off32"][-1])
+    cq, cs = mx.quantize_cols_segmented(xp, rt["offsets"], rt["off128"])
+    R32 = int(rt["off128"][-1])
     assert (qT.cpu().numpy()[:, :R32] == cq).all()
     assert (sT.cpu().numpy()[:, :R32 // 32] == cs).all()
 
@@ -211,7 +211,7 @@ def test_mx_layer_deterministic():
         layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, mx=True)
         layer.step(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])
         torch.cuda.synchronize()
-        R32 = int(layer.off32[-1].item())  # columnwise copies are written up to the last padded segment
+        R32 = int(layer.off128[-1].item())  # columnwise copies are written up to the last padded segment
         outs.append([a.clone() for a in (layer.y, layer.dx, layer.dw1, layer.dw2, layer.xq, layer.hqT[:, :R32],
                                          layer.dguqT[:, :R32])])
     for a, b in zip(*outs):

@@ -1,5 +1,5 @@
 """GPU parity of moe_route against the oracle on identical float32 logits:
-indices, counts, offsets, positions, src and off32 bit-exact; probabilities and
+indices, counts, offsets, positions, src and off128 bit-exact; probabilities and
 gates to float tolerance."""
 
 import numpy as np
@@ -24,12 +24,12 @@ def _run(logits, k, forced=None):
     out = dict(probs=torch.empty(T, E, dtype=f32, device=dev), idx=torch.empty(T, k, dtype=i32, device=dev),
                w=torch.empty(T, k, dtype=f32, device=dev), counts=torch.empty(E, dtype=i32, device=dev),
                offsets=torch.empty(E + 1, dtype=i32, device=dev), pos=torch.empty(T, k, dtype=i32, device=dev),
-               src=torch.empty(T * k, dtype=i32, device=dev), off32=torch.empty(E + 1, dtype=i32, device=dev),
+               src=torch.empty(T * k, dtype=i32, device=dev), off128=torch.empty(E + 1, dtype=i32, device=dev),
                err=torch.zeros(1, dtype=i32, device=dev))
     ws = _abi.workspace(_abi.moe_route_workspace_size(T, E, k), dev)
     fi = None if forced is None else torch.from_numpy(np.ascontiguousarray(forced, np.int32)).to(dev)
     _abi.moe_route(L, k, out["probs"], out["idx"], out["w"], out["counts"], out["offsets"], out["pos"], out["src"],
-                   ws, off32=out["off32"], forced_idx=fi, err_flag=out["err"])
+                   ws, off128=out["off128"], forced_idx=fi, err_flag=out["err"])
     torch.cuda.synchronize()
     return {n: t.cpu().numpy() for n, t in out.items()}
 
@@ -40,7 +40,7 @@ def _compare(g, r, k):
     assert (g["offsets"] == r["offsets"]).all(), "offsets"
     assert (g["pos"] == r["pos"]).all(), "pos"
     assert (g["src"] == r["src"]).all(), "src"
-    assert (g["off32"] == r["off32"]).all(), "off32"
+    assert (g["off128"] == r["off128"]).all(), "off128"
     assert np.allclose(g["probs"], r["probs"], rtol=1e-5, atol=1e-9), "probs"
     assert np.allclose(g["w"], r["w"], rtol=1e-5, atol=1e-9), "gates"
 

@@ -137,11 +137,11 @@ def test_column_segment_layout():
     T, E, k, K = 45, 6, 2, 64
     rt = ref.route(rng.standard_normal((T, E)).astype(np.float32), k)
     a = rng.standard_normal((T * k, K))
-    qT, sT = mx.quantize_cols_segmented(a, rt["offsets"], rt["off32"])
-    off, off32 = rt["offsets"], rt["off32"]
+    qT, sT = mx.quantize_cols_segmented(a, rt["offsets"], rt["off128"])
+    off, off128 = rt["offsets"], rt["off128"]
     for e in range(E):
         n = int(off[e + 1] - off[e])
-        base = int(off32[e])
+        base = int(off128[e])
         # brute force per column and block
         for c in range(0, K, 7):
             for b0 in range(0, n, 32):
@@ -152,8 +152,8 @@ def test_column_segment_layout():
                 assert (qT[c, base + b0: base + b0 + 32] == qb[0]).all()
                 assert sT[c, (base + b0) // 32] == sb[0, 0]
         # padding is zero
-        assert (qT[:, base + n: int(off32[e + 1])] == 0).all()
-    back = mx.dequantize_cols_segmented(qT, sT, off, off32)
+        assert (qT[:, base + n: int(off128[e + 1])] == 0).all()
+    back = mx.dequantize_cols_segmented(qT, sT, off, off128)
     assert back.shape == a.shape
     assert np.max(np.abs(back - a)) <= np.max(np.abs(a)) * 2 ** -3
 

@@ -56,7 +56,7 @@ def test_hand_case_golden():
     assert rt["offsets"].tolist() == [int(v) for v in g["offsets"][0]]
     assert rt["pos"].tolist() == [[int(v) for v in r] for r in g["pos"]]
     assert rt["src"].tolist() == [int(v) for v in g["src"][0]]
-    assert rt["off32"].tolist() == [int(v) for v in g["off32"][0]]
+    assert rt["off128"].tolist() == [int(v) for v in g["off128"][0]]
     assert np.allclose(rt["w"][1], g["w_t1"][0], rtol=0, atol=1e-15)
     # gates of t0 from the definition of softmax, by hand
     den = math.exp(1) + 2 * math.exp(2) + math.exp(0.5)
@@ -105,9 +105,9 @@ def test_metadata_invariants(T, E, k, seed):
         seg = src[off[e]:off[e + 1]]
         assert (idx.ravel()[seg] == e).all()
         assert (np.diff(seg // k) > 0).all()
-    c32 = rt["off32"]
-    assert c32[0] == 0 and (np.diff(c32) % 32 == 0).all() and (np.diff(c32) >= counts).all()
-    assert (np.diff(c32) - counts < 32).all()
+    c128 = rt["off128"]
+    assert c128[0] == 0 and (np.diff(c128) % 128 == 0).all() and (np.diff(c128) >= counts).all()
+    assert (np.diff(c128) - counts < 128).all()
 
 
 def test_softmax_closed_forms():

@@ -60,16 +60,16 @@ _SIGS = {
 
 class MxFwdArgs(ctypes.Structure):
     """moe_mx_fwd_args (include/moe.h)."""
-    _fields_ = [(n, ctypes.c_int) for n in ("E", "R", "d", "h", "r32cap")] + \
-        [(n, ctypes.c_void_p) for n in ("offsets", "off32", "xq", "xs", "w1q", "w1s", "w3q", "w3s", "w2q", "w2s", "g",
+    _fields_ = [(n, ctypes.c_int) for n in ("E", "R", "d", "h", "rcap")] + \
+        [(n, ctypes.c_void_p) for n in ("offsets", "off128", "xq", "xs", "w1q", "w1s", "w3q", "w3s", "w2q", "w2s", "g",
                                         "u", "hbuf", "hq", "hs", "hqT", "hsT", "yp", "ws")] + \
         [("ws_bytes", ctypes.c_size_t)]
 
 
 class MxBwdArgs(ctypes.Structure):
     """moe_mx_bwd_args (include/moe.h)."""
-    _fields_ = [(n, ctypes.c_int) for n in ("E", "R", "d", "h", "r32cap")] + \
-        [(n, ctypes.c_void_p) for n in ("offsets", "off32", "dyp", "dyq", "dys", "dyqT", "dysT", "g", "u", "hqT", "hsT",
+    _fields_ = [(n, ctypes.c_int) for n in ("E", "R", "d", "h", "rcap")] + \
+        [(n, ctypes.c_void_p) for n in ("offsets", "off128", "dyp", "dyq", "dys", "dyqT", "dysT", "g", "u", "hqT", "hsT",
                                         "xqT", "xsT", "w1tq", "w1ts", "w3tq", "w3ts", "w2tq", "w2ts", "dgu", "dguq",
                                         "dgus", "dguqT", "dgusT", "dxp", "dw1", "dw3", "dw2", "ws")] + \
         [("ws_bytes", ctypes.c_size_t)]
@@ -196,17 +196,17 @@ def moe_router_logits(x, wr, logits):
     _check(lib().moe_router_logits(_p(x), _dt(x), _p(wr), T, d, E, _p(logits), _stream()), "moe_router_logits")
 
 
-def moe_route(logits, k, probs, topk_idx, topk_w, counts, offsets, pos, src, ws, off32=None, forced_idx=None,
+def moe_route(logits, k, probs, topk_idx, topk_w, counts, offsets, pos, src, ws, off128=None, forced_idx=None,
               err_flag=None):
     T, E = logits.shape
     for t, n, dt in ((logits, "logits", torch.float32), (probs, "probs", torch.float32),
                      (topk_w, "topk_w", torch.float32), (topk_idx, "topk_idx", torch.int32),
                      (counts, "counts", torch.int32), (offsets, "offsets", torch.int32), (pos, "pos", torch.int32),
-                     (src, "src", torch.int32), (off32, "off32", torch.int32), (forced_idx, "forced_idx", torch.int32),
+                     (src, "src", torch.int32), (off128, "off128", torch.int32), (forced_idx, "forced_idx", torch.int32),
                      (err_flag, "err_flag", torch.int32)):
         _expect(t, dt, n)
     _check(lib().moe_route(_p(logits), T, E, k, _p(forced_idx), _p(probs), _p(topk_idx), _p(topk_w), _p(counts),
-                           _p(offsets), _p(pos), _p(src), _p(off32), _p(err_flag), _p(ws), ws.numel(), _stream()),
+                           _p(offsets), _p(pos), _p(src), _p(off128), _p(err_flag), _p(ws), ws.numel(), _stream()),
            "moe_route")
 
 
@@ -327,17 +327,17 @@ def moe_balance(probs, counts, k, alpha, stats, ws, aux_g=None, mean_probs=None)
 # ---------------------------------------------------------------------------
 
 def mx_quantize(x, rows, q_row=None, s_row=None, q_col=None, s_col=None, gather_src=None, gather_k=1, seg_off=None,
-                seg_off32=None, seg_rows=0):
+                seg_off128=None, seg_rows=0):
     """Quantise `rows` rows of x (bf16/f32, [*, cols]) to rowwise and/or
     columnwise MX (E4M3 + E8M0); see mx_quantize in include/moe.h."""
     cols = x.shape[1]
     nseg = 0 if seg_off is None else seg_off.numel() - 1
     for t, n in ((q_row, "q_row"), (s_row, "s_row"), (q_col, "q_col"), (s_col, "s_col")):
         _expect(t, torch.uint8, n)
-    for t, n in ((gather_src, "gather_src"), (seg_off, "seg_off"), (seg_off32, "seg_off32")):
+    for t, n in ((gather_src, "gather_src"), (seg_off, "seg_off"), (seg_off128, "seg_off128")):
         _expect(t, torch.int32, n)
     ldc = 0 if q_col is None else q_col.shape[1]
-    _check(lib().mx_quantize(_p(x), _dt(x), rows, cols, _p(gather_src), gather_k, _p(seg_off), _p(seg_off32), nseg,
+    _check(lib().mx_quantize(_p(x), _dt(x), rows, cols, _p(gather_src), gather_k, _p(seg_off), _p(seg_off128), nseg,
                              seg_rows, _p(q_row), _p(s_row), _p(q_col), _p(s_col), ldc, _stream()), "mx_quantize")
 
 

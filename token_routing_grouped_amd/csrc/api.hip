@@ -215,7 +215,7 @@ size_t moe_route_workspace_size(int T, int E, int k) {
 
 moe_status_t moe_route(const float* logits, int T, int E, int k, const int32_t* forced_idx, float* probs,
                        int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* pos,
-                       int32_t* src, int32_t* off32, int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
+                       int32_t* src, int32_t* off128, int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "moe_route";
   TRY(check_tk(fn, T, k));
   if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
@@ -231,7 +231,7 @@ moe_status_t moe_route(const float* logits, int T, int E, int k, const int32_t* 
   TRY(check_device());
   trg::ProfScope ps(fn, (hipStream_t)stream);
   return hip_status(fn, trg::launch_route(logits, T, E, k, forced_idx, probs, topk_idx, topk_w, counts, offsets, pos,
-                                          src, off32, err_flag, ws, (hipStream_t)stream));
+                                          src, off128, err_flag, ws, (hipStream_t)stream));
 }
 
 moe_status_t moe_permute(const void* x, int dt, int T, int d, int k, const int32_t* pos, void* xp, void* stream) {
@@ -449,7 +449,7 @@ moe_status_t moe_balance(const float* probs, const int32_t* counts, int T, int E
 }
 
 moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32_t* gather_src, int gather_k,
-                         const int32_t* seg_off, const int32_t* seg_off32, int nseg, int seg_rows, uint8_t* q_row,
+                         const int32_t* seg_off, const int32_t* seg_off128, int nseg, int seg_rows, uint8_t* q_row,
                          uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, int ldc, void* stream) {
   const char* fn = "mx_quantize";
   TRY(check_dt(fn, dt));
@@ -461,16 +461,16 @@ moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32
   if (gather_src && gather_k < 1) return fail(MOE_ERR_INVALID_ARG, "%s: gather_k must be >= 1", fn);
   long padded;
   if (seg_off) {
-    if (!seg_off32) return fail(MOE_ERR_INVALID_ARG, "%s: seg_off32 is required with seg_off", fn);
+    if (!seg_off128) return fail(MOE_ERR_INVALID_ARG, "%s: seg_off128 is required with seg_off", fn);
     if (nseg < 1 || nseg > 65536) return fail(MOE_ERR_INVALID_ARG, "%s: nseg must be in [1, 65536]", fn);
-    padded = ((long)rows + 31L * nseg + 31) / 32 * 32;
+    padded = ((long)rows + 127L * nseg + 31) / 32 * 32;
   } else {
     if (seg_rows < 1 || (seg_rows != rows && (seg_rows % 32 != 0 || rows % seg_rows != 0)))
       return fail(MOE_ERR_INVALID_ARG, "%s: seg_rows must equal rows, or be a multiple of 32 dividing rows", fn);
     const long seg32 = ((long)seg_rows + 31) / 32 * 32;
     padded = rows == 0 ? 0 : ((long)rows + seg_rows - 1) / seg_rows * seg32;
   }
-  if (q_col && (ldc % 32 != 0 || ldc < (seg_off ? (long)rows + 31L * nseg : padded)))
+  if (q_col && (ldc % 32 != 0 || ldc < (seg_off ? (long)rows + 127L * nseg : padded)))
     return fail(MOE_ERR_INVALID_ARG, "%s: ldc must be a multiple of 32 and cover the padded rows", fn);
   if (padded >= (1L << 31) || (long)rows * cols >= (1L << 31) * 16L)
     return fail(MOE_ERR_UNSUPPORTED, "%s: problem too large", fn);
@@ -481,20 +481,20 @@ moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32
   TRY(check_device());
   trg::ProfScope ps(fn, (hipStream_t)stream);
   return hip_status(fn, trg::launch_mx_quantize(in, dt == MOE_BF16, cols, rows, cols, gather_src, gather_k, seg_off,
-                                                seg_off32, nseg, seg_rows, (int)(padded / 32), q_row, s_row, q_col,
+                                                seg_off128, nseg, seg_rows, (int)(padded / 32), q_row, s_row, q_col,
                                                 s_col, ldc, (hipStream_t)stream));
 }
 
-static moe_status_t check_mx_dims(const char* fn, int E, int R, int d, int h, int r32cap, const void* ws,
+static moe_status_t check_mx_dims(const char* fn, int E, int R, int d, int h, int rcap, const void* ws,
                                   size_t ws_bytes) {
   if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
   if (R < 0) return fail(MOE_ERR_INVALID_ARG, "%s: R must be >= 0", fn);
   if (d <= 0 || h <= 0 || d % 128 != 0 || h % 128 != 0)
     return fail(MOE_ERR_INVALID_ARG, "%s: d and h must be positive multiples of 128", fn);
-  if (r32cap % 128 != 0 || (long)r32cap < (long)R + 31L * E)
-    return fail(MOE_ERR_INVALID_ARG, "%s: r32cap must be a multiple of 128 and >= R + 31*E", fn);
+  if (rcap % 128 != 0 || (long)rcap < (long)R + 127L * E)
+    return fail(MOE_ERR_INVALID_ARG, "%s: rcap must be a multiple of 128 and >= R + 127*E", fn);
   const long widest = 2L * h > d ? 2L * h : (long)d;
-  if ((long)R * widest * 2 >= (1L << 31) || (long)widest * r32cap >= (1L << 31))
+  if ((long)R * widest * 2 >= (1L << 31) || (long)widest * rcap >= (1L << 31))
     return fail(MOE_ERR_UNSUPPORTED, "%s: operands larger than 2^31 bytes", fn);
   const size_t need = trg::ggemm_ws_bytes(E, R, d, h);
   if (ws == nullptr || ws_bytes < need)
@@ -506,8 +506,8 @@ static moe_status_t check_mx_dims(const char* fn, int E, int R, int d, int h, in
 moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* a, void* stream) {
   const char* fn = "moe_grouped_gemm_fwd_mx";
   if (!a) return fail(MOE_ERR_INVALID_ARG, "%s: args is null", fn);
-  TRY(check_mx_dims(fn, a->E, a->R, a->d, a->h, a->r32cap, a->ws, a->ws_bytes));
-  TRY(check_ptrs(fn, {{"offsets", a->offsets}, {"off32", a->off32}, {"w1q", a->w1q}, {"w1s", a->w1s},
+  TRY(check_mx_dims(fn, a->E, a->R, a->d, a->h, a->rcap, a->ws, a->ws_bytes));
+  TRY(check_ptrs(fn, {{"offsets", a->offsets}, {"off128", a->off128}, {"w1q", a->w1q}, {"w1s", a->w1s},
                       {"w3q", a->w3q}, {"w3s", a->w3s}, {"w2q", a->w2q}, {"w2s", a->w2s}}));
   if (a->R == 0) return ok();
   TRY(check_ptrs(fn, {{"xq", a->xq}, {"xs", a->xs}, {"hbuf", a->hbuf}, {"hq", a->hq}, {"hs", a->hs},
@@ -519,7 +519,7 @@ moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* a, void* stream) {
 moe_status_t moe_grouped_gemm_recompute_gu_mx(const moe_mx_fwd_args* a, void* stream) {
   const char* fn = "moe_grouped_gemm_recompute_gu_mx";
   if (!a) return fail(MOE_ERR_INVALID_ARG, "%s: args is null", fn);
-  TRY(check_mx_dims(fn, a->E, a->R, a->d, a->h, a->r32cap, a->ws, a->ws_bytes));
+  TRY(check_mx_dims(fn, a->E, a->R, a->d, a->h, a->rcap, a->ws, a->ws_bytes));
   TRY(check_ptrs(fn, {{"offsets", a->offsets}, {"w1q", a->w1q}, {"w1s", a->w1s}, {"w3q", a->w3q}, {"w3s", a->w3s}}));
   if (a->R == 0) return ok();
   TRY(check_ptrs(fn, {{"xq", a->xq}, {"xs", a->xs}, {"g", a->g}, {"u", a->u}}));
@@ -530,8 +530,8 @@ moe_status_t moe_grouped_gemm_recompute_gu_mx(const moe_mx_fwd_args* a, void* st
 moe_status_t moe_grouped_gemm_bwd_mx(const moe_mx_bwd_args* a, void* stream) {
   const char* fn = "moe_grouped_gemm_bwd_mx";
   if (!a) return fail(MOE_ERR_INVALID_ARG, "%s: args is null", fn);
-  TRY(check_mx_dims(fn, a->E, a->R, a->d, a->h, a->r32cap, a->ws, a->ws_bytes));
-  TRY(check_ptrs(fn, {{"offsets", a->offsets}, {"off32", a->off32}, {"w1tq", a->w1tq}, {"w1ts", a->w1ts},
+  TRY(check_mx_dims(fn, a->E, a->R, a->d, a->h, a->rcap, a->ws, a->ws_bytes));
+  TRY(check_ptrs(fn, {{"offsets", a->offsets}, {"off128", a->off128}, {"w1tq", a->w1tq}, {"w1ts", a->w1ts},
                       {"w3tq", a->w3tq}, {"w3ts", a->w3ts}, {"w2tq", a->w2tq}, {"w2ts", a->w2ts}, {"dw1", a->dw1},
                       {"dw3", a->dw3}, {"dw2", a->dw2}}));
   TRY(check_ptrs(fn, {{"dyq", a->dyq}, {"dys", a->dys}, {"dyqT", a->dyqT}, {"dysT", a->dysT}, {"hqT", a->hqT},

@@ -10,7 +10,8 @@
 //   forward      up (SwiGLU epilogue), down                 ragged M
 //   backward     dgrad down (SwiGLU-bwd epilogue), dgrad up  ragged M
 //                wgrad down, wgrad up                        ragged K over
-//                the experts' 32-padded column segments
+//                the experts' column segments (padded to 128
+//                rows, so every K step's row pieces start on a 128-byte line)
 // The scheduler, the HBM->LDS operand path and the epilogues are the bf16
 // kernel's (ggemm_impl.h).  Differences:
 //   * K step of 128 bytes = 128 values: LDS rows stay 128 bytes.
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
                                        : c.rsB;
       }
     } else {
-      // weight gradients: K = the expert's 32-padded column segment
+      // weight gradients: K = the expert's 128-padded column segment
       const int per_e = g.tiles_m * g.tiles_n;
       c.e = t / per_e;
       const int r = t - c.e * per_e;
@@ -379,8 +380,8 @@ static hipError_t mx_fwd_bm(const MxFwd& p, const int* tile_off, hipStream_t s) 
   // H -> rowwise MX (down GEMM) and columnwise per expert (wgrad down)
   {
     ProfScope ps("mx_quantize_h", s);
-    const hipError_t err = launch_mx_quantize(p.hbuf, true, h, R, h, nullptr, 1, p.offsets, p.off32, E, 0,
-                                              (R + 31 * E + 31) / 32, p.hq, p.hs, p.hqT, p.hsT, p.r32cap, s);
+    const hipError_t err = launch_mx_quantize(p.hbuf, true, h, R, h, nullptr, 1, p.offsets, p.off128, E, 0,
+                                              (R + 127 * E + 31) / 32, p.hq, p.hs, p.hqT, p.hsT, p.rcap, s);
     if (err != hipSuccess) return err;
   }
   {  // down projection: hq [R,h] x W2q [E,d,h]
@@ -431,8 +432,8 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, hipStream_t s
   }
   {
     ProfScope ps("mx_quantize_dgu", s);
-    const hipError_t err = launch_mx_quantize(p.dgu, true, 2L * h, R, 2 * h, nullptr, 1, p.offsets, p.off32, E, 0,
-                                              (R + 31 * E + 31) / 32, p.dguq, p.dgus, p.dguqT, p.dgusT, p.r32cap, s);
+    const hipError_t err = launch_mx_quantize(p.dgu, true, 2L * h, R, 2 * h, nullptr, 1, p.offsets, p.off128, E, 0,
+                                              (R + 127 * E + 31) / 32, p.dguq, p.dgus, p.dguqT, p.dgusT, p.rcap, s);
     if (err != hipSuccess) return err;
   }
   {  // dgrad up: dguq [R,2h] x (W1 | W3) blocked along h ([d, E*h] each)
@@ -457,8 +458,8 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
   tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, E, tile_off);
   {  // dYp -> rowwise (dgrad down) and columnwise per expert (wgrad down)
     ProfScope ps("mx_quantize_dy", s);
-    const hipError_t err = launch_mx_quantize(p.dyp, true, d, R, d, nullptr, 1, p.offsets, p.off32, E, 0,
-                                              (R + 31 * E + 31) / 32, p.dyq, p.dys, p.dyqT, p.dysT, p.r32cap, s);
+    const hipError_t err = launch_mx_quantize(p.dyp, true, d, R, d, nullptr, 1, p.offsets, p.off128, E, 0,
+                                              (R + 127 * E + 31) / 32, p.dyq, p.dys, p.dyqT, p.dysT, p.rcap, s);
     if (err != hipSuccess) return err;
   }
   {
@@ -466,14 +467,14 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
         small_rows(E, R) ? mx_dgrad_bm<128>(p, tile_off, s) : mx_dgrad_bm<256>(p, tile_off + (E + 1), s);
     if (err != hipSuccess) return err;
   }
-  const long sc = p.r32cap / 32;
+  const long sc = p.rcap / 32;
   {  // wgrad down: dW2[e] = dYp_e^T H_e over the expert's padded segment
     Args a{};
-    a.A = (const uint16_t*)p.dyqT; a.lda = p.r32cap;
-    a.B = (const uint16_t*)p.hqT; a.ldb = p.r32cap;
+    a.A = (const uint16_t*)p.dyqT; a.lda = p.rcap;
+    a.B = (const uint16_t*)p.hqT; a.ldb = p.rcap;
     a.C = p.dw2; a.ldc = h; a.c_es = (long)d * h;
     a.M = d; a.N = h;
-    a.offsets = p.off32; a.E = E; a.R = R;
+    a.offsets = p.off128; a.E = E; a.R = R;
     a.tiles_m = cdiv(d, 256); a.tiles_n = cdiv(h, 256);
     MxArgs x{};
     x.sA = p.dysT; x.lds_a = sc; x.sA_bytes = (long)d * sc;
@@ -483,11 +484,11 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
   }
   {  // wgrad up: [dW1; dW3][e] = [dG | dU]_e^T Xp_e
     Args a{};
-    a.A = (const uint16_t*)p.dguqT; a.lda = p.r32cap;
-    a.B = (const uint16_t*)p.xqT; a.ldb = p.r32cap;
+    a.A = (const uint16_t*)p.dguqT; a.lda = p.rcap;
+    a.B = (const uint16_t*)p.xqT; a.ldb = p.rcap;
     a.C = p.dw1; a.C2 = p.dw3; a.ldc = d; a.c_es = (long)h * d;
     a.M = 2 * h; a.N = d; a.split = h;
-    a.offsets = p.off32; a.E = E; a.R = R;
+    a.offsets = p.off128; a.E = E; a.R = R;
     a.tiles_m = cdiv(2L * h, 256); a.tiles_n = cdiv(d, 256);
     MxArgs x{};
     x.sA = p.dgusT; x.lds_a = sc; x.sA_bytes = (long)2 * h * sc;

@@ -13,7 +13,7 @@ namespace trg {
 // routing
 size_t route_ws_bytes(int T, int E, int k);
 hipError_t launch_route(const float* logits, int T, int E, int k, const int* forced, float* probs, int* idx,
-                        float* w, int* counts, int* offsets, int* pos, int* src, int* off32, int* err_flag,
+                        float* w, int* counts, int* offsets, int* pos, int* src, int* off128, int* err_flag,
                         void* ws, hipStream_t s);
 
 // dispatch / combine (bf16 = uint16_t storage, or float)
@@ -64,7 +64,7 @@ hipError_t launch_ggemm_bwd_f32(const float* dyp, const float* xp, const float* 
 
 // MXFP8
 hipError_t launch_mx_quantize(const void* in, bool bf16, long ld_in, int rows, int cols, const int* src, int gk,
-                              const int* seg_off, const int* seg_off32, int nseg, int seg_rows, int max_blocks32,
+                              const int* seg_off, const int* seg_off128, int nseg, int seg_rows, int max_blocks32,
                               uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, long ldc,
                               hipStream_t s);
 typedef moe_mx_fwd_args MxFwd;

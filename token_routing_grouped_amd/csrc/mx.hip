@@ -15,7 +15,7 @@
 //                   along the columns: the forward and dgrad K);
 //   column layout   q_col [cols, ldc], s_col [cols, ldc/32]        (blocks of
 //                   32 consecutive rows inside each segment, zero-padded at
-//                   the segment's end; segment e starts at column off32[e]:
+//                   the segment's end; segment e starts at column off128[e]:
 //                   the weight-gradient K).
 // Rows can be gathered on the fly (row r reads in[src[r] / k]), which fuses
 // the rowwise dispatch of the layer input into its quantisation.
@@ -63,16 +63,16 @@ TRG_DEV uint32_t or4(uint32_t v) {
 
 // Segment of the 32-row block starting at padded row base32: the block's first
 // source row, the segment's end row; false past the padded row space.
-TRG_DEV bool mx_block_rows(int base32, int rows, const int* seg_off, const int* seg_off32, int nseg, int seg_rows,
+TRG_DEV bool mx_block_rows(int base32, int rows, const int* seg_off, const int* seg_off128, int nseg, int seg_rows,
                            int& r0, int& seg_hi) {
   if (seg_off != nullptr) {
-    if (base32 >= seg_off32[nseg]) return false;
-    int lo = 0, hi = nseg;  // last e with seg_off32[e] <= base32
+    if (base32 >= seg_off128[nseg]) return false;
+    int lo = 0, hi = nseg;  // last e with seg_off128[e] <= base32
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (seg_off32[mid] <= base32) lo = mid; else hi = mid;
+      if (seg_off128[mid] <= base32) lo = mid; else hi = mid;
     }
-    r0 = seg_off[lo] + (base32 - seg_off32[lo]);
+    r0 = seg_off[lo] + (base32 - seg_off128[lo]);
     seg_hi = seg_off[lo + 1];
   } else {
     // fixed-size segments of seg_rows rows (rows a multiple of seg_rows, or a
@@ -98,7 +98,7 @@ template <class T>
 __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, long ld_in, int rows, int cols,
                                                       const int* __restrict__ src, int gk,
                                                       const int* __restrict__ seg_off,
-                                                      const int* __restrict__ seg_off32, int nseg, int seg_rows,
+                                                      const int* __restrict__ seg_off128, int nseg, int seg_rows,
                                                       uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                                       uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
                                                       long ldc) {
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
   for (int k = 0; k < 2; ++k) {
     const int i = (tid >> 2) + 64 * k;
     int r0, seg_hi;
-    const bool blk_ok = mx_block_rows(base + (i & ~31), rows, seg_off, seg_off32, nseg, seg_rows, r0, seg_hi);
+    const bool blk_ok = mx_block_rows(base + (i & ~31), rows, seg_off, seg_off128, nseg, seg_rows, r0, seg_hi);
     rr[k] = r0 + (i & 31);
     const int c = col0 + q4 * 32;
     rok[k] = blk_ok && rr[k] < seg_hi && c < cols;
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
     const int cc = (tid >> 2) + 64 * k, sb = q4;
     const int c = col0 + cc;
     int r0, seg_hi;
-    const bool blk_ok = mx_block_rows(base + sb * 32, rows, seg_off, seg_off32, nseg, seg_rows, r0, seg_hi);
+    const bool blk_ok = mx_block_rows(base + sb * 32, rows, seg_off, seg_off128, nseg, seg_rows, r0, seg_hi);
     const bool ok = blk_ok && c < cols;
     float x[32];
 #pragma unroll
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
 }
 
 hipError_t launch_mx_quantize(const void* in, bool bf16, long ld_in, int rows, int cols, const int* src, int gk,
-                              const int* seg_off, const int* seg_off32, int nseg, int seg_rows, int max_blocks32,
+                              const int* seg_off, const int* seg_off128, int nseg, int seg_rows, int max_blocks32,
                               uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, long ldc,
                               hipStream_t s) {
   if (rows == 0 || max_blocks32 == 0) return hipSuccess;
@@ -230,9 +230,9 @@ hipError_t launch_mx_quantize(const void* in, bool bf16, long ld_in, int rows, i
   const unsigned grid = (unsigned)nblk;
   if (bf16)
     mx_dual_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)in, ld_in, rows, cols, src, gk, seg_off,
-                                                  seg_off32, nseg, seg_rows, q_row, s_row, q_col, s_col, ldc);
+                                                  seg_off128, nseg, seg_rows, q_row, s_row, q_col, s_col, ldc);
   else
-    mx_dual_kernel<float><<<grid, 256, 0, s>>>((const float*)in, ld_in, rows, cols, src, gk, seg_off, seg_off32,
+    mx_dual_kernel<float><<<grid, 256, 0, s>>>((const float*)in, ld_in, rows, cols, src, gk, seg_off, seg_off128,
                                                nseg, seg_rows, q_row, s_row, q_col, s_col, ldc);
   return hipGetLastError();
 }

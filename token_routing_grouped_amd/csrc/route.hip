@@ -8,7 +8,7 @@
 //   route_count  one wave per chunk of 256 flattened (t, j) entries -> per-chunk
 //                per-expert counts
 //   route_scan   one workgroup: per-expert exclusive scan over chunks, counts,
-//                offsets, off32
+//                offsets, off128
 //   route_rank   one wave per chunk: rank of each entry among equal experts in
 //                (token, slot) order via LDS match masks + popcount
 #include "common.h"
@@ -147,12 +147,12 @@ __global__ __launch_bounds__(256) void route_count_kernel(const int* __restrict_
 // range of chunks of expert e.  Threads are ordered expert-major, so one
 // exclusive block scan of the per-thread chunk sums gives every thread the
 // absolute row of its first entry: the counts of all lower experts plus the
-// same expert's earlier chunks.  A second scan over the experts' 32-rounded
-// counts gives off32.  Finally each thread rewrites its chunks' counts as
+// same expert's earlier chunks.  A second scan over the experts' counts
+// rounded up to 128 rows gives off128.  Finally each thread rewrites its chunks' counts as
 // absolute starting rows.
 __global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ chunk_cnt, int nchunks, int E,
                                                           int* __restrict__ counts, int* __restrict__ offsets,
-                                                          int* __restrict__ off32) {
+                                                          int* __restrict__ off128) {
   __shared__ int tmp[1024];
   __shared__ int off_s[1025];
   const int tid = threadIdx.x;
@@ -181,16 +181,16 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ chun
   if (tid == 0) off_s[E] = total;
   __syncthreads();
   const int cnt_e = mine ? off_s[e + 1] - off_s[e] : 0;
-  int total32;
-  const int o32 = block_excl_scan_1024((mine && j == 0) ? (cnt_e + 31) & ~31 : 0, tmp, &total32);
+  int total128;
+  const int o128 = block_excl_scan_1024((mine && j == 0) ? (cnt_e + 127) & ~127 : 0, tmp, &total128);
   if (mine && j == 0) {
     counts[e] = cnt_e;
     offsets[e] = off_s[e];
-    if (off32) off32[e] = o32;
+    if (off128) off128[e] = o128;
   }
   if (tid == 0) {
     offsets[E] = total;
-    if (off32) off32[E] = total32;
+    if (off128) off128[E] = total128;
   }
   if (mine) {
     int run = base;
@@ -259,13 +259,13 @@ size_t route_ws_bytes(int T, int E, int k) {
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, const int* forced, float* probs, int* idx,
-                        float* w, int* counts, int* offsets, int* pos, int* src, int* off32, int* err_flag,
+                        float* w, int* counts, int* offsets, int* pos, int* src, int* off128, int* err_flag,
                         void* ws, hipStream_t s) {
   long R = (long)T * k;
   int nchunks = (int)((R + kChunk - 1) / kChunk);
   int* chunk_cnt = (int*)ws;
   if (R == 0) {  // no tokens: counts and offsets are all zero
-    route_scan_kernel<<<1, 1024, 0, s>>>(chunk_cnt, 0, E, counts, offsets, off32);
+    route_scan_kernel<<<1, 1024, 0, s>>>(chunk_cnt, 0, E, counts, offsets, off128);
     return hipGetLastError();
   }
   dim3 g1((T + 3) / 4);
@@ -280,7 +280,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, const int* for
   else
     route_topk_kernel<16><<<g1, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
   route_count_kernel<<<(nchunks + 3) / 4, 256, 4 * E * sizeof(int), s>>>(idx, (int)R, E, nchunks, chunk_cnt);
-  route_scan_kernel<<<1, 1024, 0, s>>>(chunk_cnt, nchunks, E, counts, offsets, off32);
+  route_scan_kernel<<<1, 1024, 0, s>>>(chunk_cnt, nchunks, E, counts, offsets, off128);
   route_rank_kernel<<<nchunks, 64, E * (sizeof(unsigned long long) + sizeof(int)), s>>>(idx, (int)R, E, chunk_cnt,
                                                                                         pos, src);
   return hipGetLastError();

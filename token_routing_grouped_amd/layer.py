@@ -61,7 +61,7 @@ class MoELayerGPU:
         self.topk_w = e(T, k, dt=f32)
         self.counts = e(E, dt=i32)
         self.offsets = e(E + 1, dt=i32)
-        self.off32 = e(E + 1, dt=i32)
+        self.off128 = e(E + 1, dt=i32)
         self.pos = e(T, k, dt=i32)
         self.src = e(R, dt=i32)
         self.err_flag = torch.zeros(1, dtype=i32, device=dev)
@@ -98,7 +98,7 @@ class MoELayerGPU:
     def _alloc_mx(self, dev):
         T, d, E, k, h, R = self.T, self.d, self.E, self.k, self.h, self.R
         u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device=dev)
-        self.r32cap = rc = (R + 31 * E + 127) // 128 * 128  # columnwise row stride
+        self.rcap = rc = (R + 127 * E + 127) // 128 * 128  # columnwise row stride
         # routed x: rowwise (up) and columnwise per expert (wgrad up)
         self.xq, self.xs, self.xqT, self.xsT = u8(R, d), u8(R, d // 32), u8(d, rc), u8(d, rc // 32)
         # weights: rowwise (forward) and blocked along the other dim (dgrad)
@@ -124,17 +124,17 @@ class MoELayerGPU:
     def forward(self, x, wr, w1, w3, w2, forced_idx=None):
         _abi.moe_router_logits(x, wr, self.logits)
         _abi.moe_route(self.logits, self.k, self.probs, self.topk_idx, self.topk_w, self.counts, self.offsets,
-                       self.pos, self.src, self.ws_route, off32=self.off32, forced_idx=forced_idx,
+                       self.pos, self.src, self.ws_route, off128=self.off128, forced_idx=forced_idx,
                        err_flag=self.err_flag)
         if self.aux_alpha > 0.0:
             self.balance()
         if self.mx:
             # routed rows of x straight into their experts' MX buffers
             _abi.mx_quantize(x, self.R, self.xq, self.xs, self.xqT, self.xsT, gather_src=self.src, gather_k=self.k,
-                             seg_off=self.offsets, seg_off32=self.off32)
+                             seg_off=self.offsets, seg_off128=self.off128)
             self.quantize_weights(w1, w3, w2)
-            _abi.moe_grouped_gemm_fwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, r32cap=self.r32cap,
-                                         offsets=self.offsets, off32=self.off32, xq=self.xq, xs=self.xs, w1q=self.w1q,
+            _abi.moe_grouped_gemm_fwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, rcap=self.rcap,
+                                         offsets=self.offsets, off128=self.off128, xq=self.xq, xs=self.xs, w1q=self.w1q,
                                          w1s=self.w1s, w3q=self.w3q, w3s=self.w3s, w2q=self.w2q, w2s=self.w2s,
                                          g=None if self.lean else self.g, u=None if self.lean else self.u,
                                          hbuf=self.hb, hq=self.hq, hs=self.hs, hqT=self.hqT,
@@ -150,8 +150,8 @@ class MoELayerGPU:
         """G and U of the current routing, bit-identical to what the forward
         would have stored (memory-lean backward)."""
         if self.mx:
-            _abi.moe_grouped_gemm_recompute_gu_mx(E=self.E, R=self.R, d=self.d, h=self.h, r32cap=self.r32cap,
-                                                  offsets=self.offsets, off32=self.off32, xq=self.xq, xs=self.xs,
+            _abi.moe_grouped_gemm_recompute_gu_mx(E=self.E, R=self.R, d=self.d, h=self.h, rcap=self.rcap,
+                                                  offsets=self.offsets, off128=self.off128, xq=self.xq, xs=self.xs,
                                                   w1q=self.w1q, w1s=self.w1s, w3q=self.w3q, w3s=self.w3s, g=self.g,
                                                   u=self.u, ws=self.ws_gemm, ws_bytes=self.ws_gemm.numel())
         else:
@@ -162,8 +162,8 @@ class MoELayerGPU:
         if self.lean:
             self.recompute_gu(w1, w3)
         if self.mx:
-            _abi.moe_grouped_gemm_bwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, r32cap=self.r32cap,
-                                         offsets=self.offsets, off32=self.off32, dyp=self.dyp, dyq=self.dyq,
+            _abi.moe_grouped_gemm_bwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, rcap=self.rcap,
+                                         offsets=self.offsets, off128=self.off128, dyp=self.dyp, dyq=self.dyq,
                                          dys=self.dys, dyqT=self.dyqT, dysT=self.dysT, g=self.g, u=self.u,
                                          hqT=self.hqT, hsT=self.hsT, xqT=self.xqT, xsT=self.xsT, w1tq=self.w1tq,
                                          w1ts=self.w1ts, w3tq=self.w3tq, w3ts=self.w3ts, w2tq=self.w2tq,
