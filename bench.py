@@ -145,9 +145,6 @@ def copy_probe(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": reps}), flush=True)
 
 
-# Expert weight banks above this many fp32 bytes are drawn on the device.
-HOST_WEIGHT_BYTES = 8 << 30
-
 
 def main():
     ap = argparse.ArgumentParser()
@@ -188,30 +185,10 @@ def main():
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     log(f"bench: {cfg.slug} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} h={cfg.h} {cfg.dtype} mode={mode}")
-    wbytes = 3 * cfg.E * cfg.h * cfg.d * 4
-    if wbytes <= HOST_WEIGHT_BYTES:
-        inp = inputs.layer_inputs(cfg)
-        t = {n: torch.from_numpy(v).to(dev).to(dt) for n, v in inp.items()}
-        weights_on = "host"
-    else:
-        # weight banks too large to draw on the host in reasonable time (the
-        # trillion shape's are 58 GB in fp32): x, wr and dy as usual, the expert
-        # weights from a seeded device generator, same distribution
-        inp = inputs.layer_inputs(cfg, experts=[0])
-        t = {n: torch.from_numpy(v).to(dev).to(dt) for n, v in inp.items() if n in ("x", "wr", "dy")}
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(1000 + cfg.seed)
-        for n, shape in (("w1", (cfg.E, cfg.h, cfg.d)), ("w3", (cfg.E, cfg.h, cfg.d)), ("w2", (cfg.E, cfg.d, cfg.h))):
-            w = torch.empty(shape, device=dev, dtype=dt)
-            for e in range(cfg.E):  # one expert at a time: no fp32 copy of a whole bank
-                w[e] = (torch.randn(shape[1:], device=dev, generator=gen) * cfg.w_std).to(dt)
-            t[n] = w
-            log(f"bench: {n} generated on the device")
-        weights_on = "device"
+    t, weights_on = inputs.device_inputs(cfg, dev, log=lambda m: log(f"bench: {m}"))
     forced = None
     if mode != "router":
         forced = torch.from_numpy(inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)).to(dev)
-    del inp
     layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, dev, mx=cfg.mx, aux_alpha=a.aux_alpha, lean=a.lean,
                         overlap=a.overlap)
     args = (t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])

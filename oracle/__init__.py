@@ -28,6 +28,8 @@ are stated at each function.
 Modules:
   moe_ref  -- routing, dispatch, SwiGLU experts, combine, and the backward.
   mx_ref   -- MXFP8 (OCP E4M3FN elements, E8M0 block scales) quantisation.
+  sampled_ref -- single tokens' and single experts' outputs of the full-size
+              layer (the same definitions, for sampled parity at full size).
 
 Pins: every function here is checked against something other than itself in
 ``tests/test_oracle_*.py`` (closed forms, brute force, finite differences,

@@ -59,6 +59,40 @@ def layer_inputs(cfg, T: int | None = None, experts=None) -> dict:
     return out
 
 
+# Expert weight banks above this many fp32 bytes are drawn on the device.
+HOST_WEIGHT_BYTES = 8 << 30
+
+
+def device_inputs(cfg, dev, log=None) -> tuple:
+    """The step's inputs as device tensors of the config's dtype, as timed.
+
+    Weight banks up to HOST_WEIGHT_BYTES (fp32) come from ``layer_inputs``;
+    larger ones (the trillion shape's are 58 GB in fp32) are drawn from a
+    seeded device generator with the same distribution, one expert at a time
+    (x, wr and dy still come from the host streams).  Returns (tensors,
+    where the weights were drawn: "host" or "device").
+    """
+    import torch
+
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    wbytes = 3 * cfg.E * cfg.h * cfg.d * 4
+    if wbytes <= HOST_WEIGHT_BYTES:
+        inp = layer_inputs(cfg)
+        return {n: torch.from_numpy(v).to(dev).to(dt) for n, v in inp.items()}, "host"
+    inp = layer_inputs(cfg, experts=[0])
+    t = {n: torch.from_numpy(v).to(dev).to(dt) for n, v in inp.items() if n in ("x", "wr", "dy")}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + cfg.seed)
+    for n, shape in (("w1", (cfg.E, cfg.h, cfg.d)), ("w3", (cfg.E, cfg.h, cfg.d)), ("w2", (cfg.E, cfg.d, cfg.h))):
+        w = torch.empty(shape, device=dev, dtype=dt)
+        for e in range(cfg.E):  # one expert at a time: no fp32 copy of a whole bank
+            w[e] = (torch.randn(shape[1:], device=dev, generator=gen) * cfg.w_std).to(dt)
+        t[n] = w
+        if log is not None:
+            log(f"{n} generated on the device")
+    return t, "device"
+
+
 def expert_weights(cfg, e: int) -> tuple:
     s = cfg.seed
     return (_store(normal(s, "w1", (cfg.h, cfg.d), cfg.w_std, e), cfg.dtype),
