@@ -59,8 +59,14 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
   if constexpr (MODE == RAGGED_M) total = g.tile_off[g.E] * g.tiles_n;
   else total = g.E * g.tiles_m * g.tiles_n;
   const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
-  const int per = (total + 7) >> 3;
-  const int t_begin = xcd * per, t_end = min(total, t_begin + per);
+  int t_begin, t_end;
+  if constexpr (MODE == RAGGED_M) {  // every tile has the same K
+    const int per = (total + 7) >> 3;
+    t_begin = xcd * per;
+    t_end = min(total, t_begin + per);
+  } else {
+    wgrad_range(g.work, g.E, g.tiles_m * g.tiles_n, total, xcd, t_begin, t_end);
+  }
 
   // Per-tile geometry and operand resources.
   struct Tile {
@@ -254,6 +260,19 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict
   }
 }
 
+// Per-expert work prefix of the weight-gradient tiles (see wgrad_range) from
+// the experts' K segments koff [E+1] and the K step bk.
+__global__ __launch_bounds__(1024) void wgrad_work_kernel(const int* __restrict__ koff, int E, int bk,
+                                                          int* __restrict__ work) {
+  __shared__ int tmp[1024];
+  const int e = threadIdx.x;
+  const int w = e < E ? (koff[e + 1] - koff[e] + bk - 1) / bk + kTileFixedSteps : 0;
+  int total;
+  const int ex = block_excl_scan_1024(w, tmp, &total);
+  if (e < E) work[e] = ex;
+  if (e == 0) work[E] = total;
+}
+
 // 8 waves (two per SIMD) per 256-wide tile: while one wave of a SIMD waits
 // on LDS the other issues MFMAs.
 template <int BM, int BN, bool AKC, bool BKC, int MODE, int BSEL, int CSEL, int EPI>
@@ -266,9 +285,11 @@ static void run(const char* name, const Args& a, int max_tiles, hipStream_t s) {
 
 }  // namespace gg
 
+// [0, 2(E+1)): row-tile prefixes (tile_prefix_kernel); [2(E+1), 3(E+1)):
+// weight-gradient work prefix (wgrad_work_kernel).
 size_t ggemm_ws_bytes(int E, int R, int d, int h) {
   (void)R; (void)d; (void)h;
-  return (size_t)(2 * (E + 1)) * sizeof(int);
+  return (size_t)(3 * (E + 1)) * sizeof(int);
 }
 
 using namespace gg;
@@ -377,13 +398,15 @@ hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, cons
     else
       dgrad_bm<256>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off + (E + 1), parts, s);
   }
+  int* work = (int*)ws + 2 * (E + 1);
+  if (parts & (MOE_BWD_WGRAD_DOWN | MOE_BWD_WGRAD_UP)) wgrad_work_kernel<<<1, 1024, 0, s>>>(offsets, E, BK, work);
   if (parts & MOE_BWD_WGRAD_DOWN) {  // wgrad down: dW2[e] = dYp_e^T H_e  (M = d, N = h, K = the expert's rows)
     Args a{};
     a.A = (const uint16_t*)dyp; a.lda = d;
     a.B = (const uint16_t*)hb; a.ldb = h;
     a.C = dw2; a.ldc = h; a.c_es = (long)d * h;
     a.M = d; a.N = h;
-    a.offsets = offsets; a.E = E; a.R = R;
+    a.offsets = offsets; a.work = work; a.E = E; a.R = R;
     a.tiles_m = cdiv(d, 256); a.tiles_n = cdiv(h, 256);
     run<256, 256, false, false, RAGGED_K, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_wgrad_down", a,
                                                                           E * a.tiles_m * a.tiles_n, s);
@@ -394,7 +417,7 @@ hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, cons
     a.B = (const uint16_t*)xp; a.ldb = d;
     a.C = dw1; a.C2 = dw3; a.ldc = d; a.c_es = (long)h * d;
     a.M = 2 * h; a.N = d; a.split = h;
-    a.offsets = offsets; a.E = E; a.R = R;
+    a.offsets = offsets; a.work = work; a.E = E; a.R = R;
     a.tiles_m = cdiv(2L * h, 256); a.tiles_n = cdiv(d, 256);
     run<256, 256, false, false, RAGGED_K, BSEL_NONE, CSEL_MSPLIT, EPI_BF16>("ggemm_wgrad_up", a,
                                                                             E * a.tiles_m * a.tiles_n, s);

@@ -48,6 +48,7 @@ struct Args {
   int split;    // GLU: h;  KSPLIT: first K half;  MSPLIT: first M half
   const int* offsets;
   const int* tile_off;  // RAGGED_M: per-expert prefix of BM row tiles
+  const int* work;      // RAGGED_K: per-expert prefix of per-tile work (see wgrad_range)
   int E, R;
   int tiles_m, tiles_n;
 };
@@ -366,6 +367,55 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
     }
   });
 }
+
+// Weight-gradient tiles differ in work: a tile's K loop runs over its
+// expert's rows.  work[e] = sum over experts e' < e of one tile's work,
+// ceil(rows_e' / BK) K steps plus kTileFixedSteps for the tile's prologue and
+// epilogue; every expert has per_e tiles, expert-major.  The tile list is cut
+// into the eight XCD ranges by count (as the ragged-M GEMMs are) unless that
+// leaves one XCD more than 1.25x the mean work; then it is cut by work, so a
+// skewed routing (one expert holding a sixth of the rows) does not leave
+// seven XCDs idle while one works through the heavy experts.  By work, XCD x
+// takes the tiles whose cumulative work starts in [x W / 8, (x + 1) W / 8).
+// (The count cut stays the default because with about one tile per CU a cut
+// one tile off the count costs a whole extra tile on some CU.)
+constexpr int kTileFixedSteps = 2;
+
+TRG_DEV void wgrad_range(const int* work, int E, int per_e, int total, int xcd, int& t_begin, int& t_end) {
+  const long W = (long)work[E] * per_e;
+  const int per = (total + 7) >> 3;
+  auto cum = [&](int t) -> long {  // work of tiles [0, t)
+    if (t >= total) return W;
+    const int e = t / per_e;
+    return (long)work[e] * per_e + (long)(t - e * per_e) * (work[e + 1] - work[e]);
+  };
+  long wmax = 0;
+  for (int x = 0; x < 8; ++x) {
+    const long wx = cum(min(total, (x + 1) * per)) - cum(min(total, x * per));
+    wmax = wx > wmax ? wx : wmax;
+  }
+  if (wmax * 8 * 4 <= W * 5) {
+    t_begin = min(total, xcd * per);
+    t_end = min(total, t_begin + per);
+    return;
+  }
+  auto tile_at = [&](long target) -> int {  // first tile whose work starts at or after target
+    if (target >= W) return total;
+    int lo = 0, hi = E;  // last expert whose first tile starts at or before target
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((long)work[mid] * per_e <= target) lo = mid; else hi = mid;
+    }
+    const long we = work[lo + 1] - work[lo];  // >= kTileFixedSteps > 0
+    const long j = (target - (long)work[lo] * per_e + we - 1) / we;
+    return lo * per_e + (int)(j < per_e ? j : per_e);
+  };
+  t_begin = tile_at(xcd * W / 8);
+  t_end = xcd == 7 ? total : tile_at((xcd + 1) * W / 8);
+}
+
+__global__ __launch_bounds__(1024) void wgrad_work_kernel(const int* __restrict__ koff, int E, int bk,
+                                                          int* __restrict__ work);
 
 // Per-expert row-tile prefix for BM = 128 and 256 from the expert offsets:
 // tile_off[b*(E+1) + e] for b = 0 (128 rows) and 1 (256 rows).

@@ -87,8 +87,14 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
   if constexpr (MODE == RAGGED_M) total = g.tile_off[g.E] * g.tiles_n;
   else total = g.E * g.tiles_m * g.tiles_n;
   const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
-  const int per = (total + 7) >> 3;
-  const int t_begin = xcd * per, t_end = min(total, t_begin + per);
+  int t_begin, t_end;
+  if constexpr (MODE == RAGGED_M) {  // every tile has the same K
+    const int per = (total + 7) >> 3;
+    t_begin = xcd * per;
+    t_end = min(total, t_begin + per);
+  } else {
+    wgrad_range(g.work, g.E, g.tiles_m * g.tiles_n, total, xcd, t_begin, t_end);
+  }
 
   const __amdgpu_buffer_rsrc_t rsSA = make_rsrc(x.sA, x.sA_bytes);
   const __amdgpu_buffer_rsrc_t rsSB = make_rsrc(x.sB, x.sB_bytes);
@@ -468,13 +474,15 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   const long sc = p.rcap / 32;
+  int* work = (int*)p.ws + 2 * (E + 1);
+  wgrad_work_kernel<<<1, 1024, 0, s>>>(p.off128, E, 128, work);
   {  // wgrad down: dW2[e] = dYp_e^T H_e over the expert's padded segment
     Args a{};
     a.A = (const uint16_t*)p.dyqT; a.lda = p.rcap;
     a.B = (const uint16_t*)p.hqT; a.ldb = p.rcap;
     a.C = p.dw2; a.ldc = h; a.c_es = (long)d * h;
     a.M = d; a.N = h;
-    a.offsets = p.off128; a.E = E; a.R = R;
+    a.offsets = p.off128; a.work = work; a.E = E; a.R = R;
     a.tiles_m = cdiv(d, 256); a.tiles_n = cdiv(h, 256);
     MxArgs x{};
     x.sA = p.dysT; x.lds_a = sc; x.sA_bytes = (long)d * sc;
@@ -488,7 +496,7 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
     a.B = (const uint16_t*)p.xqT; a.ldb = p.rcap;
     a.C = p.dw1; a.C2 = p.dw3; a.ldc = d; a.c_es = (long)h * d;
     a.M = 2 * h; a.N = d; a.split = h;
-    a.offsets = p.off128; a.E = E; a.R = R;
+    a.offsets = p.off128; a.work = work; a.E = E; a.R = R;
     a.tiles_m = cdiv(2L * h, 256); a.tiles_n = cdiv(d, 256);
     MxArgs x{};
     x.sA = p.dgusT; x.lds_a = sc; x.sA_bytes = (long)2 * h * sc;
