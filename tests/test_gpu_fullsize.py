@@ -1,8 +1,9 @@
 """Parity at the workloads' full sizes, in the configuration bench.py times.
 
 Each case runs one step of the layer exactly as bench.py does (the same
-inputs from ``inputs.device_inputs``, the same default layer flags, so the
-same kernels and tile shapes) and checks against the float64 oracle:
+inputs from ``inputs.device_inputs``, the same layer flags, including the
+workload's two-stream backward where its config sets it, so the same kernels
+and tile shapes) and checks against the float64 oracle:
 
   * routing on the GPU's own float32 logits: top-k indices, counts, offsets,
     positions, src and off128 bit-exact over all tokens (the oracle routes
@@ -66,7 +67,7 @@ def test_full_size_sampled_parity(case):
     forced_np = None if mode == "router" else inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)
     forced = None if forced_np is None else torch.from_numpy(forced_np).to(DEV)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, DEV, mx=cfg.mx)
+    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, DEV, mx=cfg.mx, overlap=cfg.overlap)
     layer.step(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"], forced_idx=forced)
     torch.cuda.synchronize()
     assert int(layer.err_flag.item()) == 0
