@@ -194,6 +194,16 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int nk = num_k(cur);
+    // Ragged M: the wave's 32-row subtiles that lie wholly past the expert's
+    // last row hold no output, so their MFMAs are skipped (an expert's last
+    // row tile is often nearly empty: 8 rows of 256).  On a SIMD the two
+    // waves' MFMAs share one matrix core, so the tail tile's time shrinks with
+    // them.
+    int nv = TM;
+    if constexpr (MODE == RAGGED_M) {
+      const int rows = m_end - (m0 + wm * WTM);
+      nv = rows <= 0 ? 0 : (rows >= WTM ? TM : (rows + 31) / 32);
+    }
     for (int it = 0; it < nk; ++it) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // stage it&1 is complete; stage (it+1)&1 is free
@@ -220,9 +230,10 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
+          if (i < nv)  // uniform: only an expert's tail tile skips
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       });
     }
