@@ -30,6 +30,16 @@ def assert_close(name, got, ref, rel=REL_L2, max_frac=MAX_ABS_FRAC):
     return r, m
 
 
+def tail_routing(T, counts):
+    """Forced top-2 routing with the given per-expert row counts (sum 2T): the
+    first T entries of the expert list fill slot 0, the rest slot 1, so a
+    token's two experts differ as long as no count exceeds T.  Used to give
+    experts tails of chosen lengths past their whole 256-row tiles."""
+    lst = np.repeat(np.arange(len(counts)), counts)
+    assert lst.size == 2 * T and max(counts) <= T
+    return np.stack([lst[:T], lst[T:]], axis=1).astype(np.int32)
+
+
 def to_np(t):
     return t.detach().float().cpu().numpy() if t.dtype.is_floating_point else t.detach().cpu().numpy()
 

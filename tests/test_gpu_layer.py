@@ -17,7 +17,7 @@ import torch
 from oracle import moe_ref as ref
 from token_routing_grouped_amd import configs, inputs
 
-from helpers import assert_close, say, to_np
+from helpers import assert_close, say, tail_routing, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,9 @@ CASES = [
     ("k_eq_E", "small", dict(T=130, E=4, k=4, d=256, h=128), "router"),
     ("T1", "small", dict(T=1, d=256, h=128), "router"),
     ("E384_k8_sparse", "trillion", dict(T=24, d=256, h=128), "uniform"),
+    # experts of >= 2048 rows on average: light tails (50 and 2 rows past whole
+    # 256-row tiles) are scheduled apart from the full-cost tiles
+    ("tail_split_E4", "small", dict(T=4096, E=4, k=2, d=256, h=128), "tails"),
 ]
 
 
@@ -71,6 +74,8 @@ def test_layer_parity(case):
         differ = (to_np(layer.topk_idx) != forced).any(axis=1)
         ties = _near_tie_tokens(L32, cfg.k, 1e-4 * max(1.0, float(np.abs(L32).max())))
         assert not (differ & ~ties).any(), f"routing differs on {int((differ & ~ties).sum())} non-tied tokens"
+    elif mode == "tails":
+        forced = tail_routing(cfg.T, [2098, 1998, 2050, 2046])
     else:
         forced = inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)
 

@@ -18,7 +18,7 @@ from oracle import moe_ref as ref
 from oracle import mx_ref as mx
 from token_routing_grouped_amd import configs, inputs
 
-from helpers import rel_l2, say, to_np
+from helpers import rel_l2, say, tail_routing, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -160,6 +160,7 @@ LAYER_CASES = [
     ("k_eq_E", "small", dict(T=130, E=4, k=4, d=256, h=128), "router"),
     ("one_expert", "small", dict(T=200, E=1, k=1, d=128, h=256), "router"),
     ("T1", "small", dict(T=1, d=128, h=128), "router"),
+    ("tail_split_E4", "small", dict(T=4096, E=4, k=2, d=256, h=128), "tails"),
 ]
 
 
@@ -175,6 +176,8 @@ def test_mx_layer_parity(case):
     x, wr, w1, w3, w2, dy = (inp[n] for n in ("x", "wr", "w1", "w3", "w2", "dy"))
     if mode == "router":
         forced = ref.topk_experts(ref.router_logits(x, wr).astype(np.float32), cfg.k).astype(np.int32)
+    elif mode == "tails":
+        forced = tail_routing(cfg.T, [2098, 1998, 2050, 2046])
     else:
         forced = inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)
     layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, mx=True)

@@ -55,17 +55,17 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  int total;
-  if constexpr (MODE == RAGGED_M) total = g.tile_off[g.E] * g.tiles_n;
-  else total = g.E * g.tiles_m * g.tiles_n;
   const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+  // t runs over this XCD's walk: ragged M, positions of its RmSched slices;
+  // ragged K, global tile indices of its work-balanced range
   int t_begin, t_end;
-  if constexpr (MODE == RAGGED_M) {  // every tile has the same K
-    const int per = (total + 7) >> 3;
-    t_begin = xcd * per;
-    t_end = min(total, t_begin + per);
+  RmSched rms{};
+  if constexpr (MODE == RAGGED_M) {
+    rms = rm_sched<BM>(g.tile_off, g.E, g.tiles_n, xcd);
+    t_begin = 0;
+    t_end = rms.nf + rms.nl;
   } else {
-    wgrad_range(g.work, g.E, g.tiles_m * g.tiles_n, total, xcd, t_begin, t_end);
+    wgrad_range(g.work, g.E, g.tiles_m * g.tiles_n, g.E * g.tiles_m * g.tiles_n, xcd, t_begin, t_end);
   }
 
   // Per-tile geometry and operand resources.
@@ -77,15 +77,8 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
   auto decode = [&](int t) {
     Tile c;
     if constexpr (MODE == RAGGED_M) {
-      const int mtg = t / g.tiles_n, nt = t - mtg * g.tiles_n;
-      int lo = 0, hi = g.E;  // last expert with tile_off[e] <= mtg
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (g.tile_off[mid] <= mtg) lo = mid; else hi = mid;
-      }
-      c.e = lo;
-      c.m0 = g.offsets[lo] + (mtg - g.tile_off[lo]) * BM;
-      c.m_end = g.offsets[lo + 1];
+      int nt;
+      rm_tile<BM>(g.tile_off, g.offsets, g.E, g.tiles_n, rms, t, c.e, c.m0, c.m_end, nt);
       c.n0 = nt * BN;
       c.k0 = 0;
       c.k_end = g.K;
@@ -257,15 +250,17 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
 
 // Per-expert row-tile prefix for BM = 128 and 256 from the expert offsets.
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict__ offsets, int E,
-                                                           int* __restrict__ tile_off) {
+                                                           int* __restrict__ tile_off, int split_tails) {
   __shared__ int tmp[1024];
   const int e = threadIdx.x;
   const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int tail = c & 255;
+  const bool light = split_tails && tail > 0 && tail <= 128;
+  const int per_b[3] = {(c + 127) / 128, (c + 255) / 256 - (light ? 1 : 0), light ? 1 : 0};
 #pragma unroll 1
-  for (int b = 0; b < 2; ++b) {
-    const int bm = 128 << b;
+  for (int b = 0; b < 3; ++b) {
     int total;
-    const int ex = block_excl_scan_1024((c + bm - 1) / bm, tmp, &total);
+    const int ex = block_excl_scan_1024(per_b[b], tmp, &total);
     if (e < E) tile_off[b * (E + 1) + e] = ex;
     if (e == 0) tile_off[b * (E + 1) + E] = total;
   }
@@ -296,11 +291,11 @@ static void run(const char* name, const Args& a, int max_tiles, hipStream_t s) {
 
 }  // namespace gg
 
-// [0, 2(E+1)): row-tile prefixes (tile_prefix_kernel); [2(E+1), 3(E+1)):
+// [0, 3(E+1)): row-tile prefixes (tile_prefix_kernel); [3(E+1), 4(E+1)):
 // weight-gradient work prefix (wgrad_work_kernel).
 size_t ggemm_ws_bytes(int E, int R, int d, int h) {
   (void)R; (void)d; (void)h;
-  return (size_t)(3 * (E + 1)) * sizeof(int);
+  return (size_t)(4 * (E + 1)) * sizeof(int);
 }
 
 using namespace gg;
@@ -345,7 +340,7 @@ hipError_t launch_ggemm_fwd(const void* xp, const void* w1, const void* w3, cons
     return launch_ggemm_fwd_f32((const float*)xp, (const float*)w1, (const float*)w3, (const float*)w2, offsets, E,
                                 R, d, h, (float*)g, (float*)u, (float*)hb, (float*)yp, s);
   int* tile_off = (int*)ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off);
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off, split_tails(E, R));
   if (small_rows(E, R))
     fwd_bm<128>(xp, w1, w3, w2, offsets, E, R, d, h, g, u, hb, yp, tile_off, s);
   else
@@ -356,7 +351,7 @@ hipError_t launch_ggemm_fwd(const void* xp, const void* w1, const void* w3, cons
 hipError_t launch_ggemm_recompute_gu(const void* xp, const void* w1, const void* w3, const int* offsets, int E, int R,
                                      int d, int h, void* g, void* u, void* ws, hipStream_t s) {
   int* tile_off = (int*)ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off);
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off, split_tails(E, R));
   if (small_rows(E, R))
     up_bm<128>("ggemm_recompute_gu", xp, w1, w3, offsets, E, R, d, h, g, u, nullptr, tile_off, s);
   else
@@ -403,13 +398,13 @@ hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, cons
                                 R, d, h, (float*)dgu, (float*)dxp, (float*)dw1, (float*)dw3, (float*)dw2, s);
   if (parts & (MOE_BWD_DGRAD_DOWN | MOE_BWD_DGRAD_UP)) {
     int* tile_off = (int*)ws;
-    tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off);
+    tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off, split_tails(E, R));
     if (small_rows(E, R))
       dgrad_bm<128>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off, parts, s);
     else
       dgrad_bm<256>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off + (E + 1), parts, s);
   }
-  int* work = (int*)ws + 2 * (E + 1);
+  int* work = (int*)ws + 3 * (E + 1);
   if (parts & (MOE_BWD_WGRAD_DOWN | MOE_BWD_WGRAD_UP)) wgrad_work_kernel<<<1, 1024, 0, s>>>(offsets, E, BK, work);
   if (parts & MOE_BWD_WGRAD_DOWN) {  // wgrad down: dW2[e] = dYp_e^T H_e  (M = d, N = h, K = the expert's rows)
     Args a{};

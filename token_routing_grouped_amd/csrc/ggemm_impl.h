@@ -368,6 +368,57 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
   });
 }
 
+// Ragged-M schedule.  Every row tile has the same K, but an expert's last
+// row tile is often nearly empty, and its MFMAs are skipped
+// (subtiles past m_end): with 256-row tiles such a tail costs about half a
+// tile.  tile_off holds per-expert prefixes from tile_prefix_kernel:
+//   BM = 128: [E+1] prefix of the experts' 128-row tiles;
+//   BM = 256: [E+1] prefix of full-cost tiles (more than 128 valid rows: the
+//             whole 256-row tiles and a tail of 129..255 rows), then [E+1]
+//             prefix of light tails (1..128 rows).
+// (Light tails are split out only where split_tails() says so; otherwise
+// every row tile is in the first list and the second is empty.)
+// Each XCD takes an eighth of the full-cost tiles (times the column tiles),
+// in expert order, followed by an eighth of the light tails: its CUs walk the
+// list round-robin, so the light tails land on the CUs that got one full
+// tile fewer (8 experts of ~4096 rows: 1024 full-cost tiles, 4 per CU, and 16
+// light tails, instead of 1040 tiles of which 16 CUs ran a fifth full one).
+struct RmSched {
+  int f0, nf, l0, nl;  // this XCD's full-cost list slice [f0, f0+nf) and light slice [l0, l0+nl)
+};
+
+template <int BM>
+TRG_DEV RmSched rm_sched(const int* toff, int E, int tiles_n, int xcd) {
+  RmSched r;
+  const int F = toff[E] * tiles_n;
+  const int L = BM == 256 ? toff[(E + 1) + E] * tiles_n : 0;
+  const int fper = (F + 7) >> 3, lper = (L + 7) >> 3;
+  r.f0 = min(F, xcd * fper);
+  r.nf = min(F, r.f0 + fper) - r.f0;
+  r.l0 = min(L, xcd * lper);
+  r.nl = min(L, r.l0 + lper) - r.l0;
+  return r;
+}
+
+// Position p of an XCD's walk -> expert, first row, row end and column tile.
+template <int BM>
+TRG_DEV void rm_tile(const int* toff, const int* offs, int E, int tiles_n, const RmSched& r, int p, int& e, int& m0,
+                     int& m_end, int& nt) {
+  const bool light = p >= r.nf;
+  const int* pre = light ? toff + (E + 1) : toff;
+  const int idx = light ? r.l0 + (p - r.nf) : r.f0 + p;
+  const int mtg = idx / tiles_n;
+  nt = idx - mtg * tiles_n;
+  int lo = 0, hi = E;  // last expert with pre[e] <= mtg
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= mtg) lo = mid; else hi = mid;
+  }
+  e = lo;
+  m_end = offs[lo + 1];
+  m0 = light ? offs[lo] + ((m_end - offs[lo]) & ~255) : offs[lo] + (mtg - pre[lo]) * BM;
+}
+
 // Weight-gradient tiles differ in work: a tile's K loop runs over its
 // expert's rows.  work[e] = sum over experts e' < e of one tile's work,
 // ceil(rows_e' / BK) K steps plus kTileFixedSteps for the tile's prologue and
@@ -417,10 +468,17 @@ TRG_DEV void wgrad_range(const int* work, int E, int per_e, int total, int xcd, 
 __global__ __launch_bounds__(1024) void wgrad_work_kernel(const int* __restrict__ koff, int E, int bk,
                                                           int* __restrict__ work);
 
-// Per-expert row-tile prefix for BM = 128 and 256 from the expert offsets:
-// tile_off[b*(E+1) + e] for b = 0 (128 rows) and 1 (256 rows).
+// Per-expert row-tile prefixes from the expert offsets (see RmSched):
+// tile_off[0, E] 128-row tiles, [E+1, 2E+1] full-cost 256-row tiles,
+// [2E+2, 3E+2] light 256-row tails.
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict__ offsets, int E,
-                                                           int* __restrict__ tile_off);
+                                                           int* __restrict__ tile_off, int split_tails);
+
+// Light tails get their own place in the walk only where experts are large
+// (R >= 2048 E): there an extra tile round is a large share of the kernel,
+// while with a few hundred rows per expert moving every tail away from its
+// expert's other tiles loses the weights' L2 reuse (wide shape: +3%).
+inline int split_tails(int E, int R) { return (long)R >= 2048L * E ? 1 : 0; }
 
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 

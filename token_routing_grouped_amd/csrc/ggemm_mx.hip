@@ -83,17 +83,17 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5;
 
-  int total;
-  if constexpr (MODE == RAGGED_M) total = g.tile_off[g.E] * g.tiles_n;
-  else total = g.E * g.tiles_m * g.tiles_n;
   const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+  // t runs over this XCD's walk: ragged M, positions of its RmSched slices;
+  // ragged K, global tile indices of its work-balanced range
   int t_begin, t_end;
-  if constexpr (MODE == RAGGED_M) {  // every tile has the same K
-    const int per = (total + 7) >> 3;
-    t_begin = xcd * per;
-    t_end = min(total, t_begin + per);
+  RmSched rms{};
+  if constexpr (MODE == RAGGED_M) {
+    rms = rm_sched<BM>(g.tile_off, g.E, g.tiles_n, xcd);
+    t_begin = 0;
+    t_end = rms.nf + rms.nl;
   } else {
-    wgrad_range(g.work, g.E, g.tiles_m * g.tiles_n, total, xcd, t_begin, t_end);
+    wgrad_range(g.work, g.E, g.tiles_m * g.tiles_n, g.E * g.tiles_m * g.tiles_n, xcd, t_begin, t_end);
   }
 
   const __amdgpu_buffer_rsrc_t rsSA = make_rsrc(x.sA, x.sA_bytes);
@@ -109,15 +109,8 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
   auto decode = [&](int t) {
     Tile c;
     if constexpr (MODE == RAGGED_M) {
-      const int mtg = t / g.tiles_n, nt = t - mtg * g.tiles_n;
-      int lo = 0, hi = g.E;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (g.tile_off[mid] <= mtg) lo = mid; else hi = mid;
-      }
-      c.e = lo;
-      c.m0 = g.offsets[lo] + (mtg - g.tile_off[lo]) * BM;
-      c.m_end = g.offsets[lo + 1];
+      int nt;
+      rm_tile<BM>(g.tile_off, g.offsets, g.E, g.tiles_n, rms, t, c.e, c.m0, c.m_end, nt);
       c.n0 = nt * BN;
       c.k0 = 0;
       c.klen = g.K;
@@ -257,6 +250,13 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int nk = num_k(cur);
+    // Ragged M: the wave's 32-row subtiles wholly past the expert's last row
+    // skip their MFMAs (see the bf16 kernel).
+    int nv = TM;
+    if constexpr (MODE == RAGGED_M) {
+      const int rows = m_end - (m0 + wm * WTM);
+      nv = rows <= 0 ? 0 : (rows >= WTM ? TM : (rows + 31) / 32);
+    }
     for (int it = 0; it < nk; ++it) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // stage it&1 and this step's scales are in; stage (it+1)&1 is free
@@ -301,12 +301,14 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
         const bool lane_ok = MODE == RAGGED_M || (half ? v1 : v0);  // this lane's scale block
         static_for<TM>([&](auto I) {
           constexpr int i = decltype(I)::value;
+          const bool row_ok = i < nv;  // uniform: only an expert's tail tile skips
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
             const int sA_ = lane_ok ? (int)sa[i] : 127 << (16 * kk);
             const int sB_ = lane_ok ? (int)sb[j] : 127 << (16 * kk);
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 2 * kk, sB_,
-                                                                         2 * kk, sA_);
+            if (row_ok)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 2 * kk,
+                                                                           sB_, 2 * kk, sA_);
             if constexpr (!last && i == TM - 1) {
               __builtin_amdgcn_sched_barrier(0);
               bfr[j] = frag_mx(sB, wn * WTN + j * 32, kk + 1, lane);
@@ -372,7 +374,7 @@ static void mx_up_bm(const char* name, const MxFwd& p, void* gq, void* u, void* 
 
 hipError_t launch_ggemm_recompute_gu_mx(const MxFwd& p, hipStream_t s) {
   int* tile_off = (int*)p.ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, tile_off);
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, tile_off, split_tails(p.E, p.R));
   if (small_rows(p.E, p.R)) mx_up_bm<128>("ggemm_mx_recompute_gu", p, p.g, p.u, nullptr, tile_off, s);
   else mx_up_bm<256>("ggemm_mx_recompute_gu", p, p.g, p.u, nullptr, tile_off + (p.E + 1), s);
   return hipGetLastError();
@@ -411,8 +413,8 @@ static hipError_t mx_fwd_bm(const MxFwd& p, const int* tile_off, hipStream_t s) 
 // byte loaded, so the per-step costs need the larger tile.  The weight
 // gradients (K-tail masking, more registers) use 128 x 256.
 hipError_t launch_ggemm_fwd_mx(const MxFwd& p, hipStream_t s) {
-  int* tile_off = (int*)p.ws;  // [0, E]: 128-row prefix, [E+1, 2E+1]: 256-row prefix
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, tile_off);
+  int* tile_off = (int*)p.ws;  // 128-row prefix, then the 256-row full-cost and light prefixes (RmSched)
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, tile_off, split_tails(p.E, p.R));
   if (small_rows(p.E, p.R)) return mx_fwd_bm<128>(p, tile_off, s);
   return mx_fwd_bm<256>(p, tile_off + (p.E + 1), s);
 }
@@ -461,7 +463,7 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, hipStream_t s
 hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
   int* tile_off = (int*)p.ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, E, tile_off);
+  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, E, tile_off, split_tails(E, p.R));
   {  // dYp -> rowwise (dgrad down) and columnwise per expert (wgrad down)
     ProfScope ps("mx_quantize_dy", s);
     const hipError_t err = launch_mx_quantize(p.dyp, true, d, R, d, nullptr, 1, p.offsets, p.off128, E, 0,
@@ -474,7 +476,7 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   const long sc = p.rcap / 32;
-  int* work = (int*)p.ws + 2 * (E + 1);
+  int* work = (int*)p.ws + 3 * (E + 1);
   wgrad_work_kernel<<<1, 1024, 0, s>>>(p.off128, E, 128, work);
   {  // wgrad down: dW2[e] = dYp_e^T H_e over the expert's padded segment
     Args a{};
