@@ -353,6 +353,16 @@ typedef struct {
 moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* args, void* stream);
 moe_status_t moe_grouped_gemm_bwd_mx(const moe_mx_bwd_args* args, void* stream);
 /*
+ * moe_grouped_gemm_bwd_mx_parts: moe_grouped_gemm_bwd_mx restricted to a
+ * subset (MOE_BWD_* mask) of its four GEMMs, for two streams as with
+ * moe_grouped_gemm_bwd_parts.  MOE_BWD_DGRAD_DOWN also makes dYp's MX copies
+ * (dyq/dys, dyqT/dysT) before its GEMM and dG|dU's (dguq/dgus, dguqT/dgusT)
+ * after it, so MOE_BWD_WGRAD_DOWN and MOE_BWD_WGRAD_UP need that part done
+ * and MOE_BWD_DGRAD_UP too.  Calls that may run concurrently need separate
+ * workspaces.  Same arguments and checks as moe_grouped_gemm_bwd_mx.
+ */
+moe_status_t moe_grouped_gemm_bwd_mx_parts(const moe_mx_bwd_args* args, unsigned parts, void* stream);
+/*
  * Memory-lean MXFP8: moe_grouped_gemm_fwd_mx accepts g = u = null (not
  * stored); moe_grouped_gemm_recompute_gu_mx then runs the MX up projection
  * alone from xq/xs and the weights' forward copies, writing g and u only, so

@@ -144,3 +144,8 @@ def test_host_validation_of_the_next_rows():
     assert lib.moe_grouped_gemm_bwd_parts(*args, 0, c, 1 << 20, None) == 1
     assert lib.moe_grouped_gemm_bwd_parts(*args, 16, c, 1 << 20, None) == 1
     assert b"parts" in lib.moe_last_error_string()
+    # MXFP8 backward parts: empty and out-of-range masks are refused before anything else
+    a = _abi.MxBwdArgs(E=2, R=8, d=128, h=128, rcap=512)
+    assert lib.moe_grouped_gemm_bwd_mx_parts(ctypes.byref(a), 0, None) == 1
+    assert lib.moe_grouped_gemm_bwd_mx_parts(ctypes.byref(a), 16, None) == 1
+    assert b"parts" in lib.moe_last_error_string()

@@ -1,6 +1,7 @@
 """Weight-gradient GEMMs on a second stream next to the dgrad chain
-(moe_grouped_gemm_bwd_parts): every GEMM computes exactly what it computes on
-one stream, so the whole step must be bit-identical to the serial one."""
+(moe_grouped_gemm_bwd_parts, and moe_grouped_gemm_bwd_mx_parts for MXFP8):
+every GEMM computes exactly what it computes on one stream, so the whole step
+must be bit-identical to the serial one."""
 
 import pytest
 import torch
@@ -15,7 +16,10 @@ DEV = torch.device("cuda:0")
 
 CASES = [("small_T1024", "small", dict(T=1024, d=512, h=256), None),
          ("wide_T700_zipf", "wide", dict(T=700, d=512, h=256), "zipf"),
-         ("lean_small_T384", "small", dict(T=384, d=512, h=256), None)]
+         ("lean_small_T384", "small", dict(T=384, d=512, h=256), None),
+         ("mx_small_T1024", "small", dict(T=1024, d=512, h=256), None),
+         ("mx_wide_T700_zipf", "wide", dict(T=700, d=512, h=256), "zipf"),
+         ("mx_lean_small_T384", "small", dict(T=384, d=512, h=256), None)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -30,10 +34,11 @@ def test_two_stream_backward_is_bit_identical(case):
     forced = None
     if mode:
         forced = torch.from_numpy(inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)).to(DEV)
-    lean = name.startswith("lean")
+    lean = "lean" in name
+    mx = name.startswith("mx_")
     out = {}
     for ov in (False, True):
-        layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, lean=lean, overlap=ov)
+        layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, mx=mx, lean=lean, overlap=ov)
         assert layer.overlap == ov
         for _ in range(2):  # the second step reuses the side stream and its events
             layer.step(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"], forced_idx=forced)

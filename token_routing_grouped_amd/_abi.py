@@ -55,6 +55,7 @@ _SIGS = {
     "mx_quantize": ([_P, _I, _I, _I, _P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P], _I),
     "moe_grouped_gemm_fwd_mx": ([_P, _P], _I),
     "moe_grouped_gemm_bwd_mx": ([_P, _P], _I),
+    "moe_grouped_gemm_bwd_mx_parts": ([_P, ctypes.c_uint, _P], _I),
 }
 
 
@@ -367,3 +368,9 @@ def moe_grouped_gemm_bwd_mx(**kw):
     """Keyword arguments are the fields of moe_mx_bwd_args (tensors or ints)."""
     a = _fill(MxBwdArgs(), **kw)
     _check(lib().moe_grouped_gemm_bwd_mx(ctypes.byref(a), _stream()), "moe_grouped_gemm_bwd_mx")
+
+
+def moe_grouped_gemm_bwd_mx_parts(parts, **kw):
+    """A subset (MOE_BWD_* mask) of moe_grouped_gemm_bwd_mx's four GEMMs."""
+    a = _fill(MxBwdArgs(), **kw)
+    _check(lib().moe_grouped_gemm_bwd_mx_parts(ctypes.byref(a), parts, _stream()), "moe_grouped_gemm_bwd_mx_parts")

@@ -26,8 +26,9 @@ class LayerConfig:
     modes: tuple = ("router",)
     mx: bool = False  # MXFP8 grouped GEMMs
     # Backward schedule of the timed step: weight-gradient GEMMs on a second
-    # stream next to the dgrad chain where that measured faster (small: -5% per
-    # step; wide about -1%, kept serial; trillion +7%, serial).
+    # stream next to the dgrad chain where that measured faster (bf16 small
+    # -5% per step, MXFP8 wide -1%; bf16 wide about -1%, kept serial; trillion
+    # +7% and MXFP8 small +1%, serial).
     overlap: bool = False
     x_std: float = 1.0
     w_std: float = 0.02
@@ -55,7 +56,7 @@ CONFIGS = {
     "wide": LayerConfig("wide", T=16384, d=2048, E=128, k=4, h=1024, dtype="bf16", seed=2,
                         modes=("router", "uniform", "zipf")),
     "mxfp8": LayerConfig("mxfp8", T=16384, d=2048, E=128, k=4, h=1024, dtype="bf16", seed=2,
-                         modes=("router", "uniform"), mx=True),
+                         modes=("router", "uniform"), mx=True, overlap=True),
     "mxfp8_small": LayerConfig("mxfp8_small", T=8192, d=2048, E=8, k=4, h=1024, dtype="bf16",
                                seed=1, mx=True),
     "trillion": LayerConfig("trillion", T=4096, d=6144, E=384, k=8, h=2048, dtype="bf16", seed=4,

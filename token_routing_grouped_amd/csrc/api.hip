@@ -527,9 +527,10 @@ moe_status_t moe_grouped_gemm_recompute_gu_mx(const moe_mx_fwd_args* a, void* st
   return hip_status(fn, trg::launch_ggemm_recompute_gu_mx(*a, (hipStream_t)stream));
 }
 
-moe_status_t moe_grouped_gemm_bwd_mx(const moe_mx_bwd_args* a, void* stream) {
-  const char* fn = "moe_grouped_gemm_bwd_mx";
+static moe_status_t ggemm_bwd_mx_impl(const char* fn, const moe_mx_bwd_args* a, unsigned parts, void* stream) {
   if (!a) return fail(MOE_ERR_INVALID_ARG, "%s: args is null", fn);
+  if (parts == 0 || (parts & ~(unsigned)MOE_BWD_ALL) != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: parts must be a non-empty subset of MOE_BWD_ALL", fn);
   TRY(check_mx_dims(fn, a->E, a->R, a->d, a->h, a->rcap, a->ws, a->ws_bytes));
   TRY(check_ptrs(fn, {{"offsets", a->offsets}, {"off128", a->off128}, {"w1tq", a->w1tq}, {"w1ts", a->w1ts},
                       {"w3tq", a->w3tq}, {"w3ts", a->w3ts}, {"w2tq", a->w2tq}, {"w2ts", a->w2ts}, {"dw1", a->dw1},
@@ -540,7 +541,15 @@ moe_status_t moe_grouped_gemm_bwd_mx(const moe_mx_bwd_args* a, void* stream) {
     TRY(check_ptrs(fn, {{"dyp", a->dyp}, {"g", a->g}, {"u", a->u}, {"dgu", a->dgu}, {"dguq", a->dguq},
                         {"dgus", a->dgus}, {"dxp", a->dxp}}));
   TRY(check_device());
-  return hip_status(fn, trg::launch_ggemm_bwd_mx(*a, (hipStream_t)stream));
+  return hip_status(fn, trg::launch_ggemm_bwd_mx(*a, parts, (hipStream_t)stream));
+}
+
+moe_status_t moe_grouped_gemm_bwd_mx(const moe_mx_bwd_args* a, void* stream) {
+  return ggemm_bwd_mx_impl("moe_grouped_gemm_bwd_mx", a, MOE_BWD_ALL, stream);
+}
+
+moe_status_t moe_grouped_gemm_bwd_mx_parts(const moe_mx_bwd_args* a, unsigned parts, void* stream) {
+  return ggemm_bwd_mx_impl("moe_grouped_gemm_bwd_mx_parts", a, parts, stream);
 }
 
 }  // extern "C"

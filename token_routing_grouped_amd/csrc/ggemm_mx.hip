@@ -420,10 +420,10 @@ hipError_t launch_ggemm_fwd_mx(const MxFwd& p, hipStream_t s) {
 }
 
 template <int BM>
-static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, hipStream_t s) {
+static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, unsigned parts, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
   const int mt_max = cdiv(R, BM) + E;
-  {  // dgrad down + SwiGLU backward: dyq [R,d] x W2 blocked along d ([h, E*d])
+  if (parts & MOE_BWD_DGRAD_DOWN) {  // dgrad down + SwiGLU backward: dyq [R,d] x W2 blocked along d ([h, E*d])
     Args a{};
     a.A = (const uint16_t*)p.dyq; a.lda = d;
     a.B = (const uint16_t*)p.w2tq; a.ldb = (long)E * d; a.b_es = d;
@@ -438,13 +438,13 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, hipStream_t s
     run_mx<BM, 256, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_SWIGLU_BWD>("ggemm_mx_dgrad_down_swiglu", a, x,
                                                                     mt_max * a.tiles_n, s);
   }
-  {
+  if (parts & MOE_BWD_DGRAD_DOWN) {
     ProfScope ps("mx_quantize_dgu", s);
     const hipError_t err = launch_mx_quantize(p.dgu, true, 2L * h, R, 2 * h, nullptr, 1, p.offsets, p.off128, E, 0,
                                               (R + 127 * E + 31) / 32, p.dguq, p.dgus, p.dguqT, p.dgusT, p.rcap, s);
     if (err != hipSuccess) return err;
   }
-  {  // dgrad up: dguq [R,2h] x (W1 | W3) blocked along h ([d, E*h] each)
+  if (parts & MOE_BWD_DGRAD_UP) {  // dgrad up: dguq [R,2h] x (W1 | W3) blocked along h ([d, E*h] each)
     Args a{};
     a.A = (const uint16_t*)p.dguq; a.lda = 2L * h;
     a.B = (const uint16_t*)p.w1tq; a.B2 = (const uint16_t*)p.w3tq; a.ldb = (long)E * h; a.b_es = h;
@@ -460,25 +460,28 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
+// parts (MOE_BWD_* mask): DGRAD_DOWN also quantises dYp before its GEMM and
+// dG|dU after it, so WGRAD_DOWN and WGRAD_UP may start once it is done.
+hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
-  int* tile_off = (int*)p.ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, E, tile_off, split_tails(E, p.R));
-  {  // dYp -> rowwise (dgrad down) and columnwise per expert (wgrad down)
+  if (parts & MOE_BWD_DGRAD_DOWN) {  // dYp -> rowwise (dgrad down) and columnwise per expert (wgrad down)
     ProfScope ps("mx_quantize_dy", s);
     const hipError_t err = launch_mx_quantize(p.dyp, true, d, R, d, nullptr, 1, p.offsets, p.off128, E, 0,
                                               (R + 127 * E + 31) / 32, p.dyq, p.dys, p.dyqT, p.dysT, p.rcap, s);
     if (err != hipSuccess) return err;
   }
-  {
-    const hipError_t err =
-        small_rows(E, R) ? mx_dgrad_bm<128>(p, tile_off, s) : mx_dgrad_bm<256>(p, tile_off + (E + 1), s);
+  if (parts & (MOE_BWD_DGRAD_DOWN | MOE_BWD_DGRAD_UP)) {
+    int* tile_off = (int*)p.ws;
+    tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, E, tile_off, split_tails(E, p.R));
+    const hipError_t err = small_rows(E, R) ? mx_dgrad_bm<128>(p, tile_off, parts, s)
+                                            : mx_dgrad_bm<256>(p, tile_off + (E + 1), parts, s);
     if (err != hipSuccess) return err;
   }
+  if (!(parts & (MOE_BWD_WGRAD_DOWN | MOE_BWD_WGRAD_UP))) return hipGetLastError();
   const long sc = p.rcap / 32;
   int* work = (int*)p.ws + 3 * (E + 1);
   wgrad_work_kernel<<<1, 1024, 0, s>>>(p.off128, E, 128, work);
-  {  // wgrad down: dW2[e] = dYp_e^T H_e over the expert's padded segment
+  if (parts & MOE_BWD_WGRAD_DOWN) {  // wgrad down: dW2[e] = dYp_e^T H_e over the expert's padded segment
     Args a{};
     a.A = (const uint16_t*)p.dyqT; a.lda = p.rcap;
     a.B = (const uint16_t*)p.hqT; a.ldb = p.rcap;
@@ -492,7 +495,7 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s) {
     run_mx<256, 256, RAGGED_K, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_mx_wgrad_down", a, x, E * a.tiles_m * a.tiles_n,
                                                                s);
   }
-  {  // wgrad up: [dW1; dW3][e] = [dG | dU]_e^T Xp_e
+  if (parts & MOE_BWD_WGRAD_UP) {  // wgrad up: [dW1; dW3][e] = [dG | dU]_e^T Xp_e
     Args a{};
     a.A = (const uint16_t*)p.dguqT; a.lda = p.rcap;
     a.B = (const uint16_t*)p.xqT; a.ldb = p.rcap;

@@ -73,6 +73,6 @@ hipError_t launch_ggemm_recompute_gu(const void* xp, const void* w1, const void*
                                      int d, int h, void* g, void* u, void* ws, hipStream_t s);
 hipError_t launch_ggemm_recompute_gu_mx(const MxFwd& p, hipStream_t s);
 hipError_t launch_ggemm_fwd_mx(const MxFwd& p, hipStream_t s);
-hipError_t launch_ggemm_bwd_mx(const MxBwd& p, hipStream_t s);
+hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s);
 
 }  // namespace trg

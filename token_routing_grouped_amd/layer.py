@@ -46,9 +46,9 @@ class MoELayerGPU:
         # recomputes them (one more up projection) into g / u, which then act
         # as backward scratch
         self.lean = bool(lean)
-        # overlap (bf16): the weight-gradient GEMMs run on a second stream
-        # (default priority) next to the dgrad chain, joined by events
-        self.overlap = bool(overlap) and not mx
+        # overlap: the weight-gradient GEMMs run on a second stream (default
+        # priority) next to the dgrad chain, joined by events
+        self.overlap = bool(overlap)
         self.R = R = T * k
         self.dtype = dtype
         self.mx = mx
@@ -161,22 +161,17 @@ class MoELayerGPU:
         _abi.moe_combine_bwd(dy, self.yp, self.topk_w, self.pos, self.dyp, self.dgate)
         if self.lean:
             self.recompute_gu(w1, w3)
-        if self.mx:
-            _abi.moe_grouped_gemm_bwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, rcap=self.rcap,
-                                         offsets=self.offsets, off128=self.off128, dyp=self.dyp, dyq=self.dyq,
-                                         dys=self.dys, dyqT=self.dyqT, dysT=self.dysT, g=self.g, u=self.u,
-                                         hqT=self.hqT, hsT=self.hsT, xqT=self.xqT, xsT=self.xsT, w1tq=self.w1tq,
-                                         w1ts=self.w1ts, w3tq=self.w3tq, w3ts=self.w3ts, w2tq=self.w2tq,
-                                         w2ts=self.w2ts, dgu=self.dgu, dguq=self.dguq, dgus=self.dgus,
-                                         dguqT=self.dguqT, dgusT=self.dgusT, dxp=self.dxp, dw1=self.dw1, dw3=self.dw3,
-                                         dw2=self.dw2, ws=self.ws_gemm, ws_bytes=self.ws_gemm.numel())
+        if self.mx and self.overlap:
+            self._backward_gemms_two_streams_mx()
+        elif self.mx:
+            _abi.moe_grouped_gemm_bwd_mx(**self._mx_bwd_fields(self.ws_gemm))
         elif self.overlap:
             self._backward_gemms_two_streams(w1, w3, w2)
         else:
             _abi.moe_grouped_gemm_bwd(self.dyp, self.xp, self.g, self.u, self.hb, w1, w3, w2, self.offsets, self.dgu,
                                       self.dxp, self.dw1, self.dw3, self.dw2, self.ws_gemm)
         _abi.moe_unpermute_sum(self.dxp, self.pos, self.dx)
-        if self.overlap and not self.mx:
+        if self.overlap:
             torch.cuda.current_stream().wait_event(self._ev_side_done)
         if self.aux_alpha > 0.0:
             _abi.moe_router_bwd_aux(self.probs, self.topk_idx, self.dgate, self.aux_g, x, wr, self.dx, self.dwr,
@@ -192,6 +187,30 @@ class MoELayerGPU:
         _abi.moe_balance(self.probs, self.counts, self.k, self.aux_alpha if alpha is None else alpha,
                          self.balance_stats, self.ws_balance, aux_g=self.aux_g, mean_probs=self.mean_probs)
         return self.balance_stats
+
+    def _mx_bwd_fields(self, ws):
+        return dict(E=self.E, R=self.R, d=self.d, h=self.h, rcap=self.rcap, offsets=self.offsets, off128=self.off128,
+                    dyp=self.dyp, dyq=self.dyq, dys=self.dys, dyqT=self.dyqT, dysT=self.dysT, g=self.g, u=self.u,
+                    hqT=self.hqT, hsT=self.hsT, xqT=self.xqT, xsT=self.xsT, w1tq=self.w1tq, w1ts=self.w1ts,
+                    w3tq=self.w3tq, w3ts=self.w3ts, w2tq=self.w2tq, w2ts=self.w2ts, dgu=self.dgu, dguq=self.dguq,
+                    dgus=self.dgus, dguqT=self.dguqT, dgusT=self.dgusT, dxp=self.dxp, dw1=self.dw1, dw3=self.dw3,
+                    dw2=self.dw2, ws=ws, ws_bytes=ws.numel())
+
+    def _backward_gemms_two_streams_mx(self):
+        """MXFP8: dgrad-down (which also makes the MX copies of dYp and dG|dU)
+        on the current stream, then both weight gradients on the side stream
+        while dgrad-up runs."""
+        main, side = torch.cuda.current_stream(), self.side_stream
+        _abi.moe_grouped_gemm_bwd_mx_parts(_abi.BWD_DGRAD_DOWN, **self._mx_bwd_fields(self.ws_gemm))
+        ev = torch.cuda.Event()
+        ev.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(ev)
+            _abi.moe_grouped_gemm_bwd_mx_parts(_abi.BWD_WGRAD_DOWN | _abi.BWD_WGRAD_UP,
+                                               **self._mx_bwd_fields(self.ws_gemm2))
+            self._ev_side_done = torch.cuda.Event()
+            self._ev_side_done.record(side)
+        _abi.moe_grouped_gemm_bwd_mx_parts(_abi.BWD_DGRAD_UP, **self._mx_bwd_fields(self.ws_gemm))
 
     def _backward_gemms_two_streams(self, w1, w3, w2):
         """dgrad chain on the current stream, weight gradients on the side
