@@ -119,3 +119,24 @@ def test_full_size_sampled_parity(case):
     report["dWr"] = _check("dWr", to_np(layer.dwr), dwr, cfg.mx, tight=True)  # the router is bf16 in every config
     say(f"  {len(S)} tokens, experts {busy} ({counts[busy]} rows) and {other} ({counts[other]} rows); rel-L2: "
         + " ".join(f"{n}={v:.1e}" for n, v in report.items()))
+
+
+@pytest.mark.parametrize("slug", ["small", "mxfp8"])
+def test_full_size_step_is_bitwise_reproducible(slug):
+    """Two steps of the timed configuration (two streams where the workload's
+    config sets them; light-tail tile order at the small shape) give the same
+    bits in every output and gradient."""
+    from token_routing_grouped_amd.layer import MoELayerGPU
+
+    cfg = configs.get(slug)
+    say(f"full size determinism {slug}: overlap={cfg.overlap} mx={cfg.mx}")
+    t, _ = inputs.device_inputs(cfg, DEV)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, DEV, mx=cfg.mx, overlap=cfg.overlap)
+    outs = []
+    for _ in range(2):
+        layer.step(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])
+        torch.cuda.synchronize()
+        outs.append({n: getattr(layer, n).clone() for n in ("y", "dx", "dw1", "dw3", "dw2", "dwr", "dgate")})
+    for n in outs[0]:
+        assert torch.equal(outs[0][n], outs[1][n]), n
