@@ -49,7 +49,16 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
   static_assert(BM % 128 == 0 && BN % 128 == 0, "tile");
   static_assert(BSEL != BSEL_GLU || (TN % 2 == 0), "GLU pairs subtiles");
   static_assert(MODE == RAGGED_M || (!AKC && !BKC), "weight gradients read both operands MN-contiguous");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // Light tail tiles (RmSched: at most 128 valid rows, 256-row tiles) run a
+  // three-stage pipeline: they need only half the A stage, so three stages of
+  // LSTAGE bytes fit, and two steps of prefetch hide the load latency their
+  // few MFMAs cannot.  LPW: stage loads per wave per light step.
+  constexpr bool LIGHT3 = MODE == RAGGED_M && BM == 256 && AKC;
+  constexpr int LSA = 128 * 128, LSTAGE = LSA + SB;
+  constexpr int LPW = (128 / 8) / NW + (BKC ? (BN / 8) / NW : (64 * BN * 2 / 1024) / NW);
+  static_assert(!LIGHT3 || LPW == 6, "the light pipeline's vmcnt immediate");
+  constexpr int SMEM = LIGHT3 && 3 * LSTAGE > 2 * STAGE ? 3 * LSTAGE : 2 * STAGE;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -71,14 +80,17 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
   // Per-tile geometry and operand resources.
   struct Tile {
     int e, m0, m_end, n0, k0, k_end;
+    bool light;  // a light tail (three-stage pipeline)
     __amdgpu_buffer_rsrc_t rsA, rsB, rsB2;
   };
   const long a_ldb = g.lda * 2, b_ldb = g.ldb * 2;
   auto decode = [&](int t) {
     Tile c;
+    c.light = false;
     if constexpr (MODE == RAGGED_M) {
       int nt;
       rm_tile<BM>(g.tile_off, g.offsets, g.E, g.tiles_n, rms, t, c.e, c.m0, c.m_end, nt);
+      c.light = LIGHT3 && t >= rms.nf;
       c.n0 = nt * BN;
       c.k0 = 0;
       c.k_end = g.K;
@@ -134,7 +146,14 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
   auto issue = [&](const Tile& c, int kt, int stage) {  // kt: K offset relative to c.k0
     char* sA = smem + stage * STAGE;
     char* sB = sA + SA;
-    if constexpr (AKC) {
+    if (LIGHT3 && c.light) {  // rows 0..127 of A and all of B, stage stride LSTAGE
+      sA = smem + stage * LSTAGE;
+      sB = sA + LSA;
+      load_kc<128, NW>(sA, wave, a_lane, kt * 2, (int)a_ldb, [&](int r8, int& r0) {
+        r0 = r8;
+        return c.rsA;
+      });
+    } else if constexpr (AKC) {
       load_kc<BM, NW>(sA, wave, a_lane, kt * 2, (int)a_ldb, [&](int r8, int& r0) {
         r0 = r8;
         return c.rsA;
@@ -197,12 +216,28 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
       const int rows = m_end - (m0 + wm * WTM);
       nv = rows <= 0 ? 0 : (rows >= WTM ? TM : (rows + 31) / 32);
     }
+    const bool light = LIGHT3 && cur.light;
     for (int it = 0; it < nk; ++it) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // stage it&1 is complete; stage (it+1)&1 is free
-      if (it + 1 < nk) issue(cur, (it + 1) * BK, (it + 1) & 1);
-      const char* sA = smem + (it & 1) * STAGE;
-      const char* sB = sA + SA;
+      // light: step it+1's LPW loads per wave may stay in flight
+      if (light && it > 0 && it + 1 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // this step's stage is complete; the stage read last step is free
+      const char* sA;
+      const char* sB;
+      if (light) {
+        if (it == 0) {
+          if (nk > 1) issue(cur, BK, 1);
+          if (nk > 2) issue(cur, 2 * BK, 2);
+        } else if (it + 2 < nk) {
+          issue(cur, (it + 2) * BK, (it + 2) % 3);
+        }
+        sA = smem + (it % 3) * LSTAGE;
+        sB = sA + LSA;
+      } else {
+        if (it + 1 < nk) issue(cur, (it + 1) * BK, (it + 1) & 1);
+        sA = smem + (it & 1) * STAGE;
+        sB = sA + SA;
+      }
       bf16x8_t af[2][TM], bfr[2][TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[0][i] = frag<BM, AKC>(sA, wm * WTM + i * 32, 0, lane);
