@@ -203,7 +203,8 @@ TRG_DEV bf16x8_t frag(const char* s, int base, int kk, int lane) {
 // accumulators, see below); EPI_SWIGLU_BWD treats the tile as dH and writes
 // dG | dU from the stored G and U.
 template <int WTN, int EPI, int WLDS>
-constexpr int epilogue_slab_rows() {  // 16 rows when they fit the wave's area, else 8
+constexpr int epilogue_slab_rows() {  // plain bf16: whole 32-row subtiles when they fit; else 16 rows, else 8
+  if (EPI == EPI_BF16 && 32 * (WTN * 2 + 16) <= WLDS) return 32;
   return (EPI == EPI_SWIGLU_BWD ? 2 * 16 * (WTN * 2 + 16) : 16 * (WTN * 2 + 16)) <= WLDS ? 16 : 8;
 }
 
