@@ -57,7 +57,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
   constexpr int LSA = 128 * 128, LSTAGE = LSA + SB;
   constexpr int LPW = (128 / 8) / NW + (BKC ? (BN / 8) / NW : (64 * BN * 2 / 1024) / NW);
   static_assert(!LIGHT3 || LPW == 6, "the light pipeline's vmcnt immediate");
-  constexpr int SMEM = LIGHT3 && 3 * LSTAGE > 2 * STAGE ? 3 * LSTAGE : 2 * STAGE;
+  // (the weight gradients take the same 144 KB, for a larger epilogue area)
+  constexpr int SMEM = LIGHT3 && 3 * LSTAGE > 2 * STAGE ? 3 * LSTAGE
+                       : (MODE == RAGGED_K && BM == 256 ? 3 * (128 * 128 + SB) : 2 * STAGE);
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -278,7 +280,10 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
         cur = nxt;
       }
     }
-    constexpr int WLDS = STAGE / NW;  // LDS bytes per wave, inside stage 1
+    // LDS bytes per wave: inside stage 1; for the weight gradients everything
+    // past stage 0 (which may already hold the next tile's first step), room
+    // for 64-row slabs (ragged M measured no better with them)
+    constexpr int WLDS = MODE == RAGGED_K ? (SMEM - STAGE) / NW / 256 * 256 : STAGE / NW;
     epilogue<WTM, WTN, CSEL, EPI, WLDS, MODE == RAGGED_M>(g, acc, smem + STAGE + wave * WLDS, lane, wm, wn, e, m0, m_end, n0);
   }
 }

@@ -203,7 +203,8 @@ TRG_DEV bf16x8_t frag(const char* s, int base, int kk, int lane) {
 // accumulators, see below); EPI_SWIGLU_BWD treats the tile as dH and writes
 // dG | dU from the stored G and U.
 template <int WTN, int EPI, int WLDS>
-constexpr int epilogue_slab_rows() {  // plain bf16: whole 32-row subtiles when they fit; else 16 rows, else 8
+constexpr int epilogue_slab_rows() {  // plain bf16: two or one whole 32-row subtiles when they fit; else 16 rows, else 8
+  if (EPI == EPI_BF16 && 64 * (WTN * 2 + 16) <= WLDS) return 64;
   if (EPI == EPI_BF16 && 32 * (WTN * 2 + 16) <= WLDS) return 32;
   return (EPI == EPI_SWIGLU_BWD ? 2 * 16 * (WTN * 2 + 16) : 16 * (WTN * 2 + 16)) <= WLDS ? 16 : 8;
 }
@@ -214,7 +215,7 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int P = WTN * 2 + 16;       // staged row pitch (16-byte aligned)
   constexpr int SR = epilogue_slab_rows<WTN, EPI, WLDS>();  // slab rows: a part of an accumulator subtile
-  constexpr int NPART = 32 / SR;
+  constexpr int NPART = SR >= 32 ? 1 : 32 / SR;
   static_assert(EPI != EPI_SWIGLU_BWD || 2 * SR * P <= WLDS, "epilogue LDS");
   if constexpr (EPI == EPI_SWIGLU_FWD) {
     // G, U and H go out straight from the accumulators (8-byte pieces, merged
@@ -265,6 +266,47 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
       if (ms + row < m_end) dst(ms + row, cc * 8, *(const uint4*)(slab + row * pitch + cc * 16));
     }
   };
+  if constexpr (EPI == EPI_BF16 && SR > 32) {
+    // SUB whole 32-row subtiles per round: fewer LDS write -> read turns
+    constexpr int SUB = SR / 32;
+    static_assert(TM % SUB == 0, "subtiles per round");
+    char* sC = wl;
+    const int nw = n0 + wn * WTN;
+    static_for<TM / SUB>([&](auto IS) {
+      constexpr int i0 = decltype(IS)::value * SUB;
+      const int ms = mw + i0 * 32;
+      if (ms < m_end) {
+        static_for<SUB>([&](auto S) {
+          constexpr int sub = decltype(S)::value;
+          static_for<TN>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            static_for<4>([&](auto Q) {
+              constexpr int q = decltype(Q)::value;
+              *(uint2*)(sC + (sub * 32 + lrow) * P + (j * 32 + q * 8 + lgrp) * 2) =
+                  make_uint2(pack_bf2(acc[i0 + sub][j][q * 4 + 0], acc[i0 + sub][j][q * 4 + 1]),
+                             pack_bf2(acc[i0 + sub][j][q * 4 + 2], acc[i0 + sub][j][q * 4 + 3]));
+            });
+          });
+        });
+        __builtin_amdgcn_wave_barrier();
+        store_rows(sC, P, WTN, ms, [&](int m, int c, uint4 v) {
+          if (nw + c < g.N) {
+            uint16_t* Cb = (uint16_t*)g.C;
+            int mr = m;
+            if constexpr (CSEL == CSEL_MSPLIT) {
+              if (m >= g.split) {
+                Cb = (uint16_t*)g.C2;
+                mr = m - g.split;
+              }
+            }
+            store_row16(NT, Cb + (long)e * g.c_es + (long)mr * g.ldc + nw + c, v);
+          }
+        });
+      }
+      __builtin_amdgcn_wave_barrier();  // the slab area is rewritten next
+    });
+    return;
+  }
   // SWIGLU_BWD: G and U of one slab, GUQ 16-byte pieces per lane, in flight
   // one slab ahead
   constexpr int GUQ = EPI == EPI_SWIGLU_BWD ? SR * (WTN / 8) / 64 : 1;
