@@ -217,6 +217,56 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
   constexpr int SR = epilogue_slab_rows<WTN, EPI, WLDS>();  // slab rows: a part of an accumulator subtile
   constexpr int NPART = SR >= 32 ? 1 : 32 / SR;
   static_assert(EPI != EPI_SWIGLU_BWD || 2 * SR * P <= WLDS, "epilogue LDS");
+  if constexpr (EPI == EPI_SWIGLU_FWD && 3 * 32 * (WTN + 16) <= WLDS) {
+    // G, U and H of one 32-row subtile staged in LDS (the wave's WTN/2 hidden
+    // units, row pitch PF), then written as 16-byte row pieces
+    constexpr int PF = WTN + 16;
+    constexpr int CPR = WTN / 16;  // 16-byte chunks per staged row
+    const int lrow = lane & 31, lgrp = (lane >> 5) * 4;
+    const int hh0 = n0 / 2 + wn * (WTN / 2);
+    char* sG = wl;
+    char* sU = wl + 32 * PF;
+    char* sH = wl + 64 * PF;
+    static_for<TM>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const int ms = m0 + wm * WTM + i * 32;
+      if (ms < m_end) {
+        static_for<TN / 2>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          static_for<4>([&](auto Q) {
+            constexpr int q = decltype(Q)::value;
+            float gv[4], uv[4], hv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              gv[r] = acc[i][j][q * 4 + r];
+              uv[r] = acc[i][j + TN / 2][q * 4 + r];
+              hv[r] = silu_f(gv[r]) * uv[r];
+            }
+            const int off = lrow * PF + (j * 32 + q * 8 + lgrp) * 2;
+            *(uint2*)(sG + off) = make_uint2(pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3]));
+            *(uint2*)(sU + off) = make_uint2(pack_bf2(uv[0], uv[1]), pack_bf2(uv[2], uv[3]));
+            *(uint2*)(sH + off) = make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
+          });
+        });
+        __builtin_amdgcn_wave_barrier();
+        // any of G, U, H may be absent: a memory-lean forward stores H only,
+        // the backward's recompute G and U only (uniform branches)
+        for (int c = lane; c < 32 * CPR; c += 64) {
+          const int row = c / CPR, cc = c - row * CPR;
+          const int m = ms + row, col = hh0 + cc * 8;
+          if (m < m_end && col < g.split) {
+            const long off = (long)m * g.ldc + col;
+            const int so = row * PF + cc * 16;
+            if (g.C) *(uint4*)((uint16_t*)g.C + off) = *(const uint4*)(sG + so);
+            if (g.C2) *(uint4*)((uint16_t*)g.C2 + off) = *(const uint4*)(sU + so);
+            if (g.C3) *(uint4*)((uint16_t*)g.C3 + off) = *(const uint4*)(sH + so);
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();  // the staging area is rewritten next
+    });
+    return;
+  }
   if constexpr (EPI == EPI_SWIGLU_FWD) {
     // G, U and H go out straight from the accumulators (8-byte pieces, merged
     // into whole lines by L2): measured faster than staging three arrays
