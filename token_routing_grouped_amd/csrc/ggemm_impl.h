@@ -55,9 +55,10 @@ struct Args {
 
 // Staged epilogue rows go out with store_nt16 when NT (the ragged-M GEMMs:
 // 2-6% faster on dgrad-down and down at the small shape; the weight gradients
-// measured no better, or slower, with it).  The SwiGLU-forward epilogue's
-// direct 8-byte stores keep the default policy: as partial lines they rely on
-// L2 merging them, and with the hint that kernel took twice as long.
+// measured no better, or slower, with it).  The SwiGLU-forward epilogue keeps
+// the default policy: its staged stores gained nothing overall with the hint
+// (the down projection that reads H next slowed by more), and its direct
+// 8-byte stores rely on L2 merging partial lines (twice as slow with it).
 TRG_DEV void store_row16(bool nt, void* p, uint4 v) {
   if (nt) store_nt16(p, v);
   else *(uint4*)p = v;
@@ -192,15 +193,16 @@ TRG_DEV bf16x8_t frag(const char* s, int base, int kk, int lane) {
   else return frag_mnc<BMN>(s, base, kk, lane);
 }
 
-// Epilogue of one output tile.  Each wave stages 16-row slabs of its tile in
-// a private LDS area `wl` (WLDS bytes) and writes whole row segments with
-// 16-byte stores; the accumulator layout alone would scatter 8-byte pieces over
+// Epilogue of one output tile.  Each wave stages slabs of its tile (8 to 64
+// rows, as many as its private LDS area `wl` of WLDS bytes holds) and writes
+// whole row segments with 16-byte stores; the accumulator layout alone would scatter 8-byte pieces over
 // 32 rows per store instruction.  Accumulator lane (lrow, lgrp) owns row lrow
 // and, per 32-column subtile j and group q, columns j*32 + q*8 + lgrp + {0..3}.
 // EPI_BF16 writes C (rows >= split go to C2 under CSEL_MSPLIT, plus e*c_es);
 // EPI_SWIGLU_FWD treats the first TN/2 subtiles as G and the rest as U of the
-// same hidden units and writes G, U and H = silu(G) * U (directly from the
-// accumulators, see below); EPI_SWIGLU_BWD treats the tile as dH and writes
+// same hidden units and writes G, U and H = silu(G) * U (staged per 32-row
+// subtile where the three fit, else directly from the accumulators, see
+// below); EPI_SWIGLU_BWD treats the tile as dH and writes
 // dG | dU from the stored G and U.
 template <int WTN, int EPI, int WLDS>
 constexpr int epilogue_slab_rows() {  // plain bf16: two or one whole 32-row subtiles when they fit; else 16 rows, else 8
