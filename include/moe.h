@@ -84,9 +84,12 @@ const char* moe_last_error_string(void);
  * `name` and returns their count and summed milliseconds (this call does
  * block the host).  moe_prof_names(): newline-separated names seen so far;
  * returns the size needed (including the NUL).  moe_prof_reset() frees all
- * recorded events.
+ * recorded events.  moe_prof_only(name): from then on only launches called
+ * `name` are bracketed (null or "": every launch, the default); the name is
+ * copied.
  */
 moe_status_t moe_prof_enable(int on);
+moe_status_t moe_prof_only(const char* name);
 moe_status_t moe_prof_reset(void);
 moe_status_t moe_prof_query(const char* name, int* count, float* total_ms);
 size_t moe_prof_names(char* buf, size_t n);

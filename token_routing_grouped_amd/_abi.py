@@ -30,6 +30,7 @@ _SIGS = {
     "moe_last_error_string": ([], ctypes.c_char_p),
     "moe_prof_enable": ([_I], _I),
     "moe_prof_reset": ([], _I),
+    "moe_prof_only": ([ctypes.c_char_p], _I),
     "moe_prof_query": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)], _I),
     "moe_prof_names": ([ctypes.c_char_p, _Z], _Z),
     "moe_router_logits": ([_P, _I, _P, _I, _I, _I, _P, _P], _I),
@@ -140,6 +141,11 @@ def _stream():
 
 def prof_enable(on: bool = True):
     _check(lib().moe_prof_enable(1 if on else 0), "moe_prof_enable")
+
+
+def prof_only(name=None):
+    """Bracket only launches called `name` with events (None: every launch)."""
+    _check(lib().moe_prof_only(name.encode() if name else None), "moe_prof_only")
 
 
 def prof_reset():

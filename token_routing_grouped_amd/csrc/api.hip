@@ -26,11 +26,18 @@ struct ProfRec {
 };
 std::vector<ProfRec> g_prof_done;
 std::vector<std::pair<std::string, hipEvent_t>> g_prof_open;
+std::string g_prof_only;  // empty: every launch; else only launches of this name
+
+bool prof_selected(const char* name) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  return g_prof_only.empty() || g_prof_only == name;
+}
 }  // namespace
 
 bool prof_on() { return g_prof.load(std::memory_order_relaxed); }
 
 void prof_begin(const char* name, hipStream_t s) {
+  if (!prof_selected(name)) return;
   hipEvent_t ev;
   if (hipEventCreate(&ev) != hipSuccess) return;
   (void)hipEventRecord(ev, s);
@@ -39,6 +46,7 @@ void prof_begin(const char* name, hipStream_t s) {
 }
 
 void prof_end(const char* name, hipStream_t s) {
+  if (!prof_selected(name)) return;
   hipEvent_t ev;
   if (hipEventCreate(&ev) != hipSuccess) return;
   (void)hipEventRecord(ev, s);
@@ -145,6 +153,12 @@ const char* moe_last_error_string(void) { return g_err.c_str(); }
 
 moe_status_t moe_prof_enable(int on) {
   trg::g_prof.store(on != 0);
+  return ok();
+}
+
+moe_status_t moe_prof_only(const char* name) {
+  std::lock_guard<std::mutex> lk(trg::g_prof_mu);
+  trg::g_prof_only = name ? name : "";
   return ok();
 }
 
