@@ -33,7 +33,10 @@ Modules:
 
 Pins: every function here is checked against something other than itself in
 ``tests/test_oracle_*.py`` (closed forms, brute force, finite differences,
-hand-derived vectors in ``tests/golden/``).  The MXFP8 layer result (QDQ
-oracle) has no external value to pin its end-to-end number: parity unpinned
-beyond the per-step pins of mx_ref.
+hand-derived vectors in ``tests/golden/``).  The MXFP8 layer (QDQ oracle)
+is pinned GEMM by GEMM: where every operand is already on the MX grid along
+the axis its GEMM blocks it on, and off the grid along the other axis, its
+result must equal the float oracle's exactly (tests/test_oracle_mx_layer.py,
+which also checks that quantising any operand along the wrong axis, over
+whole-R instead of per-expert blocks, or from another MX copy, fails a pin).
 """

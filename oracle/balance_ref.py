@@ -44,10 +44,3 @@ def balance(probs, counts, k, alpha, dtype=F):
                 g=(alpha * E * f / T) if T > 0 else np.zeros(E, dtype),
                 max_over_mean=(float(c.max()) / mean_load) if T > 0 else 0.0)
 
-
-def aux_logits_grad(probs, g, dtype=F):
-    """dL_aux / dlogits: the softmax backward of a gradient g_e that is the same
-    for every token."""
-    p = np.asarray(probs, dtype)
-    gg = np.broadcast_to(np.asarray(g, dtype), p.shape)
-    return p * (gg - np.sum(p * gg, axis=1, keepdims=True))
