@@ -69,6 +69,12 @@ def test_host_side_validation_without_gpu():
     # k out of range
     st = lib.moe_combine(None, None, None, 4, 64, 0, 1, None, None)
     assert st == 1
+    # optional G / U outputs must be 16-byte aligned when given
+    c = ctypes.c_void_p(16)
+    st = lib.moe_grouped_gemm_fwd(c, c, c, c, c, 2, 8, 64, 64, 1, ctypes.c_void_p(24), None, c, c, c, 1 << 20, None)
+    assert st == 3 and b"g is not 16-byte aligned" in lib.moe_last_error_string()
+    st = lib.moe_grouped_gemm_fwd(c, c, c, c, c, 2, 8, 64, 64, 1, None, ctypes.c_void_p(40), c, c, c, 1 << 20, None)
+    assert st == 3 and b"u is not 16-byte aligned" in lib.moe_last_error_string()
 
 
 def test_mx_arg_structs_match_the_header(tmp_path):
@@ -121,6 +127,12 @@ def test_mx_host_side_validation_without_gpu():
     a = _abi.MxFwdArgs(E=2, R=8, d=128, h=128, rcap=96)
     assert lib.moe_grouped_gemm_fwd_mx(ctypes.byref(a), None) == 1
     assert b"multiple of 128" in lib.moe_last_error_string()
+    # optional G / U outputs must be 16-byte aligned when given
+    p = {n: 16 for n in ("offsets", "off128", "xq", "xs", "w1q", "w1s", "w3q", "w3s", "w2q", "w2s", "hbuf", "hq", "hs",
+                         "hqT", "hsT", "yp", "ws")}
+    a = _abi.MxFwdArgs(E=2, R=8, d=128, h=128, rcap=384, ws_bytes=1 << 20, g=24, **p)
+    assert lib.moe_grouped_gemm_fwd_mx(ctypes.byref(a), None) == 3
+    assert b"g is not 16-byte aligned" in lib.moe_last_error_string()
 
 
 @pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")

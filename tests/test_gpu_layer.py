@@ -24,21 +24,31 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 CASES = [
-    # id, base config, overrides, routing mode
-    ("tiny", "tiny", {}, "router"),
-    ("small_T384", "small", dict(T=384), "router"),
-    ("wide_T512_router", "wide", dict(T=512, d=512, h=256), "router"),
-    ("wide_T512_zipf", "wide", dict(T=512, d=512, h=256), "zipf"),
-    ("wide_T640_uniform", "wide", dict(T=640, d=512, h=256), "uniform"),
-    ("trillion_shape_E8", "trillion", dict(T=32, E=8), "uniform"),
-    ("glu_mask_h192", "small", dict(T=100, d=256, h=192), "router"),
-    ("one_expert", "small", dict(T=200, E=1, k=1, d=256, h=256), "router"),
-    ("k_eq_E", "small", dict(T=130, E=4, k=4, d=256, h=128), "router"),
-    ("T1", "small", dict(T=1, d=256, h=128), "router"),
-    ("E384_k8_sparse", "trillion", dict(T=24, d=256, h=128), "uniform"),
+    # id, base config, overrides, routing mode, layer flags
+    ("tiny", "tiny", {}, "router", {}),
+    ("small_T384", "small", dict(T=384), "router", {}),
+    ("wide_T512_router", "wide", dict(T=512, d=512, h=256), "router", {}),
+    ("wide_T512_zipf", "wide", dict(T=512, d=512, h=256), "zipf", {}),
+    ("wide_T640_uniform", "wide", dict(T=640, d=512, h=256), "uniform", {}),
+    ("trillion_shape_E8", "trillion", dict(T=32, E=8), "uniform", {}),
+    ("glu_mask_h192", "small", dict(T=100, d=256, h=192), "router", {}),
+    ("one_expert", "small", dict(T=200, E=1, k=1, d=256, h=256), "router", {}),
+    ("k_eq_E", "small", dict(T=130, E=4, k=4, d=256, h=128), "router", {}),
+    ("T1", "small", dict(T=1, d=256, h=128), "router", {}),
+    ("E384_k8_sparse", "trillion", dict(T=24, d=256, h=128), "uniform", {}),
     # experts of >= 2048 rows on average: light tails (50 and 2 rows past whole
     # 256-row tiles) are scheduled apart from the full-cost tiles
-    ("tail_split_E4", "small", dict(T=4096, E=4, k=2, d=256, h=128), "tails"),
+    ("tail_split_E4", "small", dict(T=4096, E=4, k=2, d=256, h=128), "tails", {}),
+    # d not a multiple of the 256-wide tiles: partial N tiles of the down and
+    # dgrad-up GEMMs, partial M tiles of wgrad-down and partial N tiles of
+    # wgrad-up (256-row tiles at d = 320, 128-row tiles at d = 192)
+    ("d320_router", "small", dict(T=600, d=320, h=256), "router", {}),
+    ("d192_uniform_E16", "wide", dict(T=500, E=16, d=192, h=128), "uniform", {}),
+    # memory-lean backward: G and U recomputed in the backward, checked against
+    # the oracle like the stored ones
+    ("small_T384_lean", "small", dict(T=384), "router", dict(lean=True)),
+    ("wide_T512_zipf_lean", "wide", dict(T=512, d=512, h=256), "zipf", dict(lean=True)),
+    ("trillion_shape_lean", "trillion", dict(T=48, d=256, h=256), "uniform", dict(lean=True)),
 ]
 
 
@@ -54,14 +64,14 @@ def test_layer_parity(case):
     from token_routing_grouped_amd import _abi
     from token_routing_grouped_amd.layer import MoELayerGPU
 
-    name, base, over, mode = case
+    name, base, over, mode, flags = case
     cfg = configs.get(base).with_(**over)
-    say(f"layer {name}: T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} h={cfg.h} {cfg.dtype} {mode}")
+    say(f"layer {name}: T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} h={cfg.h} {cfg.dtype} {mode} {flags}")
     inp = inputs.layer_inputs(cfg)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     t = {n: torch.from_numpy(v).to(DEV).to(dt) for n, v in inp.items()}
     x, wr, w1, w3, w2, dy = (inp[n] for n in ("x", "wr", "w1", "w3", "w2", "dy"))
-    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, DEV)
+    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dt, DEV, **flags)
 
     # --- logits and the unforced routing
     L_ref = ref.router_logits(x, wr)

@@ -152,15 +152,20 @@ def test_mx_quantize_deterministic():
 
 
 LAYER_CASES = [
-    # id, base config, overrides, routing mode
-    ("small_T384", "small", dict(T=384, d=512, h=256), "router"),
-    ("wide_T512_uniform", "wide", dict(T=512, d=256, h=128), "uniform"),
-    ("wide_T512_zipf", "wide", dict(T=512, d=256, h=128), "zipf"),
-    ("trillion_shape", "trillion", dict(T=48, d=256, h=256), "uniform"),
-    ("k_eq_E", "small", dict(T=130, E=4, k=4, d=256, h=128), "router"),
-    ("one_expert", "small", dict(T=200, E=1, k=1, d=128, h=256), "router"),
-    ("T1", "small", dict(T=1, d=128, h=128), "router"),
-    ("tail_split_E4", "small", dict(T=4096, E=4, k=2, d=256, h=128), "tails"),
+    # id, base config, overrides, routing mode, layer flags
+    ("small_T384", "small", dict(T=384, d=512, h=256), "router", {}),
+    ("wide_T512_uniform", "wide", dict(T=512, d=256, h=128), "uniform", {}),
+    ("wide_T512_zipf", "wide", dict(T=512, d=256, h=128), "zipf", {}),
+    ("trillion_shape", "trillion", dict(T=48, d=256, h=256), "uniform", {}),
+    ("k_eq_E", "small", dict(T=130, E=4, k=4, d=256, h=128), "router", {}),
+    ("one_expert", "small", dict(T=200, E=1, k=1, d=128, h=256), "router", {}),
+    ("T1", "small", dict(T=1, d=128, h=128), "router", {}),
+    ("tail_split_E4", "small", dict(T=4096, E=4, k=2, d=256, h=128), "tails", {}),
+    # d not a multiple of the 256-wide tiles (partial N / M tiles)
+    ("d384_router", "small", dict(T=600, d=384, h=256), "router", {}),
+    # memory-lean backward (G and U recomputed from the fp8 copies)
+    ("small_T384_lean", "small", dict(T=384, d=512, h=256), "router", dict(lean=True)),
+    ("wide_T512_zipf_lean", "wide", dict(T=512, d=256, h=128), "zipf", dict(lean=True)),
 ]
 
 
@@ -168,9 +173,9 @@ LAYER_CASES = [
 def test_mx_layer_parity(case):
     from token_routing_grouped_amd.layer import MoELayerGPU
 
-    name, base, over, mode = case
+    name, base, over, mode, flags = case
     cfg = configs.get(base).with_(**over)
-    say(f"mx layer {name}: T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} h={cfg.h} {mode}")
+    say(f"mx layer {name}: T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} h={cfg.h} {mode} {flags}")
     inp = inputs.layer_inputs(cfg)
     t = {n: torch.from_numpy(v).to(DEV).to(torch.bfloat16) for n, v in inp.items()}
     x, wr, w1, w3, w2, dy = (inp[n] for n in ("x", "wr", "w1", "w3", "w2", "dy"))
@@ -180,7 +185,7 @@ def test_mx_layer_parity(case):
         forced = tail_routing(cfg.T, [2098, 1998, 2050, 2046])
     else:
         forced = inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)
-    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, mx=True)
+    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, mx=True, **flags)
     layer.step(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"], forced_idx=torch.from_numpy(forced).to(DEV))
     torch.cuda.synchronize()
     f = mxl.layer_forward_mx(x, wr, w1, w3, w2, cfg.k, forced_idx=forced)

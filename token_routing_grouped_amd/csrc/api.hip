@@ -111,6 +111,15 @@ moe_status_t check_ptrs(const char* fn, std::initializer_list<std::pair<const ch
   return MOE_OK;
 }
 
+// Nullable pointers (not stored when null) must still be 16-byte aligned when
+// given: the epilogues write them in 16-byte pieces.
+moe_status_t check_optional_aligned(const char* fn, std::initializer_list<std::pair<const char*, const void*>> ps) {
+  for (auto& p : ps)
+    if (p.second != nullptr && !aligned16(p.second))
+      return fail(MOE_ERR_ALIGNMENT, "%s: %s is not 16-byte aligned", fn, p.first);
+  return MOE_OK;
+}
+
 moe_status_t check_dt(const char* fn, int dt) {
   if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: dt must be MOE_F32 or MOE_BF16", fn);
   return MOE_OK;
@@ -330,6 +339,7 @@ moe_status_t moe_grouped_gemm_fwd(const void* xp, const void* w1, const void* w3
     return fail(MOE_ERR_UNSUPPORTED, "%s: the memory-lean forward (g or u null) needs bf16", fn);
   if (R == 0) return ok();
   TRY(check_ptrs(fn, {{"xp", xp}, {"hbuf", hbuf}, {"yp", yp}}));
+  TRY(check_optional_aligned(fn, {{"g", g}, {"u", u}}));
   const size_t need = trg::ggemm_ws_bytes(E, R, d, h);
   if (ws == nullptr || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
@@ -526,6 +536,7 @@ moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* a, void* stream) {
   if (a->R == 0) return ok();
   TRY(check_ptrs(fn, {{"xq", a->xq}, {"xs", a->xs}, {"hbuf", a->hbuf}, {"hq", a->hq}, {"hs", a->hs},
                       {"hqT", a->hqT}, {"hsT", a->hsT}, {"yp", a->yp}}));
+  TRY(check_optional_aligned(fn, {{"g", a->g}, {"u", a->u}}));
   TRY(check_device());
   return hip_status(fn, trg::launch_ggemm_fwd_mx(*a, (hipStream_t)stream));
 }
