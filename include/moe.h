@@ -23,7 +23,8 @@
  * ---------------------------
  *  - All pointers are DEVICE pointers unless stated; the caller owns every
  *    buffer.  The library never allocates device memory: scratch comes from a
- *    caller workspace sized by the matching *_workspace_size() call.
+ *    caller workspace sized by the matching *_workspace_size() call (the one
+ *    exception, moe_route_noalloc, uses a fixed static array of the library).
  *  - Every call only enqueues work on `stream` (a hipStream_t; NULL = the null
  *    stream) and returns.  No call copies device data to the host and none
  *    synchronises a stream or the device.  Buffer sizes depend only on
@@ -127,6 +128,24 @@ moe_status_t moe_route(const float* logits, int T, int E, int k, const int32_t* 
                        float* probs, int32_t* topk_idx, float* topk_w, int32_t* counts,
                        int32_t* offsets, int32_t* pos, int32_t* src, int32_t* off128,
                        int32_t* err_flag, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_noalloc: moe_route for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments and results without ws / ws_bytes.  Its
+ * scratch (the per-chunk expert counts) is a static device array of 4 MiB
+ * inside the library, one per GPU, held until the process ends; routings that
+ * need more (ceil(T*k/256) * E * 4 bytes: T*k above 2^18 rows at E = 1024,
+ * above 2^21 at E = 128) are refused with MOE_ERR_WORKSPACE.  The call itself allocates nothing.
+ * Every call on one GPU uses that GPU's array and leaves its contents behind
+ * (each call writes every word it reads first), so calls that overlap on one
+ * GPU -- concurrent streams, or threads enqueueing at once -- race; serialise
+ * them or use moe_route.
+ */
+moe_status_t moe_route_noalloc(const float* logits, int T, int E, int k, const int32_t* forced_idx,
+                               float* probs, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                               int32_t* offsets, int32_t* pos, int32_t* src, int32_t* off128,
+                               int32_t* err_flag, void* stream);
 
 /*
  * moe_permute: rowwise dispatch ("Routing and compute optimisation": routed

@@ -36,6 +36,7 @@ _SIGS = {
     "moe_router_logits": ([_P, _I, _P, _I, _I, _I, _P, _P], _I),
     "moe_route_workspace_size": ([_I, _I, _I], _Z),
     "moe_route": ([_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "moe_route_noalloc": ([_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "moe_permute": ([_P, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_combine": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "moe_combine_bwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P], _I),
@@ -215,6 +216,22 @@ def moe_route(logits, k, probs, topk_idx, topk_w, counts, offsets, pos, src, ws,
     _check(lib().moe_route(_p(logits), T, E, k, _p(forced_idx), _p(probs), _p(topk_idx), _p(topk_w), _p(counts),
                            _p(offsets), _p(pos), _p(src), _p(off128), _p(err_flag), _p(ws), ws.numel(), _stream()),
            "moe_route")
+
+
+def moe_route_noalloc(logits, k, probs, topk_idx, topk_w, counts, offsets, pos, src, off128=None, forced_idx=None,
+                      err_flag=None):
+    """moe_route with the library's own static scratch instead of a workspace
+    (allocates nothing; calls that overlap on one GPU race)."""
+    T, E = logits.shape
+    for t, n, dt in ((logits, "logits", torch.float32), (probs, "probs", torch.float32),
+                     (topk_w, "topk_w", torch.float32), (topk_idx, "topk_idx", torch.int32),
+                     (counts, "counts", torch.int32), (offsets, "offsets", torch.int32), (pos, "pos", torch.int32),
+                     (src, "src", torch.int32), (off128, "off128", torch.int32), (forced_idx, "forced_idx", torch.int32),
+                     (err_flag, "err_flag", torch.int32)):
+        _expect(t, dt, n)
+    _check(lib().moe_route_noalloc(_p(logits), T, E, k, _p(forced_idx), _p(probs), _p(topk_idx), _p(topk_w),
+                                   _p(counts), _p(offsets), _p(pos), _p(src), _p(off128), _p(err_flag), _stream()),
+           "moe_route_noalloc")
 
 
 def moe_permute(x, pos, xp):

@@ -257,6 +257,32 @@ moe_status_t moe_route(const float* logits, int T, int E, int k, const int32_t* 
                                           src, off128, err_flag, ws, (hipStream_t)stream));
 }
 
+moe_status_t moe_route_noalloc(const float* logits, int T, int E, int k, const int32_t* forced_idx, float* probs,
+                               int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* pos,
+                               int32_t* src, int32_t* off128, int32_t* err_flag, void* stream) {
+  const char* fn = "moe_route_noalloc";
+  TRY(check_tk(fn, T, k));
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "%s: k (%d) > E (%d)", fn, k, E);
+  const size_t need = trg::route_ws_bytes(T, E, k);
+  if (need > trg::kRouteScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "%s: this routing needs %zu bytes of scratch (ceil(T*k/256) * E * 4), more than the %zu the library "
+                "holds; use moe_route with a workspace",
+                fn, need, trg::kRouteScratchBytes);
+  if (T > 0)
+    TRY(check_ptrs(fn, {{"logits", logits}, {"probs", probs}, {"topk_idx", topk_idx}, {"topk_w", topk_w},
+                        {"pos", pos}, {"src", src}}));
+  TRY(check_ptrs(fn, {{"counts", counts}, {"offsets", offsets}}));
+  TRY(check_device());
+  void* scratch = nullptr;
+  const hipError_t err = trg::route_scratch(&scratch);
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "%s: scratch address: %s", fn, hipGetErrorString(err));
+  trg::ProfScope ps(fn, (hipStream_t)stream);
+  return hip_status(fn, trg::launch_route(logits, T, E, k, forced_idx, probs, topk_idx, topk_w, counts, offsets, pos,
+                                          src, off128, err_flag, scratch, (hipStream_t)stream));
+}
+
 moe_status_t moe_permute(const void* x, int dt, int T, int d, int k, const int32_t* pos, void* xp, void* stream) {
   const char* fn = "moe_permute";
   TRY(check_dt(fn, dt));

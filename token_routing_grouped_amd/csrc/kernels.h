@@ -12,6 +12,10 @@ namespace trg {
 
 // routing
 size_t route_ws_bytes(int T, int E, int k);
+// moe_route_noalloc: largest routing workspace its static scratch array holds
+constexpr size_t kRouteScratchBytes = 4u << 20;
+// device address of that array on the current device (resolved once per device)
+hipError_t route_scratch(void** out);
 hipError_t launch_route(const float* logits, int T, int E, int k, const int* forced, float* probs, int* idx,
                         float* w, int* counts, int* offsets, int* pos, int* src, int* off128, int* err_flag,
                         void* ws, hipStream_t s);

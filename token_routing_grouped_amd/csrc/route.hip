@@ -11,6 +11,8 @@
 //                offsets, off128
 //   route_rank   one wave per chunk: rank of each entry among equal experts in
 //                (token, slot) order via LDS match masks + popcount
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -250,6 +252,36 @@ __global__ __launch_bounds__(64) void route_rank_kernel(const int* __restrict__ 
       src[p] = (int)i;
     }
   }
+}
+
+// ---- scratch for the entry point that allocates nothing (moe_route_noalloc)
+// The per-chunk counts live in this file-scope device array instead of a
+// caller workspace.  Every GPU that loads the library holds its own copy until
+// the process ends; host code never uses the symbol itself (on the host it is
+// only a stand-in), but the per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) int scratch[kRouteScratchBytes / sizeof(int)];
+
+namespace {
+constexpr int kMaxScratchDev = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDev];  // device address of `scratch` per device, once resolved
+}  // namespace
+
+hipError_t route_scratch(void** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxScratchDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 size_t route_ws_bytes(int T, int E, int k) {
