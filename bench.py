@@ -114,7 +114,13 @@ def cpu_baseline(cfg, mode, sample_T, min_seconds=10.0):
     if mode != "router":
         forced = inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)[:sample_T]
     args = (inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"])
-    fwd, bwd = (mxl.layer_forward_mx, mxl.layer_backward_mx) if cfg.mx else (ref.layer_forward, ref.layer_backward)
+    if cfg.mx:  # the MXFP8 oracle computes in float64 only
+        prec = "float64"
+        fwd, bwd = mxl.layer_forward_mx, mxl.layer_backward_mx
+    else:  # the float oracle run in fp32, the precision the layer accumulates in
+        prec = "float32"
+        fwd = lambda *a, **kw: ref.layer_forward(*a, dtype=np.float32, **kw)
+        bwd = lambda *a, **kw: ref.layer_backward(*a, dtype=np.float32, **kw)
     times = []
     while True:  # repeat the same sample until ~10 s of CPU work (at most 20 runs)
         t0 = time.perf_counter()
@@ -125,10 +131,88 @@ def cpu_baseline(cfg, mode, sample_T, min_seconds=10.0):
             break
     el = float(np.median(times))
     return {"value": sample_T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"first {sample_T} of {cfg.T} tokens, all {cfg.E} experts, full d={cfg.d} h={cfg.h}; "
-                      f"float64 numpy {'MXFP8 (quantise-dequantise) ' if cfg.mx else ''}fwd+bwd, median of "
-                      f"{len(times)} runs ({sum(times):.1f} s total) on {cpu_model()}",
+                      f"{prec} numpy {'MXFP8 (quantise-dequantise) ' if cfg.mx else ''}fwd+bwd, median of "
+                      f"{len(times)} runs ({sum(times):.1f} s total), BLAS on {threads} threads of "
+                      f"{os.cpu_count()} host CPUs ({cpu_model()})",
             "seconds_per_run": el}
+
+
+def plain_ms_per_step(layer, args, forced, steps, warmup):
+    """Milliseconds per step of `steps` back-to-back steps with no events at all
+    (wall clock around the loop), and the median of one event pair per step."""
+    import numpy as np
+    import torch
+
+    for _ in range(warmup):
+        layer.step(*args, forced_idx=forced)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.step(*args, forced_idx=forced)
+    torch.cuda.synchronize()
+    wall = 1000.0 * (time.perf_counter() - t0) / steps
+    pairs = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer.step(*args, forced_idx=forced)
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return {"ms_per_step": wall, "median_ms": float(np.median([x.elapsed_time(y) for x, y in pairs]))}
+
+
+def gate_runs(small_tensors, small_ms, steps, warmup, dev):
+    """The layer at the other gated shapes, in the same process: the wide
+    128-expert layer in bf16 and MXFP8, and the small layer in MXFP8 (its inputs
+    are the small bf16 layer's, so MXFP8 and bf16 are value-matched at each
+    shape).  Returns ms per step and the two gate checks: the layer's share of
+    the bf16 MFMA peak, and MXFP8 faster than bf16 at the same shape."""
+    import torch
+
+    from token_routing_grouped_amd import configs, inputs
+    from token_routing_grouped_amd.layer import MoELayerGPU
+
+    out = {}
+    small = configs.get("small")
+    for slug in ("mxfp8_small", "wide", "mxfp8"):
+        cfg = configs.get(slug)
+        if (cfg.T, cfg.d, cfg.E) == (small.T, small.d, small.E):
+            t = small_tensors
+        else:
+            if "wide_tensors" not in out:
+                log(f"bench: gate inputs for {cfg.T}x{cfg.d}, {cfg.E} experts")
+                out["wide_tensors"] = inputs.device_inputs(cfg, dev)[0]
+            t = out["wide_tensors"]
+        layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, dev, mx=cfg.mx, overlap=cfg.overlap)
+        args = (t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])
+        r = plain_ms_per_step(layer, args, None, steps, warmup)
+        r["tokens_per_s"] = cfg.T / (r["ms_per_step"] * 1e-3)
+        r["layer_tflops"] = (cfg.gemm_flops() + cfg.router_flops()) / (r["ms_per_step"] * 1e-3) / 1e12
+        r["streams"] = 2 if layer.overlap else 1
+        out[slug] = r
+        del layer
+        torch.cuda.empty_cache()
+        log(f"bench: gate {slug}: {r['ms_per_step']:.3f} ms/step")
+    out.pop("wide_tensors", None)
+    wide = configs.get("wide")
+    sm_fl = small.gemm_flops() + small.router_flops()
+    wd_fl = wide.gemm_flops() + wide.router_flops()
+    return {
+        "ms_per_step": {"small_bf16": small_ms, "small_mxfp8": out["mxfp8_small"]["ms_per_step"],
+                        "wide_bf16": out["wide"]["ms_per_step"], "wide_mxfp8": out["mxfp8"]["ms_per_step"]},
+        "median_ms": {"small_mxfp8": out["mxfp8_small"]["median_ms"], "wide_bf16": out["wide"]["median_ms"],
+                      "wide_mxfp8": out["mxfp8"]["median_ms"]},
+        "layer_frac_bf16_peak": {"small": sm_fl / (small_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                 "wide": wd_fl / (out["wide"]["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "mxfp8_faster_than_bf16": {"small": out["mxfp8_small"]["ms_per_step"] < small_ms,
+                                   "wide": out["mxfp8"]["ms_per_step"] < out["wide"]["ms_per_step"]},
+        "note": "ms_per_step: wall clock of back-to-back steps with no events, each workload's default "
+                "stream schedule, router routing, same process and inputs as above (wide and MXFP8-wide share "
+                "one input set, small and MXFP8-small another)",
+    }
 
 
 def copy_probe(nbytes=1 << 30, reps=5):
@@ -164,6 +248,9 @@ def main():
                     help="memory-lean backward: G and U are not stored by the forward but recomputed")
     ap.add_argument("--aux-alpha", type=float, default=0.0,
                     help="include the router balance loss (weight alpha) in every timed step")
+    ap.add_argument("--no-gates", action="store_true",
+                    help="skip the extra runs of the other gated shapes (wide bf16, MXFP8 small and wide) that "
+                         "the default workload reports next to its own line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
@@ -341,6 +428,8 @@ def main():
                    "note": "bytes the layer keeps from the forward to the backward (routing metadata, inputs and "
                            "weights excluded)"},
     }
+    if cfg.slug == "small" and mode == "router" and not (a.no_gates or a.lean or a.aux_alpha or a.serial or a.overlap):
+        out["gates"] = gate_runs(t, out["ms_per_step_no_events"], a.steps, a.warmup, dev)
     if not a.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(cfg, mode, min(a.cpu_sample_tokens, cfg.T))
