@@ -301,11 +301,19 @@ moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, con
  * exponent bits (s = -127 for an all-zero block), scale byte s + 127,
  * elements E4M3FN(v / 2^s) rounded to nearest even and saturated to +-448,
  * sign of zero kept.  Layouts:
- *   rowwise      q [rows, cols] u8, s [rows, cols/32] u8 (blocks along cols)
- *   columnwise   q [cols, ldc] u8, s [cols, ldc/32] u8: blocks of 32
- *                consecutive rows inside each row segment, the last block of
- *                a segment zero-padded; segment e starts at column off128[e]
- *                (the transpose of the rowwise form of each padded segment)
+ *   rowwise      q [rows, cols] u8 (blocks along cols)
+ *   columnwise   q [cols, ldc] u8: blocks of 32 consecutive rows inside each
+ *                row segment, the last block of a segment zero-padded;
+ *                segment e starts at column off128[e] (the transpose of the
+ *                rowwise form of each padded segment)
+ *   scales       K-chunk major: for an MX matrix of n rows (rowwise: rows;
+ *                columnwise: cols) with K values per row (rowwise: cols;
+ *                columnwise: ldc), the scale of block b (K values 32b ..
+ *                32b+31) of row r is byte (b/4 * n + r) * 4 + b%4, i.e.
+ *                [ceil(K/128)][n][4] bytes: the four scales of a 128-wide
+ *                K chunk of a row form one dword, and one chunk's dwords of
+ *                consecutive rows are contiguous (a GEMM K step of 128 reads
+ *                its tile's scales in one piece)
  * ---------------------------------------------------------------------------
  *
  * mx_quantize: quantise `rows` rows of a [*, cols] matrix `in` (dt = MOE_BF16
@@ -317,9 +325,11 @@ moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, con
  *     starts: multiples of 32, each padded segment at least as long as its
  *     segment and at most 127 rows longer (moe_route's offsets / off128); if null, segments of seg_rows rows
  *     (rows a multiple of seg_rows, or seg_rows = rows), each padded to 32.
- *   q_row/s_row (nullable): rowwise output.  q_col/s_col (nullable): columnwise
- *     output with row stride ldc (a multiple of 32, at least the padded row
- *     count: rows + 127*nseg with seg_off, else segments x round32(seg_rows)).
+ *   q_row/s_row (nullable): rowwise output; s_row holds ceil(cols/128) * rows
+ *     * 4 bytes.  q_col/s_col (nullable): columnwise output with row stride ldc
+ *     (a multiple of 32, at least the padded row count: rows + 127*nseg with
+ *     seg_off, else segments x round32(seg_rows)); s_col holds ceil(ldc/128) *
+ *     cols * 4 bytes.
  * cols must be a multiple of 32.  Bit-exact and deterministic.
  */
 moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32_t* gather_src, int gather_k,
@@ -331,7 +341,10 @@ moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32
  * as moe_grouped_gemm_fwd / _bwd, with every GEMM operand quantised along its
  * own reduction dimension and multiplied on gfx950's scaled matrix cores
  * (fp32 accumulation, bf16 outputs).  d and h must be multiples of 128; rcap
- * (row stride of every columnwise copy) a multiple of 128 and >= R + 127*E.
+ * (row stride of every columnwise copy) a multiple of 128 and >= R + 127*E;
+ * off128 as moe_route writes it (segment starts on multiples of 128).  Scale
+ * arrays are in the K-chunk-major layout above; with d, h and rcap multiples
+ * of 128 each holds exactly (values)/32 bytes, e.g. xs = R*d/32.
  * The caller quantises x (mx_quantize with gather) and the weights; the calls
  * quantise H, dYp and dG|dU themselves (both layouts, from the stored bf16
  * values).  ws: moe_grouped_gemm_workspace_size() bytes.

@@ -46,3 +46,16 @@ def to_np(t):
 
 def say(*a):
     print(*a, flush=True)
+
+
+def mx_scale_bytes(rows, K):
+    """Bytes of an MX scale array in the library's K-chunk-major layout."""
+    return -(-K // 128) * rows * 4
+
+
+def mx_scales_to_rows(buf, rows, K):
+    """The library's K-chunk-major scale bytes (block b of row r at byte
+    (b // 4 * rows + r) * 4 + b % 4) as a [rows, K/32] array, the layout the
+    oracle uses.  A pure re-indexing."""
+    a = np.asarray(buf).reshape(-1)[:mx_scale_bytes(rows, K)].reshape(-(-K // 128), rows, 4)
+    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(rows, -1)[:, :K // 32])

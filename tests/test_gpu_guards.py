@@ -36,7 +36,6 @@ ROUTING = ["logits", "probs", "topk_idx", "topk_w", "counts", "offsets", "off128
 FLOAT_OUT = ["g", "u", "hb", "yp", "y", "dyp", "dgate", "dgu", "dxp", "dx", "dwr", "dw1", "dw3", "dw2"]
 MX_BUFS = ["xq", "xs", "xqT", "xsT", "w1q", "w1s", "w1tq", "w1ts", "w3q", "w3s", "w3tq", "w3ts", "w2q", "w2s",
            "w2tq", "w2ts", "hq", "hs", "hqT", "hsT", "dyq", "dys", "dyqT", "dysT", "dguq", "dgus", "dguqT", "dgusT"]
-MX_COL = {"xqT": 1, "hqT": 1, "dyqT": 1, "dguqT": 1, "xsT": 32, "hsT": 32, "dysT": 32, "dgusT": 32}
 WORKSPACES = ["ws_route", "ws_gemm", "ws_router", "ws_balance"]
 
 
@@ -129,7 +128,10 @@ def test_step_writes_only_its_buffers(case):
         assert (getattr(layer, n) >= 0).all(), f"{n}: entries left unwritten"
     if flags.get("mx"):
         end = int(layer.off128[-1].item())
-        for n, per in MX_COL.items():
-            tail = getattr(layer, n)[:, end // per:]
-            assert (tail == 0xEE).all(), f"{n}: written past the last padded segment"
+        for n in ("xqT", "hqT", "dyqT", "dguqT"):  # payload [cols, rcap]
+            assert (getattr(layer, n)[:, end:] == 0xEE).all(), f"{n}: written past the last padded segment"
+        for n in ("xsT", "hsT", "dysT", "dgusT"):  # scales, K-chunk major: [rcap/128][cols][4]
+            buf = getattr(layer, n)
+            cols = buf.shape[0]
+            assert (buf.reshape(-1)[end // 128 * cols * 4:] == 0xEE).all(), f"{n}: written past the last segment"
     say(f"  {len(guards)} buffers guarded, expert rows {counts.tolist()[:16]}")

@@ -18,7 +18,7 @@ from oracle import moe_ref as ref
 from oracle import mx_ref as mx
 from token_routing_grouped_amd import configs, inputs
 
-from helpers import rel_l2, say, tail_routing, to_np
+from helpers import mx_scale_bytes, mx_scales_to_rows, rel_l2, say, tail_routing, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -39,10 +39,10 @@ def _rowwise(a_f32, dt=torch.bfloat16):
     from token_routing_grouped_amd import _abi
 
     rows, cols = a_f32.shape
-    q, s = _u8(rows, cols), _u8(rows, cols // 32)
+    q, s = _u8(rows, cols), _u8(mx_scale_bytes(rows, cols))
     _abi.mx_quantize(_dev(a_f32, dt), rows, q, s, seg_rows=rows)
     torch.cuda.synchronize()
-    return q.cpu().numpy(), s.cpu().numpy()
+    return q.cpu().numpy(), mx_scales_to_rows(s.cpu().numpy(), rows, cols)
 
 
 def _hand_cases():
@@ -114,18 +114,18 @@ def test_mx_quantize_gather_both_layouts(T, E, k, cols, mode):
     x = _special_matrix(T, cols, 3 * T)
     R = T * k
     rc = (R + 127 * E + 127) // 128 * 128
-    q, s, qT, sT = _u8(R, cols), _u8(R, cols // 32), _u8(cols, rc), _u8(cols, rc // 32)
+    q, s, qT, sT = _u8(R, cols), _u8(mx_scale_bytes(R, cols)), _u8(cols, rc), _u8(mx_scale_bytes(cols, rc))
     i32 = lambda a: _dev(np.asarray(a, np.int32), torch.int32)
     _abi.mx_quantize(_dev(x, torch.bfloat16), R, q, s, qT, sT, gather_src=i32(rt["src"]), gather_k=k,
                      seg_off=i32(rt["offsets"]), seg_off128=i32(rt["off128"]))
     torch.cuda.synchronize()
     xp = ref.permute(x, rt["pos"])
     rq, rs = mx.quantize_rows(xp)
-    assert (q.cpu().numpy() == rq).all() and (s.cpu().numpy() == rs).all()
+    assert (q.cpu().numpy() == rq).all() and (mx_scales_to_rows(s.cpu().numpy(), R, cols) == rs).all()
     cq, cs = mx.quantize_cols_segmented(xp, rt["offsets"], rt["off128"])
     R32 = int(rt["off128"][-1])
     assert (qT.cpu().numpy()[:, :R32] == cq).all()
-    assert (sT.cpu().numpy()[:, :R32 // 32] == cs).all()
+    assert (mx_scales_to_rows(sT.cpu().numpy(), cols, rc)[:, :R32 // 32] == cs).all()
 
 
 def test_mx_quantize_fixed_segments():
@@ -134,14 +134,14 @@ def test_mx_quantize_fixed_segments():
 
     E, h, d = 3, 96, 160
     w = _special_matrix(E * h, d, 5)
-    q, s, qT, sT = _u8(E * h, d), _u8(E * h, d // 32), _u8(d, E * h), _u8(d, E * h // 32)
+    q, s, qT, sT = _u8(E * h, d), _u8(mx_scale_bytes(E * h, d)), _u8(d, E * h), _u8(mx_scale_bytes(d, E * h))
     _abi.mx_quantize(_dev(w, torch.bfloat16), E * h, q, s, qT, sT, seg_rows=h)
     torch.cuda.synchronize()
     rq, rs = mx.quantize_rows(w)
-    assert (q.cpu().numpy() == rq).all() and (s.cpu().numpy() == rs).all()
+    assert (q.cpu().numpy() == rq).all() and (mx_scales_to_rows(s.cpu().numpy(), E * h, d) == rs).all()
     off = np.arange(E + 1) * h
     cq, cs = mx.quantize_cols_segmented(w, off, off)
-    assert (qT.cpu().numpy() == cq).all() and (sT.cpu().numpy() == cs).all()
+    assert (qT.cpu().numpy() == cq).all() and (mx_scales_to_rows(sT.cpu().numpy(), d, E * h) == cs).all()
 
 
 def test_mx_quantize_deterministic():

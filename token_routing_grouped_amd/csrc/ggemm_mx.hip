@@ -20,10 +20,14 @@
 //     its scale register covers the 32-wide block h of its row (probed on the
 //     hardware).  Each K step's scale words are staged in LDS with its
 //     operands.
-//   * K is a multiple of 128 on the ragged-M side (the call requires d and h
-//     to be); the weight gradients' K segments are multiples of 32, and their
-//     tails are masked per 32-wide block: the block's data is zeroed and its
-//     scale set to 1.
+//   * K is a multiple of 128 everywhere: the ragged-M side because the call
+//     requires d and h to be, the weight gradients because their K segments
+//     are the experts' 128-padded column segments (off128), whose padding
+//     blocks the quantiser fills with zeros.
+//   * Scales are stored K-chunk major (mx.hip): one K step's scale dwords for
+//     256 consecutive rows are 1 KiB of contiguous memory, which one wave
+//     moves into LDS with a single 16-byte-per-lane load.  (Loaded a dword per
+//     row, 64 rows per instruction, they cost every MX GEMM 5-25% of its time.)
 #include "ggemm_impl.h"
 
 namespace trg {
@@ -32,12 +36,16 @@ namespace gg {
 typedef int v8i32_t __attribute__((ext_vector_type(8)));
 typedef int v4i32_t __attribute__((ext_vector_type(4)));
 
+// Scale operands in the K-chunk-major layout: the dword of row r and K chunk
+// c (128 values) is at base + c * step + 4 r.
 struct MxArgs {
-  const uint8_t* sA;  // A scales: row r at sA + r*lds_a (+ the K block)
-  long lds_a;
-  const uint8_t* sB;  // B scales, per expert + e*sb_es
-  const uint8_t* sB2;
-  long lds_b, sb_es;
+  const uint8_t* sA;   // A scales
+  long sa_step;        // bytes per K chunk of A (4 x A's rows)
+  const uint8_t* sB;   // B scales (GLU: W1; KSPLIT: the first K half)
+  const uint8_t* sB2;  // GLU: W3; KSPLIT: the second K half
+  long sb_step;        // bytes per K chunk of B
+  int sb_row_es;       // B scale rows per expert (forward weights: N rows each)
+  int sb_k_es;         // B K values per expert (dgrad weights: experts side by side along K)
   long sA_bytes, sB_bytes;  // extents (bounds for the scale loads)
 };
 
@@ -62,17 +70,13 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
   constexpr int STAGE = SA + SB;
   static_assert(BM % 128 == 0 && BN % 128 == 0, "tile");
   static_assert(BSEL != BSEL_GLU || (TN % 2 == 0), "GLU pairs subtiles");
-  // Each K step's scale words are staged in LDS next to its operands: the
-  // step's four 32-blocks of every A row and every B row, loaded once per
-  // workgroup by one 64-row chunk per wave.  Ragged-M steps start on a 4-block
-  // boundary (one dword per row); ragged-K steps start at the expert's
-  // 32-block offset, so two dwords per row are staged ([low words][high
-  // words]) and aligned at read time by a byte shift that is the same for the
-  // whole tile.
-  constexpr bool KTAIL = MODE == RAGGED_K;
-  constexpr int SCW = KTAIL ? 2 : 1;
-  constexpr int SCB = (BM + BN) * 4 * SCW;
-  static_assert((BM + BN) / 64 <= WM * WN, "one scale chunk per wave");
+  // Each K step's scale dwords are staged in LDS next to its operands: 256
+  // rows of A, 256 rows of B and, for the GLU B, 256 rows of W3 (1 KiB each,
+  // one wave each; a 128-row operand reads 128 rows past its own, which it
+  // ignores).
+  constexpr int NSC = BSEL == BSEL_GLU ? 3 : 2;
+  constexpr int SCB = NSC * 1024;
+  static_assert(NSC <= WM * WN && BM <= 256 && BN <= 256, "one scale piece per wave");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 2 * SCB];
 
   const uint8_t* A = (const uint8_t*)g.A;
@@ -99,6 +103,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
   const __amdgpu_buffer_rsrc_t rsSA = make_rsrc(x.sA, x.sA_bytes);
   const __amdgpu_buffer_rsrc_t rsSB = make_rsrc(x.sB, x.sB_bytes);
   const __amdgpu_buffer_rsrc_t rsSB2 = make_rsrc(BSEL != BSEL_NONE ? x.sB2 : x.sB, x.sB_bytes);
+  static_assert(MODE == RAGGED_M || BSEL == BSEL_NONE, "weight gradients have one B");
   const int a_lane[2] = {kc_lane_off(lane, 0, (int)g.lda), kc_lane_off(lane, 1, (int)g.lda)};
   const int b_lane[2] = {kc_lane_off(lane, 0, (int)g.ldb), kc_lane_off(lane, 1, (int)g.ldb)};
 
@@ -171,61 +176,42 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
     }
   };
 
-  // LDS scale rows of a stage: [A rows BM][B rows BN]; GLU B rows are [W1
-  // half][W3 half] (each wave chunk reads from one of them).
+  // LDS scale pieces of a stage: [A 256 rows][B 256 rows][W3 256 rows (GLU)],
+  // each the step's K chunk of consecutive rows (one wave, one 1 KiB load).
   auto issue_scales = [&](const Tile& c, int kt, int stage) {
-    char* dst = smem + 2 * STAGE + stage * SCB + wave * 256;
-    const int p = wave * 64 + lane;  // scale row of this lane
-    if constexpr (KTAIL) {
-      const int blk = ((c.k0 + kt) >> 5) & ~3;  // dword holding the step's first block
-      if (wave * 64 < BM) {
-        const int off = (c.m0 + p) * (int)x.lds_a + blk;
-        lds_load4(rsSA, dst, off);
-        lds_load4(rsSA, dst + (BM + BN) * 4, off + 4);
-      } else if (wave * 64 < BM + BN) {
-        const int off = (c.n0 + p - BM) * (int)x.lds_b + blk;
-        lds_load4(rsSB, dst, off);
-        lds_load4(rsSB, dst + (BM + BN) * 4, off + 4);
-      }
+    if (wave >= NSC) return;
+    char* dst = smem + 2 * STAGE + stage * SCB + wave * 1024;
+    if (wave == 0) {  // A rows m0.. of chunk (k0 + kt) / 128 (k0 = 0 on the ragged-M side)
+      lds_load16(rsSA, dst, (int)(((c.k0 + kt) >> 7) * x.sa_step) + c.m0 * 4 + lane * 16);
     } else {
-      if (wave * 64 < BM) {
-        lds_load4(rsSA, dst, (c.m0 + p) * (int)x.lds_a + (kt >> 5));
-      } else if (wave * 64 < BM + BN) {
-        const int q = p - BM;
-        if constexpr (BSEL == BSEL_GLU) {
-          const bool w3 = (wave * 64 - BM) >= BN / 2;
-          const int hh = c.n0 / 2 + q - (w3 ? BN / 2 : 0);
-          lds_load4(w3 ? rsSB2 : rsSB, dst, (int)(c.e * x.sb_es) + hh * (int)x.lds_b + (kt >> 5));
-        } else if constexpr (BSEL == BSEL_KSPLIT) {
-          const bool second = kt >= g.split;
-          lds_load4(second ? rsSB2 : rsSB, dst,
-                    (int)(c.e * x.sb_es) + (c.n0 + q) * (int)x.lds_b + ((second ? kt - g.split : kt) >> 5));
-        } else {
-          lds_load4(rsSB, dst, (int)(c.e * x.sb_es) + (c.n0 + q) * (int)x.lds_b + (kt >> 5));
-        }
+      int ktb = c.k0 + kt, row0 = c.n0;
+      bool second = false;
+      if constexpr (BSEL == BSEL_GLU) {
+        second = wave == 2;  // W3 next to W1, the same hidden units
+        row0 = c.n0 / 2;
+      } else if constexpr (BSEL == BSEL_KSPLIT) {
+        second = kt >= g.split;
+        if (second) ktb -= g.split;
       }
+      const long off = ((long)(c.e * x.sb_k_es + ktb) >> 7) * x.sb_step + ((long)c.e * x.sb_row_es + row0) * 4;
+      lds_load16(second ? rsSB2 : rsSB, dst, (int)off + lane * 16);
     }
   };
   // this lane's scale words of the step in `stage`, pre-shifted so that byte
   // 0 / byte 2 are the lane's blocks of slice 0 / slice 1
-  auto lds_scales = [&](int stage, int shift, uint32_t(&sa)[TM], uint32_t(&sb)[TN]) {
+  auto lds_scales = [&](int stage, uint32_t(&sa)[TM], uint32_t(&sb)[TN]) {
     const char* sc = smem + 2 * STAGE + stage * SCB;
     const int l32 = lane & 31;
-    auto word = [&](int row) -> uint32_t {
-      const uint32_t lo = *(const uint32_t*)(sc + row * 4);
-      if constexpr (KTAIL) return __builtin_amdgcn_alignbyte(*(const uint32_t*)(sc + (BM + BN + row) * 4), lo, shift);
-      else return lo;
-    };
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] = word(wm * WTM + i * 32 + l32) >> (8 * half);
+    for (int i = 0; i < TM; ++i) sa[i] = *(const uint32_t*)(sc + (wm * WTM + i * 32 + l32) * 4) >> (8 * half);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      int row;
+      int off;
       if constexpr (BSEL == BSEL_GLU)
-        row = (j < TN / 2 ? 0 : BN / 2) + wn * (WTN / 2) + (j % (TN / 2)) * 32 + l32;
+        off = (j < TN / 2 ? 1024 : 2048) + (wn * (WTN / 2) + (j % (TN / 2)) * 32 + l32) * 4;
       else
-        row = wn * WTN + j * 32 + l32;
-      sb[j] = word(BM + row) >> (8 * half);
+        off = 1024 + (wn * WTN + j * 32 + l32) * 4;
+      sb[j] = *(const uint32_t*)(sc + off) >> (8 * half);
     }
   };
 
@@ -260,7 +246,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
     for (int it = 0; it < nk; ++it) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // stage it&1 and this step's scales are in; stage (it+1)&1 is free
-      lds_scales(it & 1, KTAIL ? (cur.k0 >> 5) & 3 : 0, sa, sb);  // K steps are 4 blocks: same shift throughout
+      lds_scales(it & 1, sa, sb);
       if (it + 1 < nk) {
         issue_scales(cur, (it + 1) * BK, (it + 1) & 1);
         issue(cur, (it + 1) * BK, (it + 1) & 1);
@@ -281,34 +267,14 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
         constexpr int kk = decltype(KK)::value;
         constexpr bool last = kk + 1 == BK / 64;
         __builtin_amdgcn_sched_barrier(0);
-        const int kb = kt + kk * 64;  // first k of the slice
-        // block validity of the slice's two 32-wide blocks (uniform)
-        const bool v0 = kb < cur.klen, v1 = kb + 32 < cur.klen;
-        if constexpr (MODE == RAGGED_K) {  // K tail: zero the invalid block(s) of every fragment
-          // (branch-free: a conditional rewrite would keep two copies of the
-          // fragments alive)
-          const int m0v = v0 ? -1 : 0, m1v = v1 ? -1 : 0;
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int z = 0; z < 8; ++z) af[i][z] &= z < 4 ? m0v : m1v;
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int z = 0; z < 8; ++z) bfr[j][z] &= z < 4 ? m0v : m1v;
-        }
-        // ragged-M K is a multiple of 128: only the weight gradients have tails
-        const bool lane_ok = MODE == RAGGED_M || (half ? v1 : v0);  // this lane's scale block
         static_for<TM>([&](auto I) {
           constexpr int i = decltype(I)::value;
           const bool row_ok = i < nv;  // uniform: only an expert's tail tile skips
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const int sA_ = lane_ok ? (int)sa[i] : 127 << (16 * kk);
-            const int sB_ = lane_ok ? (int)sb[j] : 127 << (16 * kk);
             if (row_ok)
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 2 * kk,
-                                                                           sB_, 2 * kk, sA_);
+                                                                           (int)sb[j], 2 * kk, (int)sa[i]);
             if constexpr (!last && i == TM - 1) {
               __builtin_amdgcn_sched_barrier(0);
               bfr[j] = frag_mx(sB, wn * WTN + j * 32, kk + 1, lane);
@@ -367,8 +333,8 @@ static void mx_up_bm(const char* name, const MxFwd& p, void* gq, void* u, void* 
   a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
   a.tiles_n = cdiv(2L * h, 256);
   MxArgs x{};
-  x.sA = p.xs; x.lds_a = d / 32; x.sA_bytes = (long)R * (d / 32);
-  x.sB = p.w1s; x.sB2 = p.w3s; x.lds_b = d / 32; x.sb_es = (long)h * (d / 32); x.sB_bytes = (long)E * h * (d / 32);
+  x.sA = p.xs; x.sa_step = 4L * R; x.sA_bytes = (long)R * (d / 32);
+  x.sB = p.w1s; x.sB2 = p.w3s; x.sb_step = 4L * E * h; x.sb_row_es = h; x.sB_bytes = (long)E * h * (d / 32);
   run_mx<BM, 256, RAGGED_M, BSEL_GLU, CSEL_NONE, EPI_SWIGLU_FWD>(name, a, x, mt_max * a.tiles_n, s);
 }
 
@@ -401,8 +367,8 @@ static hipError_t mx_fwd_bm(const MxFwd& p, const int* tile_off, hipStream_t s) 
     a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
     a.tiles_n = cdiv(d, 256);
     MxArgs x{};
-    x.sA = p.hs; x.lds_a = h / 32; x.sA_bytes = (long)R * (h / 32);
-    x.sB = p.w2s; x.lds_b = h / 32; x.sb_es = (long)d * (h / 32); x.sB_bytes = (long)E * d * (h / 32);
+    x.sA = p.hs; x.sa_step = 4L * R; x.sA_bytes = (long)R * (h / 32);
+    x.sB = p.w2s; x.sb_step = 4L * E * d; x.sb_row_es = d; x.sB_bytes = (long)E * d * (h / 32);
     run_mx<BM, 256, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_mx_down", a, x, mt_max * a.tiles_n, s);
   }
   return hipGetLastError();
@@ -433,8 +399,8 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, unsigned part
     a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
     a.tiles_n = cdiv(h, 256);
     MxArgs x{};
-    x.sA = p.dys; x.lds_a = d / 32; x.sA_bytes = (long)R * (d / 32);
-    x.sB = p.w2ts; x.lds_b = (long)E * d / 32; x.sb_es = d / 32; x.sB_bytes = (long)h * E * d / 32;
+    x.sA = p.dys; x.sa_step = 4L * R; x.sA_bytes = (long)R * (d / 32);
+    x.sB = p.w2ts; x.sb_step = 4L * h; x.sb_k_es = d; x.sB_bytes = (long)h * E * d / 32;
     run_mx<BM, 256, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_SWIGLU_BWD>("ggemm_mx_dgrad_down_swiglu", a, x,
                                                                     mt_max * a.tiles_n, s);
   }
@@ -453,8 +419,8 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, unsigned part
     a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
     a.tiles_n = cdiv(d, 256);
     MxArgs x{};
-    x.sA = p.dgus; x.lds_a = 2 * h / 32; x.sA_bytes = (long)R * (2 * h / 32);
-    x.sB = p.w1ts; x.sB2 = p.w3ts; x.lds_b = (long)E * h / 32; x.sb_es = h / 32; x.sB_bytes = (long)d * E * h / 32;
+    x.sA = p.dgus; x.sa_step = 4L * R; x.sA_bytes = (long)R * (2 * h / 32);
+    x.sB = p.w1ts; x.sB2 = p.w3ts; x.sb_step = 4L * d; x.sb_k_es = h; x.sB_bytes = (long)d * E * h / 32;
     run_mx<BM, 256, RAGGED_M, BSEL_KSPLIT, CSEL_NONE, EPI_BF16>("ggemm_mx_dgrad_up", a, x, mt_max * a.tiles_n, s);
   }
   return hipGetLastError();
@@ -490,8 +456,8 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s) {
     a.offsets = p.off128; a.work = work; a.E = E; a.R = R;
     a.tiles_m = cdiv(d, 256); a.tiles_n = cdiv(h, 256);
     MxArgs x{};
-    x.sA = p.dysT; x.lds_a = sc; x.sA_bytes = (long)d * sc;
-    x.sB = p.hsT; x.lds_b = sc; x.sB_bytes = (long)h * sc;
+    x.sA = p.dysT; x.sa_step = 4L * d; x.sA_bytes = (long)d * sc;
+    x.sB = p.hsT; x.sb_step = 4L * h; x.sB_bytes = (long)h * sc;
     run_mx<256, 256, RAGGED_K, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_mx_wgrad_down", a, x, E * a.tiles_m * a.tiles_n,
                                                                s);
   }
@@ -504,8 +470,8 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s) {
     a.offsets = p.off128; a.work = work; a.E = E; a.R = R;
     a.tiles_m = cdiv(2L * h, 256); a.tiles_n = cdiv(d, 256);
     MxArgs x{};
-    x.sA = p.dgusT; x.lds_a = sc; x.sA_bytes = (long)2 * h * sc;
-    x.sB = p.xsT; x.lds_b = sc; x.sB_bytes = (long)d * sc;
+    x.sA = p.dgusT; x.sa_step = 8L * h; x.sA_bytes = (long)2 * h * sc;
+    x.sB = p.xsT; x.sb_step = 4L * d; x.sB_bytes = (long)d * sc;
     run_mx<256, 256, RAGGED_K, BSEL_NONE, CSEL_MSPLIT, EPI_BF16>("ggemm_mx_wgrad_up", a, x,
                                                                  E * a.tiles_m * a.tiles_n, s);
   }

@@ -11,12 +11,17 @@
 //
 // One kernel writes both layouts a MoE layer needs from a single read of the
 // source:
-//   row layout      q_row [rows, cols], s_row [rows, cols/32]      (blocks
+//   row layout      q_row [rows, cols]                             (blocks
 //                   along the columns: the forward and dgrad K);
-//   column layout   q_col [cols, ldc], s_col [cols, ldc/32]        (blocks of
+//   column layout   q_col [cols, ldc]                              (blocks of
 //                   32 consecutive rows inside each segment, zero-padded at
 //                   the segment's end; segment e starts at column off128[e]:
 //                   the weight-gradient K).
+// Scale bytes are stored K-chunk major: the scale of block b (of 32 values
+// along K) of row r of an n-row MX matrix is byte (b / 4 * n + r) * 4 + b % 4,
+// so the four scales of one 128-wide K chunk of a row form one dword and the
+// chunk's dwords of consecutive rows are contiguous: a GEMM K step of 128
+// reads its tile's scales as one piece instead of a dword per row.
 // Rows can be gathered on the fly (row r reads in[src[r] / k]), which fuses
 // the rowwise dispatch of the layer input into its quantisation.
 #include "common.h"
@@ -118,10 +123,10 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
   const int ncb = (cols + kMxCols - 1) / kMxCols;
   const int base = (int)(blockIdx.x / ncb) * kMxRows;
   const int col0 = (int)(blockIdx.x % ncb) * kMxCols;
-  // whole scale dwords: the row's (column's) four blocks are all in range and
-  // 4-byte aligned
-  const bool row_dw = cols % 128 == 0 && ((uintptr_t)s_row & 3) == 0;
-  const bool col_dw = ldc % 128 == 0 && ((uintptr_t)s_col & 3) == 0;
+  // whole scale dwords (a row's four blocks of a 128-chunk) where the base is
+  // 4-byte aligned and all four blocks are written
+  const bool row_dw = ((uintptr_t)s_row & 3) == 0;
+  const bool col_dw = ((uintptr_t)s_col & 3) == 0;
 
   // ---- rowwise: both units' loads first
   uint4 raw[2][32 / V];
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
         uint4* dst = (uint4*)(q_row + (long)rr[k] * cols + c);
         store_nt16(dst, make_uint4(w[0], w[1], w[2], w[3]));
         store_nt16(dst + 1, make_uint4(w[4], w[5], w[6], w[7]));
-        uint8_t* sp = s_row + (long)rr[k] * (cols / 32) + c / 32;
+        uint8_t* sp = s_row + ((long)(c >> 7) * rows + rr[k]) * 4 + ((c >> 5) & 3);
         if (row_dw && all == 15u) {
           if (q4 == 0) *(uint32_t*)sp = sw;
         } else {
@@ -210,7 +215,8 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
       uint4* dst = (uint4*)(q_col + (long)c * ldc + base + sb * 32);
       store_nt16(dst, make_uint4(w[0], w[1], w[2], w[3]));
       store_nt16(dst + 1, make_uint4(w[4], w[5], w[6], w[7]));
-      uint8_t* sp = s_col + (long)c * (ldc / 32) + (base + sb * 32) / 32;
+      const int b = (base + sb * 32) >> 5;  // block along the padded rows
+      uint8_t* sp = s_col + ((long)(b >> 2) * cols + c) * 4 + (b & 3);
       if (col_dw && all == 15u) {
         if (sb == 0) *(uint32_t*)sp = sw;
       } else {
