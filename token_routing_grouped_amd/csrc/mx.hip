@@ -128,6 +128,39 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
   const bool row_dw = ((uintptr_t)s_row & 3) == 0;
   const bool col_dw = ((uintptr_t)s_col & 3) == 0;
 
+  // The band's four 32-row blocks -> (first source row, segment end, valid),
+  // looked up once per workgroup.  Segment starts go through LDS first (one
+  // coalesced load instead of a chain of dependent loads per thread: the
+  // search's latency was a large part of a band's time).
+  __shared__ int s_off[1025];
+  __shared__ int blk[4][3];
+  if (seg_off != nullptr && nseg <= 1024) {
+    for (int e = tid; e <= nseg; e += 256) s_off[e] = seg_off128[e];
+    __syncthreads();
+  }
+  if (tid < 4) {
+    const int b32 = base + tid * 32;
+    int r0 = 0, seg_hi = 0, ok = 0;
+    if (seg_off != nullptr && nseg <= 1024) {
+      if (b32 < s_off[nseg]) {
+        int lo = 0, hi = nseg;  // last e with seg_off128[e] <= b32
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_off[mid] <= b32) lo = mid; else hi = mid;
+        }
+        r0 = seg_off[lo] + (b32 - s_off[lo]);
+        seg_hi = seg_off[lo + 1];
+        ok = 1;
+      }
+    } else {
+      ok = mx_block_rows(b32, rows, seg_off, seg_off128, nseg, seg_rows, r0, seg_hi) ? 1 : 0;
+    }
+    blk[tid][0] = r0;
+    blk[tid][1] = seg_hi;
+    blk[tid][2] = ok;
+  }
+  __syncthreads();
+
   // ---- rowwise: both units' loads first
   uint4 raw[2][32 / V];
   int rr[2];
@@ -135,8 +168,8 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int i = (tid >> 2) + 64 * k;
-    int r0, seg_hi;
-    const bool blk_ok = mx_block_rows(base + (i & ~31), rows, seg_off, seg_off128, nseg, seg_rows, r0, seg_hi);
+    const int r0 = blk[i >> 5][0], seg_hi = blk[i >> 5][1];
+    const bool blk_ok = blk[i >> 5][2] != 0;
     rr[k] = r0 + (i & 31);
     const int c = col0 + q4 * 32;
     rok[k] = blk_ok && rr[k] < seg_hi && c < cols;
@@ -194,9 +227,7 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
   for (int k = 0; k < 2; ++k) {
     const int cc = (tid >> 2) + 64 * k, sb = q4;
     const int c = col0 + cc;
-    int r0, seg_hi;
-    const bool blk_ok = mx_block_rows(base + sb * 32, rows, seg_off, seg_off128, nseg, seg_rows, r0, seg_hi);
-    const bool ok = blk_ok && c < cols;
+    const bool ok = blk[sb][2] != 0 && c < cols;
     float x[32];
 #pragma unroll
     for (int z = 0; z < 32; ++z) x[z] = to_f32(at(sb * 32 + z, cc));
