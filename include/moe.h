@@ -185,7 +185,9 @@ moe_status_t moe_unpermute_sum(const void* dxp, const int32_t* pos, int T, int d
  *   g = xp w1[e]^T, u = xp w3[e]^T, hbuf = silu(g) * u   (SwiGLU fused in the
  *   epilogue; g, u, hbuf stored in dt for the backward),
  * and a second launch yp = hbuf w2[e]^T.  The tile map is derived on the
- * device from offsets.  ws: moe_grouped_gemm_workspace_size() bytes.
+ * device from offsets, by every workgroup in its prologue.  ws:
+ * moe_grouped_gemm_workspace_size() bytes (0 in this version; ws may then be
+ * null).
  * bf16 needs d and h to be multiples of 64 and R * max(d, 2h) * 2 < 2^31.
  * Memory-lean forward (bf16): g and/or u may be null, then they are not
  * stored; the backward recomputes them with moe_grouped_gemm_recompute_gu

@@ -367,9 +367,9 @@ moe_status_t moe_grouped_gemm_fwd(const void* xp, const void* w1, const void* w3
   TRY(check_ptrs(fn, {{"xp", xp}, {"hbuf", hbuf}, {"yp", yp}}));
   TRY(check_optional_aligned(fn, {{"g", g}, {"u", u}}));
   const size_t need = trg::ggemm_ws_bytes(E, R, d, h);
-  if (ws == nullptr || ws_bytes < need)
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
-  if (!aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+  if (ws && !aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
   TRY(check_device());
   return hip_status(fn, trg::launch_ggemm_fwd(xp, w1, w3, w2, offsets, E, R, d, h, dt == MOE_BF16, g, u, hbuf, yp, ws,
                                               (hipStream_t)stream));
@@ -385,9 +385,9 @@ moe_status_t moe_grouped_gemm_recompute_gu(const void* xp, const void* w1, const
   if (R == 0) return ok();
   TRY(check_ptrs(fn, {{"xp", xp}, {"g", g}, {"u", u}}));
   const size_t need = trg::ggemm_ws_bytes(E, R, d, h);
-  if (ws == nullptr || ws_bytes < need)
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
-  if (!aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+  if (ws && !aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
   TRY(check_device());
   return hip_status(fn, trg::launch_ggemm_recompute_gu(xp, w1, w3, offsets, E, R, d, h, g, u, ws, (hipStream_t)stream));
 }
@@ -407,9 +407,9 @@ static moe_status_t ggemm_bwd_impl(const char* fn, const void* dyp, const void* 
   if (R > 0)
     TRY(check_ptrs(fn, {{"dyp", dyp}, {"xp", xp}, {"g", g}, {"u", u}, {"hbuf", hbuf}, {"dgu", dgu}, {"dxp", dxp}}));
   const size_t need = trg::ggemm_ws_bytes(E, R, d, h);
-  if (ws == nullptr || ws_bytes < need)
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
-  if (!aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+  if (ws && !aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
   TRY(check_device());
   return hip_status(fn, trg::launch_ggemm_bwd(dyp, xp, g, u, hbuf, w1, w3, w2, offsets, E, R, d, h, dt == MOE_BF16,
                                               dgu, dxp, dw1, dw3, dw2, ws, parts, (hipStream_t)stream));
@@ -547,9 +547,9 @@ static moe_status_t check_mx_dims(const char* fn, int E, int R, int d, int h, in
   if ((long)R * widest * 2 >= (1L << 31) || (long)widest * rcap >= (1L << 31))
     return fail(MOE_ERR_UNSUPPORTED, "%s: operands larger than 2^31 bytes", fn);
   const size_t need = trg::ggemm_ws_bytes(E, R, d, h);
-  if (ws == nullptr || ws_bytes < need)
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
-  if (!aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+  if (ws && !aligned16(ws)) return fail(MOE_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
   return MOE_OK;
 }
 

@@ -67,16 +67,21 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
   const int wm = wave / WN, wn = wave % WN;
 
   const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+  // the schedule's per-expert prefixes, from the expert offsets
+  __shared__ int pre[2 * 1025];
+  __shared__ int ptmp[16];
+  if constexpr (MODE == RAGGED_M) rm_prefix<BM, NW * 64>(g.offsets, g.E, g.split_tails, pre, ptmp);
+  else wgrad_prefix<NW * 64>(g.offsets, g.E, g.kstep, pre, ptmp);
   // t runs over this XCD's walk: ragged M, positions of its RmSched slices;
   // ragged K, global tile indices of its work-balanced range
   int t_begin, t_end;
   RmSched rms{};
   if constexpr (MODE == RAGGED_M) {
-    rms = rm_sched<BM>(g.tile_off, g.E, g.tiles_n, xcd);
+    rms = rm_sched<BM>(pre, g.E, g.tiles_n, xcd);
     t_begin = 0;
     t_end = rms.nf + rms.nl;
   } else {
-    wgrad_range(g.work, g.E, g.tiles_m * g.tiles_n, g.E * g.tiles_m * g.tiles_n, xcd, t_begin, t_end);
+    wgrad_range(pre, g.E, g.tiles_m * g.tiles_n, g.E * g.tiles_m * g.tiles_n, xcd, t_begin, t_end);
   }
 
   // Per-tile geometry and operand resources.
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
     c.light = false;
     if constexpr (MODE == RAGGED_M) {
       int nt;
-      rm_tile<BM>(g.tile_off, g.offsets, g.E, g.tiles_n, rms, t, c.e, c.m0, c.m_end, nt);
+      rm_tile<BM>(pre, g.offsets, g.E, g.tiles_n, rms, t, c.e, c.m0, c.m_end, nt);
       c.light = LIGHT3 && t >= rms.nf;
       c.n0 = nt * BN;
       c.k0 = 0;
@@ -288,37 +293,6 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
   }
 }
 
-// Per-expert row-tile prefix for BM = 128 and 256 from the expert offsets.
-__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict__ offsets, int E,
-                                                           int* __restrict__ tile_off, int split_tails) {
-  __shared__ int tmp[1024];
-  const int e = threadIdx.x;
-  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-  const int tail = c & 255;
-  const bool light = split_tails && tail > 0 && tail <= 128;
-  const int per_b[3] = {(c + 127) / 128, (c + 255) / 256 - (light ? 1 : 0), light ? 1 : 0};
-#pragma unroll 1
-  for (int b = 0; b < 3; ++b) {
-    int total;
-    const int ex = block_excl_scan_1024(per_b[b], tmp, &total);
-    if (e < E) tile_off[b * (E + 1) + e] = ex;
-    if (e == 0) tile_off[b * (E + 1) + E] = total;
-  }
-}
-
-// Per-expert work prefix of the weight-gradient tiles (see wgrad_range) from
-// the experts' K segments koff [E+1] and the K step bk.
-__global__ __launch_bounds__(1024) void wgrad_work_kernel(const int* __restrict__ koff, int E, int bk,
-                                                          int* __restrict__ work) {
-  __shared__ int tmp[1024];
-  const int e = threadIdx.x;
-  const int w = e < E ? (koff[e + 1] - koff[e] + bk - 1) / bk + kTileFixedSteps : 0;
-  int total;
-  const int ex = block_excl_scan_1024(w, tmp, &total);
-  if (e < E) work[e] = ex;
-  if (e == 0) work[E] = total;
-}
-
 // 8 waves (two per SIMD) per 256-wide tile: while one wave of a SIMD waits
 // on LDS the other issues MFMAs.
 template <int BM, int BN, bool AKC, bool BKC, int MODE, int BSEL, int CSEL, int EPI>
@@ -331,11 +305,11 @@ static void run(const char* name, const Args& a, int max_tiles, hipStream_t s) {
 
 }  // namespace gg
 
-// [0, 3(E+1)): row-tile prefixes (tile_prefix_kernel); [3(E+1), 4(E+1)):
-// weight-gradient work prefix (wgrad_work_kernel).
+// The grouped GEMMs need no scratch: every workgroup derives its schedule's
+// prefixes from the expert offsets in its prologue.
 size_t ggemm_ws_bytes(int E, int R, int d, int h) {
-  (void)R; (void)d; (void)h;
-  return (size_t)(4 * (E + 1)) * sizeof(int);
+  (void)E; (void)R; (void)d; (void)h;
+  return 0;
 }
 
 using namespace gg;
@@ -344,30 +318,30 @@ using namespace gg;
 // G, U, H may be null (not stored).
 template <int BM>
 static void up_bm(const char* name, const void* xp, const void* w1, const void* w3, const int* offsets, int E, int R,
-                  int d, int h, void* gq, void* u, void* hb, const int* tile_off, hipStream_t s) {
+                  int d, int h, void* gq, void* u, void* hb, hipStream_t s) {
   const int mt_max = cdiv(R, BM) + E;
   Args a{};
   a.A = (const uint16_t*)xp; a.lda = d;
   a.B = (const uint16_t*)w1; a.B2 = (const uint16_t*)w3; a.ldb = d; a.b_es = (long)h * d;
   a.C = gq; a.C2 = u; a.C3 = hb; a.ldc = h;
   a.N = 2 * h; a.K = d; a.split = h;
-  a.offsets = offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+  a.offsets = offsets; a.split_tails = split_tails(E, R); a.E = E; a.R = R;
   a.tiles_n = cdiv(2L * h, 256);
   run<BM, 256, true, true, RAGGED_M, BSEL_GLU, CSEL_NONE, EPI_SWIGLU_FWD>(name, a, mt_max * a.tiles_n, s);
 }
 
 template <int BM>
 static void fwd_bm(const void* xp, const void* w1, const void* w3, const void* w2, const int* offsets, int E, int R,
-                   int d, int h, void* gq, void* u, void* hb, void* yp, const int* tile_off, hipStream_t s) {
+                   int d, int h, void* gq, void* u, void* hb, void* yp, hipStream_t s) {
   const int mt_max = cdiv(R, BM) + E;
-  up_bm<BM>("ggemm_up_swiglu", xp, w1, w3, offsets, E, R, d, h, gq, u, hb, tile_off, s);
+  up_bm<BM>("ggemm_up_swiglu", xp, w1, w3, offsets, E, R, d, h, gq, u, hb, s);
   {  // down projection
     Args a{};
     a.A = (const uint16_t*)hb; a.lda = h;
     a.B = (const uint16_t*)w2; a.ldb = h; a.b_es = (long)d * h;
     a.C = yp; a.ldc = d;
     a.N = d; a.K = h;
-    a.offsets = offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.offsets = offsets; a.split_tails = split_tails(E, R); a.E = E; a.R = R;
     a.tiles_n = cdiv(d, 256);
     run<BM, 256, true, true, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_down", a, mt_max * a.tiles_n, s);
   }
@@ -379,30 +353,28 @@ hipError_t launch_ggemm_fwd(const void* xp, const void* w1, const void* w3, cons
   if (!bf16)
     return launch_ggemm_fwd_f32((const float*)xp, (const float*)w1, (const float*)w3, (const float*)w2, offsets, E,
                                 R, d, h, (float*)g, (float*)u, (float*)hb, (float*)yp, s);
-  int* tile_off = (int*)ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off, split_tails(E, R));
+  (void)ws;
   if (small_rows(E, R))
-    fwd_bm<128>(xp, w1, w3, w2, offsets, E, R, d, h, g, u, hb, yp, tile_off, s);
+    fwd_bm<128>(xp, w1, w3, w2, offsets, E, R, d, h, g, u, hb, yp, s);
   else
-    fwd_bm<256>(xp, w1, w3, w2, offsets, E, R, d, h, g, u, hb, yp, tile_off + (E + 1), s);
+    fwd_bm<256>(xp, w1, w3, w2, offsets, E, R, d, h, g, u, hb, yp, s);
   return hipGetLastError();
 }
 
 hipError_t launch_ggemm_recompute_gu(const void* xp, const void* w1, const void* w3, const int* offsets, int E, int R,
                                      int d, int h, void* g, void* u, void* ws, hipStream_t s) {
-  int* tile_off = (int*)ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off, split_tails(E, R));
+  (void)ws;
   if (small_rows(E, R))
-    up_bm<128>("ggemm_recompute_gu", xp, w1, w3, offsets, E, R, d, h, g, u, nullptr, tile_off, s);
+    up_bm<128>("ggemm_recompute_gu", xp, w1, w3, offsets, E, R, d, h, g, u, nullptr, s);
   else
-    up_bm<256>("ggemm_recompute_gu", xp, w1, w3, offsets, E, R, d, h, g, u, nullptr, tile_off + (E + 1), s);
+    up_bm<256>("ggemm_recompute_gu", xp, w1, w3, offsets, E, R, d, h, g, u, nullptr, s);
   return hipGetLastError();
 }
 
 template <int BM>
 static void dgrad_bm(const void* dyp, const void* g, const void* u, const void* w1, const void* w3, const void* w2,
-                     const int* offsets, int E, int R, int d, int h, void* dgu, void* dxp, const int* tile_off,
-                     unsigned parts, hipStream_t s) {
+                     const int* offsets, int E, int R, int d, int h, void* dgu, void* dxp, unsigned parts,
+                     hipStream_t s) {
   const int mt_max = cdiv(R, BM) + E;
   if (parts & MOE_BWD_DGRAD_DOWN) {  // dgrad down + SwiGLU backward: dH = dYp W2[e] -> dG, dU
     Args a{};
@@ -411,7 +383,7 @@ static void dgrad_bm(const void* dyp, const void* g, const void* u, const void* 
     a.C = dgu; a.ldc = 2L * h;
     a.G = (const uint16_t*)g; a.U = (const uint16_t*)u; a.ldgu = h;
     a.N = h; a.K = d; a.split = h;
-    a.offsets = offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.offsets = offsets; a.split_tails = split_tails(E, R); a.E = E; a.R = R;
     a.tiles_n = cdiv(h, 256);
     run<BM, 256, true, false, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_SWIGLU_BWD>("ggemm_dgrad_down_swiglu", a,
                                                                               mt_max * a.tiles_n, s);
@@ -422,7 +394,7 @@ static void dgrad_bm(const void* dyp, const void* g, const void* u, const void* 
     a.B = (const uint16_t*)w1; a.B2 = (const uint16_t*)w3; a.ldb = d; a.b_es = (long)h * d;
     a.C = dxp; a.ldc = d;
     a.N = d; a.K = 2 * h; a.split = h;
-    a.offsets = offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.offsets = offsets; a.split_tails = split_tails(E, R); a.E = E; a.R = R;
     a.tiles_n = cdiv(d, 256);
     run<BM, 256, true, false, RAGGED_M, BSEL_KSPLIT, CSEL_NONE, EPI_BF16>("ggemm_dgrad_up", a, mt_max * a.tiles_n, s);
   }
@@ -436,23 +408,20 @@ hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, cons
     return launch_ggemm_bwd_f32((const float*)dyp, (const float*)xp, (const float*)g, (const float*)u,
                                 (const float*)hb, (const float*)w1, (const float*)w3, (const float*)w2, offsets, E,
                                 R, d, h, (float*)dgu, (float*)dxp, (float*)dw1, (float*)dw3, (float*)dw2, s);
+  (void)ws;
   if (parts & (MOE_BWD_DGRAD_DOWN | MOE_BWD_DGRAD_UP)) {
-    int* tile_off = (int*)ws;
-    tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, E, tile_off, split_tails(E, R));
     if (small_rows(E, R))
-      dgrad_bm<128>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off, parts, s);
+      dgrad_bm<128>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, parts, s);
     else
-      dgrad_bm<256>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, tile_off + (E + 1), parts, s);
+      dgrad_bm<256>(dyp, g, u, w1, w3, w2, offsets, E, R, d, h, dgu, dxp, parts, s);
   }
-  int* work = (int*)ws + 3 * (E + 1);
-  if (parts & (MOE_BWD_WGRAD_DOWN | MOE_BWD_WGRAD_UP)) wgrad_work_kernel<<<1, 1024, 0, s>>>(offsets, E, BK, work);
   if (parts & MOE_BWD_WGRAD_DOWN) {  // wgrad down: dW2[e] = dYp_e^T H_e  (M = d, N = h, K = the expert's rows)
     Args a{};
     a.A = (const uint16_t*)dyp; a.lda = d;
     a.B = (const uint16_t*)hb; a.ldb = h;
     a.C = dw2; a.ldc = h; a.c_es = (long)d * h;
     a.M = d; a.N = h;
-    a.offsets = offsets; a.work = work; a.E = E; a.R = R;
+    a.offsets = offsets; a.kstep = BK; a.E = E; a.R = R;
     a.tiles_m = cdiv(d, 256); a.tiles_n = cdiv(h, 256);
     run<256, 256, false, false, RAGGED_K, BSEL_NONE, CSEL_NONE, EPI_BF16>("ggemm_wgrad_down", a,
                                                                           E * a.tiles_m * a.tiles_n, s);
@@ -463,7 +432,7 @@ hipError_t launch_ggemm_bwd(const void* dyp, const void* xp, const void* g, cons
     a.B = (const uint16_t*)xp; a.ldb = d;
     a.C = dw1; a.C2 = dw3; a.ldc = d; a.c_es = (long)h * d;
     a.M = 2 * h; a.N = d; a.split = h;
-    a.offsets = offsets; a.work = work; a.E = E; a.R = R;
+    a.offsets = offsets; a.kstep = BK; a.E = E; a.R = R;
     a.tiles_m = cdiv(2L * h, 256); a.tiles_n = cdiv(d, 256);
     run<256, 256, false, false, RAGGED_K, BSEL_NONE, CSEL_MSPLIT, EPI_BF16>("ggemm_wgrad_up", a,
                                                                             E * a.tiles_m * a.tiles_n, s);

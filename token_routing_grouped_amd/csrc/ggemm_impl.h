@@ -47,8 +47,8 @@ struct Args {
   int M, N, K;  // RAGGED_K: M x N output per expert;  RAGGED_M: N, K
   int split;    // GLU: h;  KSPLIT: first K half;  MSPLIT: first M half
   const int* offsets;
-  const int* tile_off;  // RAGGED_M: per-expert prefix of BM row tiles
-  const int* work;      // RAGGED_K: per-expert prefix of per-tile work (see wgrad_range)
+  int split_tails;  // RAGGED_M, 256-row tiles: light tails scheduled apart (see RmSched)
+  int kstep;        // RAGGED_K: K values per step (the work prefix's unit)
   int E, R;
   int tiles_m, tiles_n;
 };
@@ -463,10 +463,80 @@ TRG_DEV void epilogue(const Args& g, f32x16_t (&acc)[WTM / 32][WTN / 32], char* 
   });
 }
 
+// Per-expert prefixes of the persistent schedules, computed by every
+// workgroup in its prologue from the expert offsets (E <= 1024) into LDS:
+// one read of offsets and a block scan, instead of a separate launch per
+// GEMM that the GEMM would wait for (a one-block kernel queued behind a
+// persistent GEMM on another stream waits for whole tiles to drain).
+// pre[0, E] (and pre[E+1, 2E+1] for two lists) receive the exclusive prefix
+// of f0(e) (and f1(e)); pre[E] is the total.
+template <int NT, class F>
+TRG_DEV void block_prefix_1024(int n, F f, int* out, int* tmp) {
+  constexpr int PER = 1024 / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int v[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid * PER + i;
+    v[i] = e < n ? f(e) : 0;
+    sum += v[i];
+  }
+  int x = sum;  // inclusive scan over the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wv] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < NT / 64; ++w) {
+      const int t = tmp[w];
+      tmp[w] = run;
+      run += t;
+    }
+  }
+  __syncthreads();
+  int ex = tmp[wv] + x - sum;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid * PER + i;
+    if (e < n) out[e] = ex;
+    ex += v[i];
+  }
+  if (tid == NT - 1) out[n] = ex;
+  __syncthreads();  // tmp is reused by the next call
+}
+
+// Ragged-M tile prefixes (see RmSched): BM = 128, [E+1] 128-row tiles;
+// BM = 256, [E+1] full-cost tiles then [E+1] light tails.
+template <int BM, int NT>
+TRG_DEV void rm_prefix(const int* offsets, int E, int split, int* pre, int* tmp) {
+  auto cnt = [&](int e) { return offsets[e + 1] - offsets[e]; };
+  if constexpr (BM == 128) {
+    block_prefix_1024<NT>(E, [&](int e) { return (cnt(e) + 127) / 128; }, pre, tmp);
+  } else {
+    auto light = [&](int c) { const int tail = c & 255; return split && tail > 0 && tail <= 128; };
+    block_prefix_1024<NT>(E, [&](int e) { const int c = cnt(e); return (c + 255) / 256 - (light(c) ? 1 : 0); },
+                          pre, tmp);
+    block_prefix_1024<NT>(E, [&](int e) { return light(cnt(e)) ? 1 : 0; }, pre + (E + 1), tmp);
+  }
+}
+
+// Ragged-K work prefix (see wgrad_range): K steps of each expert's tiles plus
+// kTileFixedSteps.
+constexpr int kTileFixedSteps = 2;
+template <int NT>
+TRG_DEV void wgrad_prefix(const int* koff, int E, int kstep, int* pre, int* tmp) {
+  block_prefix_1024<NT>(E, [&](int e) { return (koff[e + 1] - koff[e] + kstep - 1) / kstep + kTileFixedSteps; },
+                        pre, tmp);
+}
+
 // Ragged-M schedule.  Every row tile has the same K, but an expert's last
 // row tile is often nearly empty, and its MFMAs are skipped
 // (subtiles past m_end): with 256-row tiles such a tail costs about half a
-// tile.  tile_off holds per-expert prefixes from tile_prefix_kernel:
+// tile.  toff holds the per-expert prefixes of rm_prefix:
 //   BM = 128: [E+1] prefix of the experts' 128-row tiles;
 //   BM = 256: [E+1] prefix of full-cost tiles (more than 128 valid rows: the
 //             whole 256-row tiles and a tail of 129..255 rows), then [E+1]
@@ -516,8 +586,8 @@ TRG_DEV void rm_tile(const int* toff, const int* offs, int E, int tiles_n, const
 
 // Weight-gradient tiles differ in work: a tile's K loop runs over its
 // expert's rows.  work[e] = sum over experts e' < e of one tile's work,
-// ceil(rows_e' / BK) K steps plus kTileFixedSteps for the tile's prologue and
-// epilogue; every expert has per_e tiles, expert-major.  The tile list is cut
+// ceil(rows_e' / K step) K steps plus kTileFixedSteps for the tile's prologue
+// and epilogue; every expert has per_e tiles, expert-major.  The tile list is cut
 // into the eight XCD ranges by count (as the ragged-M GEMMs are) unless that
 // leaves one XCD more than 1.25x the mean work; then it is cut by work, so a
 // skewed routing (one expert holding a sixth of the rows) does not leave
@@ -525,8 +595,6 @@ TRG_DEV void rm_tile(const int* toff, const int* offs, int E, int tiles_n, const
 // takes the tiles whose cumulative work starts in [x W / 8, (x + 1) W / 8).
 // (The count cut stays the default because with about one tile per CU a cut
 // one tile off the count costs a whole extra tile on some CU.)
-constexpr int kTileFixedSteps = 2;
-
 TRG_DEV void wgrad_range(const int* work, int E, int per_e, int total, int xcd, int& t_begin, int& t_end) {
   const long W = (long)work[E] * per_e;
   const int per = (total + 7) >> 3;
@@ -559,15 +627,6 @@ TRG_DEV void wgrad_range(const int* work, int E, int per_e, int total, int xcd, 
   t_begin = tile_at(xcd * W / 8);
   t_end = xcd == 7 ? total : tile_at((xcd + 1) * W / 8);
 }
-
-__global__ __launch_bounds__(1024) void wgrad_work_kernel(const int* __restrict__ koff, int E, int bk,
-                                                          int* __restrict__ work);
-
-// Per-expert row-tile prefixes from the expert offsets (see RmSched):
-// tile_off[0, E] 128-row tiles, [E+1, 2E+1] full-cost 256-row tiles,
-// [2E+2, 3E+2] light 256-row tails.
-__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict__ offsets, int E,
-                                                           int* __restrict__ tile_off, int split_tails);
 
 // Light tails get their own place in the walk only where experts are large
 // (R >= 2048 E): there an extra tile round is a large share of the kernel,

@@ -88,16 +88,21 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
   const int half = lane >> 5;
 
   const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+  // the schedule's per-expert prefixes, from the expert offsets
+  __shared__ int pre[2 * 1025];
+  __shared__ int ptmp[16];
+  if constexpr (MODE == RAGGED_M) rm_prefix<BM, NW * 64>(g.offsets, g.E, g.split_tails, pre, ptmp);
+  else wgrad_prefix<NW * 64>(g.offsets, g.E, g.kstep, pre, ptmp);
   // t runs over this XCD's walk: ragged M, positions of its RmSched slices;
   // ragged K, global tile indices of its work-balanced range
   int t_begin, t_end;
   RmSched rms{};
   if constexpr (MODE == RAGGED_M) {
-    rms = rm_sched<BM>(g.tile_off, g.E, g.tiles_n, xcd);
+    rms = rm_sched<BM>(pre, g.E, g.tiles_n, xcd);
     t_begin = 0;
     t_end = rms.nf + rms.nl;
   } else {
-    wgrad_range(g.work, g.E, g.tiles_m * g.tiles_n, g.E * g.tiles_m * g.tiles_n, xcd, t_begin, t_end);
+    wgrad_range(pre, g.E, g.tiles_m * g.tiles_n, g.E * g.tiles_m * g.tiles_n, xcd, t_begin, t_end);
   }
 
   const __amdgpu_buffer_rsrc_t rsSA = make_rsrc(x.sA, x.sA_bytes);
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
     Tile c;
     if constexpr (MODE == RAGGED_M) {
       int nt;
-      rm_tile<BM>(g.tile_off, g.offsets, g.E, g.tiles_n, rms, t, c.e, c.m0, c.m_end, nt);
+      rm_tile<BM>(pre, g.offsets, g.E, g.tiles_n, rms, t, c.e, c.m0, c.m_end, nt);
       c.n0 = nt * BN;
       c.k0 = 0;
       c.klen = g.K;
@@ -321,8 +326,7 @@ using namespace gg;
 // Up projection + SwiGLU: xq [R,d] x (W1q | W3q) [E,h,d]; any of G, U, H may
 // be null (not stored).
 template <int BM>
-static void mx_up_bm(const char* name, const MxFwd& p, void* gq, void* u, void* hb, const int* tile_off,
-                     hipStream_t s) {
+static void mx_up_bm(const char* name, const MxFwd& p, void* gq, void* u, void* hb, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
   const int mt_max = cdiv(R, BM) + E;
   Args a{};
@@ -330,7 +334,7 @@ static void mx_up_bm(const char* name, const MxFwd& p, void* gq, void* u, void* 
   a.B = (const uint16_t*)p.w1q; a.B2 = (const uint16_t*)p.w3q; a.ldb = d; a.b_es = (long)h * d;
   a.C = gq; a.C2 = u; a.C3 = hb; a.ldc = h;
   a.N = 2 * h; a.K = d; a.split = h;
-  a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+  a.offsets = p.offsets; a.split_tails = split_tails(E, R); a.E = E; a.R = R;
   a.tiles_n = cdiv(2L * h, 256);
   MxArgs x{};
   x.sA = p.xs; x.sa_step = 4L * R; x.sA_bytes = (long)R * (d / 32);
@@ -339,18 +343,16 @@ static void mx_up_bm(const char* name, const MxFwd& p, void* gq, void* u, void* 
 }
 
 hipError_t launch_ggemm_recompute_gu_mx(const MxFwd& p, hipStream_t s) {
-  int* tile_off = (int*)p.ws;
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, tile_off, split_tails(p.E, p.R));
-  if (small_rows(p.E, p.R)) mx_up_bm<128>("ggemm_mx_recompute_gu", p, p.g, p.u, nullptr, tile_off, s);
-  else mx_up_bm<256>("ggemm_mx_recompute_gu", p, p.g, p.u, nullptr, tile_off + (p.E + 1), s);
+  if (small_rows(p.E, p.R)) mx_up_bm<128>("ggemm_mx_recompute_gu", p, p.g, p.u, nullptr, s);
+  else mx_up_bm<256>("ggemm_mx_recompute_gu", p, p.g, p.u, nullptr, s);
   return hipGetLastError();
 }
 
 template <int BM>
-static hipError_t mx_fwd_bm(const MxFwd& p, const int* tile_off, hipStream_t s) {
+static hipError_t mx_fwd_bm(const MxFwd& p, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
   const int mt_max = cdiv(R, BM) + E;
-  mx_up_bm<BM>("ggemm_mx_up_swiglu", p, p.g, p.u, p.hbuf, tile_off, s);
+  mx_up_bm<BM>("ggemm_mx_up_swiglu", p, p.g, p.u, p.hbuf, s);
   // H -> rowwise MX (down GEMM) and columnwise per expert (wgrad down)
   {
     ProfScope ps("mx_quantize_h", s);
@@ -364,7 +366,7 @@ static hipError_t mx_fwd_bm(const MxFwd& p, const int* tile_off, hipStream_t s) 
     a.B = (const uint16_t*)p.w2q; a.ldb = h; a.b_es = (long)d * h;
     a.C = p.yp; a.ldc = d;
     a.N = d; a.K = h;
-    a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.offsets = p.offsets; a.split_tails = split_tails(E, R); a.E = E; a.R = R;
     a.tiles_n = cdiv(d, 256);
     MxArgs x{};
     x.sA = p.hs; x.sa_step = 4L * R; x.sA_bytes = (long)R * (h / 32);
@@ -379,14 +381,12 @@ static hipError_t mx_fwd_bm(const MxFwd& p, const int* tile_off, hipStream_t s) 
 // byte loaded, so the per-step costs need the larger tile.  The weight
 // gradients (K-tail masking, more registers) use 128 x 256.
 hipError_t launch_ggemm_fwd_mx(const MxFwd& p, hipStream_t s) {
-  int* tile_off = (int*)p.ws;  // 128-row prefix, then the 256-row full-cost and light prefixes (RmSched)
-  tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, tile_off, split_tails(p.E, p.R));
-  if (small_rows(p.E, p.R)) return mx_fwd_bm<128>(p, tile_off, s);
-  return mx_fwd_bm<256>(p, tile_off + (p.E + 1), s);
+  if (small_rows(p.E, p.R)) return mx_fwd_bm<128>(p, s);
+  return mx_fwd_bm<256>(p, s);
 }
 
 template <int BM>
-static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, unsigned parts, hipStream_t s) {
+static hipError_t mx_dgrad_bm(const MxBwd& p, unsigned parts, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
   const int mt_max = cdiv(R, BM) + E;
   if (parts & MOE_BWD_DGRAD_DOWN) {  // dgrad down + SwiGLU backward: dyq [R,d] x W2 blocked along d ([h, E*d])
@@ -396,7 +396,7 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, unsigned part
     a.C = p.dgu; a.ldc = 2L * h;
     a.G = (const uint16_t*)p.g; a.U = (const uint16_t*)p.u; a.ldgu = h;
     a.N = h; a.K = d; a.split = h;
-    a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.offsets = p.offsets; a.split_tails = split_tails(E, R); a.E = E; a.R = R;
     a.tiles_n = cdiv(h, 256);
     MxArgs x{};
     x.sA = p.dys; x.sa_step = 4L * R; x.sA_bytes = (long)R * (d / 32);
@@ -416,7 +416,7 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, const int* tile_off, unsigned part
     a.B = (const uint16_t*)p.w1tq; a.B2 = (const uint16_t*)p.w3tq; a.ldb = (long)E * h; a.b_es = h;
     a.C = p.dxp; a.ldc = d;
     a.N = d; a.K = 2 * h; a.split = h;
-    a.offsets = p.offsets; a.tile_off = tile_off; a.E = E; a.R = R;
+    a.offsets = p.offsets; a.split_tails = split_tails(E, R); a.E = E; a.R = R;
     a.tiles_n = cdiv(d, 256);
     MxArgs x{};
     x.sA = p.dgus; x.sa_step = 4L * R; x.sA_bytes = (long)R * (2 * h / 32);
@@ -437,23 +437,18 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   if (parts & (MOE_BWD_DGRAD_DOWN | MOE_BWD_DGRAD_UP)) {
-    int* tile_off = (int*)p.ws;
-    tile_prefix_kernel<<<1, 1024, 0, s>>>(p.offsets, E, tile_off, split_tails(E, p.R));
-    const hipError_t err = small_rows(E, R) ? mx_dgrad_bm<128>(p, tile_off, parts, s)
-                                            : mx_dgrad_bm<256>(p, tile_off + (E + 1), parts, s);
+    const hipError_t err = small_rows(E, R) ? mx_dgrad_bm<128>(p, parts, s) : mx_dgrad_bm<256>(p, parts, s);
     if (err != hipSuccess) return err;
   }
   if (!(parts & (MOE_BWD_WGRAD_DOWN | MOE_BWD_WGRAD_UP))) return hipGetLastError();
   const long sc = p.rcap / 32;
-  int* work = (int*)p.ws + 3 * (E + 1);
-  wgrad_work_kernel<<<1, 1024, 0, s>>>(p.off128, E, 128, work);
   if (parts & MOE_BWD_WGRAD_DOWN) {  // wgrad down: dW2[e] = dYp_e^T H_e over the expert's padded segment
     Args a{};
     a.A = (const uint16_t*)p.dyqT; a.lda = p.rcap;
     a.B = (const uint16_t*)p.hqT; a.ldb = p.rcap;
     a.C = p.dw2; a.ldc = h; a.c_es = (long)d * h;
     a.M = d; a.N = h;
-    a.offsets = p.off128; a.work = work; a.E = E; a.R = R;
+    a.offsets = p.off128; a.kstep = 128; a.E = E; a.R = R;
     a.tiles_m = cdiv(d, 256); a.tiles_n = cdiv(h, 256);
     MxArgs x{};
     x.sA = p.dysT; x.sa_step = 4L * d; x.sA_bytes = (long)d * sc;
@@ -467,7 +462,7 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s) {
     a.B = (const uint16_t*)p.xqT; a.ldb = p.rcap;
     a.C = p.dw1; a.C2 = p.dw3; a.ldc = d; a.c_es = (long)h * d;
     a.M = 2 * h; a.N = d; a.split = h;
-    a.offsets = p.off128; a.work = work; a.E = E; a.R = R;
+    a.offsets = p.off128; a.kstep = 128; a.E = E; a.R = R;
     a.tiles_m = cdiv(2L * h, 256); a.tiles_n = cdiv(d, 256);
     MxArgs x{};
     x.sA = p.dgusT; x.sa_step = 8L * h; x.sA_bytes = (long)2 * h * sc;
