@@ -164,7 +164,8 @@ moe_status_t moe_combine(const void* yp, const float* topk_w, const int32_t* pos
 
 /*
  * moe_combine_bwd: dyp[pos[t,j]] = topk_w[t,j] * dy[t] (rounded to dt) and
- * dgate[t,j] = <dy[t], yp[pos[t,j]]> (fp32).
+ * dgate[t,j] = <dy[t], yp[pos[t,j]]> (fp32).  dyp may be null: then only dgate
+ * is written (the MXFP8 backward quantises dYp straight from dy).
  */
 moe_status_t moe_combine_bwd(const void* dy, const void* yp, const float* topk_w,
                              const int32_t* pos, int T, int d, int k, int dt, void* dyp,
@@ -385,6 +386,12 @@ typedef struct {
   void* dxp;                                /* out: [R,d] bf16                      */
   void* dw1; void* dw3; void* dw2;          /* out: weight gradients, bf16          */
   void* ws; size_t ws_bytes;
+  /* dYp's MX copies straight from dy, without dyp: when dyp is null, row r of
+   * dYp is taken as bf16(topk_w[src[r]] * dy[src[r] / k]), exactly what
+   * moe_combine_bwd would have stored (it may then be called with dyp = null,
+   * for dgate only).  dy [T,d] bf16, topk_w [T,k] f32 and src [R] i32 as
+   * moe_route wrote them; unused when dyp is given. */
+  const void* dy; const float* topk_w; const int32_t* src; int k;
 } moe_mx_bwd_args;
 
 moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* args, void* stream);

@@ -191,10 +191,17 @@ def test_mx_layer_parity(case):
     f = mxl.layer_forward_mx(x, wr, w1, w3, w2, cfg.k, forced_idx=forced)
     b = mxl.layer_backward_mx(f, dy, x, wr, w1, w3, w2)
     assert (to_np(layer.pos) == f["pos"]).all()
-    h = cfg.h
+    h, d, R = cfg.h, cfg.d, cfg.R
     dgu = to_np(layer.dgu)
+    # dYp is not stored on the MXFP8 path: its two MX copies are checked
+    off, off128 = f["offsets"], f["off128"]
+    R32 = int(off128[-1])
+    dyq = mx.dequantize_rows(to_np(layer.dyq), mx_scales_to_rows(to_np(layer.dys), R, d))
+    dyqT = mx.dequantize_cols_segmented(to_np(layer.dyqT)[:, :R32],
+                                        mx_scales_to_rows(to_np(layer.dysT), d, layer.rcap)[:, :R32 // 32], off, off128)
     checks = [("G", layer.g, f["G"]), ("U", layer.u, f["U"]), ("H", layer.hb, f["H"]), ("Yp", layer.yp, f["yp"]),
-              ("y", layer.y, f["y"]), ("dYp", layer.dyp, b["dyp"]), ("dG", dgu[:, :h], b["dG"]),
+              ("y", layer.y, f["y"]), ("dYp (MX rows)", dyq, mx.qdq_rows(b["dyp"])),
+              ("dYp (MX cols)", dyqT, mx.qdq_cols_segmented(b["dyp"], off, off128)), ("dG", dgu[:, :h], b["dG"]),
               ("dU", dgu[:, h:], b["dU"]), ("dXp", layer.dxp, b["dxp"]), ("dx", layer.dx, b["dx"]),
               ("dW1", layer.dw1, b["dw1"]), ("dW3", layer.dw3, b["dw3"]), ("dW2", layer.dw2, b["dw2"]),
               ("dWr", layer.dwr, b["dwr"])]
@@ -224,3 +231,35 @@ def test_mx_layer_deterministic():
                                          layer.dguqT[:, :R32])])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("T,E,mode", [(512, 16, "uniform"), (300, 8, "router")])
+def test_mx_dy_copies_from_dy_equal_the_quantised_stored_dyp(T, E, mode):
+    """The MXFP8 backward builds dYp's MX copies straight from dy (row r =
+    bf16(topk_w[src[r]] * dy[src[r] / k])); they must equal, byte for byte,
+    mx_quantize of the dYp that moe_combine_bwd stores (the reading that every
+    MX copy is made from its bf16 value)."""
+    from token_routing_grouped_amd import _abi
+    from token_routing_grouped_amd.layer import MoELayerGPU
+
+    cfg = configs.get("wide").with_(T=T, E=E, d=256, h=128)
+    say(f"mx dY copies T={T} E={E} {mode}")
+    inp = inputs.layer_inputs(cfg)
+    t = {n: torch.from_numpy(v).to(DEV).to(torch.bfloat16) for n, v in inp.items()}
+    forced = None if mode == "router" else torch.from_numpy(
+        inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)).to(DEV)
+    layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, mx=True)
+    layer.step(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"], forced_idx=forced)
+    R, d, rc = cfg.R, cfg.d, layer.rcap
+    dyp = torch.empty(R, d, dtype=torch.bfloat16, device=DEV)
+    dgate = torch.empty_like(layer.dgate)
+    _abi.moe_combine_bwd(t["dy"], layer.yp, layer.topk_w, layer.pos, dyp, dgate)
+    q, s, qT, sT = _u8(R, d), _u8(mx_scale_bytes(R, d)), _u8(d, rc), _u8(mx_scale_bytes(d, rc))
+    _abi.mx_quantize(dyp, R, q, s, qT, sT, seg_off=layer.offsets, seg_off128=layer.off128)
+    torch.cuda.synchronize()
+    end = int(layer.off128[-1].item())
+    assert torch.equal(dgate, layer.dgate)
+    assert torch.equal(q, layer.dyq) and torch.equal(s.view(-1), layer.dys.view(-1))
+    assert torch.equal(qT[:, :end], layer.dyqT[:, :end])
+    nb = end // 128 * d * 4  # scale chunks up to the last padded segment
+    assert torch.equal(sT.view(-1)[:nb], layer.dysT.view(-1)[:nb])

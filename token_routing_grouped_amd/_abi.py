@@ -75,7 +75,7 @@ class MxBwdArgs(ctypes.Structure):
         [(n, ctypes.c_void_p) for n in ("offsets", "off128", "dyp", "dyq", "dys", "dyqT", "dysT", "g", "u", "hqT", "hsT",
                                         "xqT", "xsT", "w1tq", "w1ts", "w3tq", "w3ts", "w2tq", "w2ts", "dgu", "dguq",
                                         "dgus", "dguqT", "dgusT", "dxp", "dw1", "dw3", "dw2", "ws")] + \
-        [("ws_bytes", ctypes.c_size_t)]
+        [("ws_bytes", ctypes.c_size_t)] + [(n, ctypes.c_void_p) for n in ("dy", "topk_w", "src")] + [("k", ctypes.c_int)]
 
 EXPORTED = tuple(_SIGS)
 
@@ -249,6 +249,7 @@ def moe_combine(yp, topk_w, pos, y):
 
 
 def moe_combine_bwd(dy, yp, topk_w, pos, dyp, dgate):
+    """dyp may be None: then only dgate is written."""
     T, k = pos.shape
     d = yp.shape[1]
     _expect(dy, yp.dtype, "dy")

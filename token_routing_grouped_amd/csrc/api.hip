@@ -315,7 +315,8 @@ moe_status_t moe_combine_bwd(const void* dy, const void* yp, const float* topk_w
   TRY(check_tk(fn, T, k));
   TRY(check_row(fn, "d", d, dt));
   if (T == 0) return ok();
-  TRY(check_ptrs(fn, {{"dy", dy}, {"yp", yp}, {"topk_w", topk_w}, {"pos", pos}, {"dyp", dyp}, {"dgate", dgate}}));
+  TRY(check_ptrs(fn, {{"dy", dy}, {"yp", yp}, {"topk_w", topk_w}, {"pos", pos}, {"dgate", dgate}}));
+  TRY(check_optional_aligned(fn, {{"dyp", dyp}}));
   TRY(check_device());
   trg::ProfScope ps(fn, (hipStream_t)stream);
   return hip_status(fn, trg::launch_combine_bwd(dy, yp, topk_w, pos, T, d, k, dt == MOE_BF16, dyp, dgate,
@@ -588,9 +589,17 @@ static moe_status_t ggemm_bwd_mx_impl(const char* fn, const moe_mx_bwd_args* a, 
                       {"dw3", a->dw3}, {"dw2", a->dw2}}));
   TRY(check_ptrs(fn, {{"dyq", a->dyq}, {"dys", a->dys}, {"dyqT", a->dyqT}, {"dysT", a->dysT}, {"hqT", a->hqT},
                       {"hsT", a->hsT}, {"xqT", a->xqT}, {"xsT", a->xsT}, {"dguqT", a->dguqT}, {"dgusT", a->dgusT}}));
-  if (a->R > 0)
-    TRY(check_ptrs(fn, {{"dyp", a->dyp}, {"g", a->g}, {"u", a->u}, {"dgu", a->dgu}, {"dguq", a->dguq},
-                        {"dgus", a->dgus}, {"dxp", a->dxp}}));
+  if (a->R > 0) {
+    TRY(check_ptrs(fn, {{"g", a->g}, {"u", a->u}, {"dgu", a->dgu}, {"dguq", a->dguq}, {"dgus", a->dgus},
+                        {"dxp", a->dxp}}));
+    if (a->dyp == nullptr) {  // dYp's MX copies from dy, topk_w and src
+      TRY(check_ptrs(fn, {{"dy", a->dy}, {"topk_w", a->topk_w}, {"src", a->src}}));
+      if (a->k < 1 || a->k > 32 || a->R % a->k != 0)
+        return fail(MOE_ERR_INVALID_ARG, "%s: k must be in [1, 32] and divide R when dyp is null", fn);
+    } else {
+      TRY(check_ptrs(fn, {{"dyp", a->dyp}}));
+    }
+  }
   TRY(check_device());
   return hip_status(fn, trg::launch_ggemm_bwd_mx(*a, parts, (hipStream_t)stream));
 }

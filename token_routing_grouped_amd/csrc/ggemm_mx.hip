@@ -432,8 +432,12 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
   if (parts & MOE_BWD_DGRAD_DOWN) {  // dYp -> rowwise (dgrad down) and columnwise per expert (wgrad down)
     ProfScope ps("mx_quantize_dy", s);
-    const hipError_t err = launch_mx_quantize(p.dyp, true, d, R, d, nullptr, 1, p.offsets, p.off128, E, 0,
-                                              (R + 127 * E + 31) / 32, p.dyq, p.dys, p.dyqT, p.dysT, p.rcap, s);
+    // from the stored dYp, or straight from dy (row r: topk_w[src[r]] * dy[src[r] / k])
+    const bool from_dy = p.dyp == nullptr;
+    const hipError_t err =
+        launch_mx_quantize(from_dy ? p.dy : p.dyp, true, d, R, d, from_dy ? p.src : nullptr, from_dy ? p.k : 1,
+                           p.offsets, p.off128, E, 0, (R + 127 * E + 31) / 32, p.dyq, p.dys, p.dyqT, p.dysT, p.rcap, s,
+                           from_dy ? p.topk_w : nullptr);
     if (err != hipSuccess) return err;
   }
   if (parts & (MOE_BWD_DGRAD_DOWN | MOE_BWD_DGRAD_UP)) {

@@ -70,7 +70,7 @@ hipError_t launch_ggemm_bwd_f32(const float* dyp, const float* xp, const float* 
 hipError_t launch_mx_quantize(const void* in, bool bf16, long ld_in, int rows, int cols, const int* src, int gk,
                               const int* seg_off, const int* seg_off128, int nseg, int seg_rows, int max_blocks32,
                               uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, long ldc,
-                              hipStream_t s);
+                              hipStream_t s, const float* gate = nullptr);
 typedef moe_mx_fwd_args MxFwd;
 typedef moe_mx_bwd_args MxBwd;
 hipError_t launch_ggemm_recompute_gu(const void* xp, const void* w1, const void* w3, const int* offsets, int E, int R,

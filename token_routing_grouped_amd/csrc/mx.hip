@@ -23,7 +23,10 @@
 // chunk's dwords of consecutive rows are contiguous: a GEMM K step of 128
 // reads its tile's scales as one piece instead of a dword per row.
 // Rows can be gathered on the fly (row r reads in[src[r] / k]), which fuses
-// the rowwise dispatch of the layer input into its quantisation.
+// the rowwise dispatch of the layer input into its quantisation; a gathered
+// row can also be scaled by gate[src[r]] and rounded to bf16 first, which is
+// the combine backward's dYp row (gate * dy[t]) quantised without being
+// stored.
 #include "common.h"
 #include "kernels.h"
 
@@ -102,6 +105,7 @@ TRG_DEV bool mx_block_rows(int base32, int rows, const int* seg_off, const int* 
 template <class T>
 __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, long ld_in, int rows, int cols,
                                                       const int* __restrict__ src, int gk,
+                                                      const float* __restrict__ gate,
                                                       const int* __restrict__ seg_off,
                                                       const int* __restrict__ seg_off128, int nseg, int seg_rows,
                                                       uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
@@ -175,10 +179,25 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
     rok[k] = blk_ok && rr[k] < seg_hi && c < cols;
     if (rok[k]) {
       long srow = rr[k];
-      if (src != nullptr) srow = src[rr[k]] / gk;
+      float gw = 1.0f;
+      if (src != nullptr) {
+        const int sr = src[rr[k]];
+        srow = sr / gk;
+        if (gate != nullptr) gw = gate[sr];
+      }
       const uint4* p = (const uint4*)(in + srow * ld_in + c);
 #pragma unroll
       for (int q = 0; q < 32 / V; ++q) raw[k][q] = p[q];
+      if (gate != nullptr) {  // the gated row, rounded to the source type (bf16 RNE)
+#pragma unroll
+        for (int q = 0; q < 32 / V; ++q) {
+          float f[V];
+          unpack16<T>(raw[k][q], f);
+#pragma unroll
+          for (int z = 0; z < V; ++z) f[z] *= gw;
+          raw[k][q] = pack16<T>(f);
+        }
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < 32 / V; ++q) raw[k][q] = make_uint4(0, 0, 0, 0);
@@ -260,16 +279,16 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
 hipError_t launch_mx_quantize(const void* in, bool bf16, long ld_in, int rows, int cols, const int* src, int gk,
                               const int* seg_off, const int* seg_off128, int nseg, int seg_rows, int max_blocks32,
                               uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, long ldc,
-                              hipStream_t s) {
+                              hipStream_t s, const float* gate) {
   if (rows == 0 || max_blocks32 == 0) return hipSuccess;
   const long nblk = (long)((max_blocks32 + 3) / 4) * ((cols + kMxCols - 1) / kMxCols);
   if (nblk > 0x7FFFFFFFL) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)nblk;
   if (bf16)
-    mx_dual_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)in, ld_in, rows, cols, src, gk, seg_off,
+    mx_dual_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)in, ld_in, rows, cols, src, gk, gate, seg_off,
                                                   seg_off128, nseg, seg_rows, q_row, s_row, q_col, s_col, ldc);
   else
-    mx_dual_kernel<float><<<grid, 256, 0, s>>>((const float*)in, ld_in, rows, cols, src, gk, seg_off, seg_off128,
+    mx_dual_kernel<float><<<grid, 256, 0, s>>>((const float*)in, ld_in, rows, cols, src, gk, gate, seg_off, seg_off128,
                                                nseg, seg_rows, q_row, s_row, q_col, s_col, ldc);
   return hipGetLastError();
 }

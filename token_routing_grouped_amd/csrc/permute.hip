@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
         float o[V], g[V];
 #pragma unroll
         for (int i = 0; i < V; ++i) o[i] = wj * f[i];
-        ((uint4*)(dyp + (long)p * d))[v] = pack16<T>(o);
+        if (dyp != nullptr) ((uint4*)(dyp + (long)p * d))[v] = pack16<T>(o);  // null: dgate only
         unpack16<T>(((const uint4*)(yp + (long)p * d))[v], g);
         float s = 0.f;
 #pragma unroll

@@ -33,9 +33,10 @@ class MoELayerGPU:
     mx=True runs the six grouped GEMMs in MXFP8 (E4M3 + E8M0 per 32 values,
     each operand blocked along its own GEMM's K): the routed rows of x are
     quantised straight from x (dispatch and quantisation in one pass), the
-    weights are quantised in both layouts every step, and H, dYp and dG|dU are
-    quantised inside the grouped-GEMM calls.  Router, combine and all outputs
-    stay bf16.
+    weights are quantised in both layouts every step, dYp's MX copies come
+    straight from dy (gate-scaled gather; dYp itself is not stored), and H and
+    dG|dU are quantised inside the grouped-GEMM calls.  Router, combine and
+    all outputs stay bf16.
     """
 
     def __init__(self, T: int, d: int, E: int, k: int, h: int, dtype: torch.dtype, device="cuda", mx: bool = False,
@@ -158,7 +159,9 @@ class MoELayerGPU:
             _abi.moe_grouped_gemm_recompute_gu(self.xp, w1, w3, self.offsets, self.g, self.u, self.ws_gemm)
 
     def backward(self, dy, x, wr, w1, w3, w2):
-        _abi.moe_combine_bwd(dy, self.yp, self.topk_w, self.pos, self.dyp, self.dgate)
+        # MXFP8: dYp is not stored; its MX copies come straight from dy (gate-scaled gather)
+        self._dy = dy
+        _abi.moe_combine_bwd(dy, self.yp, self.topk_w, self.pos, None if self.mx else self.dyp, self.dgate)
         if self.lean:
             self.recompute_gu(w1, w3)
         if self.mx and self.overlap:
@@ -190,7 +193,7 @@ class MoELayerGPU:
 
     def _mx_bwd_fields(self, ws):
         return dict(E=self.E, R=self.R, d=self.d, h=self.h, rcap=self.rcap, offsets=self.offsets, off128=self.off128,
-                    dyp=self.dyp, dyq=self.dyq, dys=self.dys, dyqT=self.dyqT, dysT=self.dysT, g=self.g, u=self.u,
+                    dyp=None, dy=self._dy, topk_w=self.topk_w, src=self.src, k=self.k, dyq=self.dyq, dys=self.dys, dyqT=self.dyqT, dysT=self.dysT, g=self.g, u=self.u,
                     hqT=self.hqT, hsT=self.hsT, xqT=self.xqT, xsT=self.xsT, w1tq=self.w1tq, w1ts=self.w1ts,
                     w3tq=self.w3tq, w3ts=self.w3ts, w2tq=self.w2tq, w2ts=self.w2ts, dgu=self.dgu, dguq=self.dguq,
                     dgus=self.dgus, dguqT=self.dguqT, dgusT=self.dgusT, dxp=self.dxp, dw1=self.dw1, dw3=self.dw3,
