@@ -40,7 +40,7 @@ class MoELayerGPU:
     """
 
     def __init__(self, T: int, d: int, E: int, k: int, h: int, dtype: torch.dtype, device="cuda", mx: bool = False,
-                 aux_alpha: float = 0.0, lean: bool = False, overlap: bool = False):
+                 aux_alpha: float = 0.0, lean: bool = False, overlap: bool = False, wq_overlap: bool = True):
         self.T, self.d, self.E, self.k, self.h = T, d, E, k, h
         self.aux_alpha = float(aux_alpha)
         # memory-lean: the forward does not store G and U; the backward
@@ -93,8 +93,11 @@ class MoELayerGPU:
         self.aux_g = e(E, dt=f32)
         self.mean_probs = e(E, dt=f32)
         self.ws_balance = _abi.workspace(_abi.moe_balance_workspace_size(T, E), dev)
+        self.wq_stream = None
         if mx:
             self._alloc_mx(dev)
+            if wq_overlap:
+                self.wq_stream = torch.cuda.Stream(device=dev)  # default priority
 
     def _alloc_mx(self, dev):
         T, d, E, k, h, R = self.T, self.d, self.E, self.k, self.h, self.R
@@ -123,6 +126,18 @@ class MoELayerGPU:
 
     # ------------------------------------------------------------------
     def forward(self, x, wr, w1, w3, w2, forced_idx=None):
+        if self.mx and self.wq_stream is not None:
+            # the weights' MX copies do not depend on the routing: they are made
+            # on a second stream while the router and the routing run (small,
+            # latency-bound launches that leave most of the GPU idle)
+            main = torch.cuda.current_stream()
+            ev = torch.cuda.Event()
+            ev.record(main)
+            with torch.cuda.stream(self.wq_stream):
+                self.wq_stream.wait_event(ev)
+                self.quantize_weights(w1, w3, w2)
+                self._ev_wq = torch.cuda.Event()
+                self._ev_wq.record(self.wq_stream)
         _abi.moe_router_logits(x, wr, self.logits)
         _abi.moe_route(self.logits, self.k, self.probs, self.topk_idx, self.topk_w, self.counts, self.offsets,
                        self.pos, self.src, self.ws_route, off128=self.off128, forced_idx=forced_idx,
@@ -133,7 +148,10 @@ class MoELayerGPU:
             # routed rows of x straight into their experts' MX buffers
             _abi.mx_quantize(x, self.R, self.xq, self.xs, self.xqT, self.xsT, gather_src=self.src, gather_k=self.k,
                              seg_off=self.offsets, seg_off128=self.off128)
-            self.quantize_weights(w1, w3, w2)
+            if self.wq_stream is not None:
+                torch.cuda.current_stream().wait_event(self._ev_wq)
+            else:
+                self.quantize_weights(w1, w3, w2)
             _abi.moe_grouped_gemm_fwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, rcap=self.rcap,
                                          offsets=self.offsets, off128=self.off128, xq=self.xq, xs=self.xs, w1q=self.w1q,
                                          w1s=self.w1s, w3q=self.w3q, w3s=self.w3s, w2q=self.w2q, w2s=self.w2s,
