@@ -10,49 +10,32 @@
 //    registers: the next K tile's global loads are issued before the current
 //    tile's MFMAs.
 //  * An operand stored K-contiguous is copied with 16-byte loads.  An operand
-//    stored MN-contiguous (the dgrad / wgrad cases) is read as 8x8 blocks of
-//    16-byte row pieces and transposed in registers before the LDS write, so
-//    every GEMM feeds the matrix cores from the same LDS layout.
+//    stored MN-contiguous (dWr's both operands, dx's router weights) is read as
+//    8x8 blocks of 16-byte row pieces and transposed in registers before the
+//    LDS write, so every GEMM feeds the matrix cores from the same LDS layout.
 //  * The MFMA is issued as (B fragment, A fragment): each lane then owns 4
-//    consecutive output columns of one row, stored as one 8- or 16-byte write.
-//  * Grouping modes: DENSE (one problem, optional split-K), RAGGED_M (expert
-//    segments of the routed rows; the per-expert tile prefix is derived on the
-//    device from the offsets), RAGGED_K (weight gradients: the reduction runs
-//    over the expert's rows).
-//  * Epilogues: bf16 / fp32 store, SwiGLU forward (G, U, H), SwiGLU backward
-//    (dG, dU from dH, G, U), and read-add-write bf16.
+//    consecutive output columns of one row, stored as one 16-byte write.
+//  * One dense problem per launch, with an optional fixed-order split-K (fp32
+//    partials); epilogues: fp32 store, or read-add-write into a bf16 output.
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
 
 namespace trg {
 
-enum Mode { DENSE = 0, RAGGED_M = 1, RAGGED_K = 2 };
-enum BSel { BSEL_NONE = 0, BSEL_GLU = 1, BSEL_KSPLIT = 2 };
-enum CSel { CSEL_NONE = 0, CSEL_MSPLIT = 1 };
-enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_SWIGLU_FWD = 2, EPI_SWIGLU_BWD = 3, EPI_ADD_BF16 = 4 };
+enum Epi { EPI_F32 = 1, EPI_ADD_BF16 = 4 };
 
 struct GemmArgs {
   // A[m][k]: K-contiguous -> A[m*lda + k]; MN-contiguous -> A[k*lda + m]
   const uint16_t* A;
-  long lda, a_es;  // a_es: per-expert element stride (0 = shared)
+  long lda;
   const uint16_t* B;
-  const uint16_t* B2;  // second matrix for BSEL_GLU / BSEL_KSPLIT
-  long ldb, b_es;
+  long ldb;
   void* C;
-  void* C2;  // CSEL_MSPLIT second output; SWIGLU_FWD: U
-  void* C3;  // SWIGLU_FWD: H
-  long ldc, c_es;
-  const uint16_t* G;  // SWIGLU_BWD inputs
-  const uint16_t* U;
-  long ldgu;
+  long ldc;
   int M, N, K;
-  int split;  // h: GLU rows per matrix / K split point / M split point
-  const int* offsets;
-  const int* tile_off;
-  int E;
   int tiles_m, tiles_n;
-  int ksplit_len;  // DENSE split-K: K elements per split (multiple of 64); 0 = none
+  int ksplit_len;  // split-K: K elements per split (multiple of 64); 0 = none
   long c_split_stride;
 };
 
@@ -78,7 +61,7 @@ TRG_DEV void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int MODE, int BSEL, int CSEL, int EPI>
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BK = 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -86,7 +69,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int STAGE = (BM + BN) * 8;  // uint4 per LDS stage
   static_assert(WM * WN == 4, "4 waves");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
-  static_assert(BSEL != BSEL_GLU || (TN % 2 == 0), "GLU pairs subtiles");
   constexpr int NA = AKC ? BM * 8 / 256 : ((BM + 255) / 256) * 8;
   constexpr int NB = BKC ? BN * 8 / 256 : ((BN + 255) / 256) * 8;
   static_assert(!AKC || (BM * 8) % 256 == 0, "A tile");
@@ -96,56 +78,20 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // ---------------- tile decode ----------------
-  int e = 0, m0, m_end, n0, k0, k_end;
-  long split_idx = 0;
-  if constexpr (MODE == DENSE) {
-    int t = blockIdx.x;
-    const int per = g.tiles_m * g.tiles_n;
-    split_idx = t / per;
-    t -= (int)split_idx * per;
-    const int mt = t / g.tiles_n, nt = t % g.tiles_n;
-    m0 = mt * BM;
-    m_end = g.M;
-    n0 = nt * BN;
-    if (g.ksplit_len > 0) {
-      k0 = (int)split_idx * g.ksplit_len;
-      k_end = min(g.K, k0 + g.ksplit_len);
-    } else {
-      k0 = 0;
-      k_end = g.K;
-    }
-  } else if constexpr (MODE == RAGGED_M) {
-    const int t = blockIdx.x;
-    const int mtg = t / g.tiles_n, nt = t % g.tiles_n;
-    if (mtg >= g.tile_off[g.E]) return;  // beyond the real tile count: whole block exits
-    int lo = 0, hi = g.E;                // last expert with tile_off[e] <= mtg
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (g.tile_off[mid] <= mtg) lo = mid; else hi = mid;
-    }
-    e = lo;
-    m0 = g.offsets[e] + (mtg - g.tile_off[e]) * BM;
-    m_end = g.offsets[e + 1];
-    n0 = nt * BN;
-    k0 = 0;
-    k_end = g.K;
-  } else {
-    int t = blockIdx.x;
-    const int per = g.tiles_m * g.tiles_n;
-    e = t / per;
-    t -= e * per;
-    const int mt = t / g.tiles_n, nt = t % g.tiles_n;
-    m0 = mt * BM;
-    m_end = g.M;
-    n0 = nt * BN;
-    k0 = g.offsets[e];
-    k_end = g.offsets[e + 1];
+  // ---------------- tile: (split, row tile, column tile) ----------------
+  int t = blockIdx.x;
+  const int per = g.tiles_m * g.tiles_n;
+  const long split_idx = t / per;
+  t -= (int)split_idx * per;
+  const int mt = t / g.tiles_n, nt = t % g.tiles_n;
+  const int m0 = mt * BM, m_end = g.M, n0 = nt * BN;
+  int k0 = 0, k_end = g.K;
+  if (g.ksplit_len > 0) {
+    k0 = (int)split_idx * g.ksplit_len;
+    k_end = min(g.K, k0 + g.ksplit_len);
   }
-
-  const uint16_t* Ab = g.A + (long)e * g.a_es;
-  const uint16_t* Bb = g.B + (long)e * g.b_es;
-  const uint16_t* B2b = (BSEL != BSEL_NONE) ? g.B2 + (long)e * g.b_es : nullptr;
+  const uint16_t* Ab = g.A;
+  const uint16_t* Bb = g.B;
 
   uint4 ra[NA], rb[NB];
 
@@ -178,31 +124,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int q = tid + 256 * i, row = q >> 3, ch = q & 7;
-        const int gk = kt + ch * 8;
-        const uint16_t* src;
-        bool ok;
-        if constexpr (BSEL == BSEL_GLU) {
-          const int part = row / WTN, p = row % WTN;
-          const int which = p / (WTN / 2);
-          const int hh = n0 / 2 + part * (WTN / 2) + p % (WTN / 2);
-          src = (which ? B2b : Bb) + (long)hh * g.ldb + gk;
-          ok = hh < g.split && gk < k_end;
-        } else {
-          const int gn = n0 + row;
-          src = Bb + (long)gn * g.ldb + gk;
-          ok = gn < g.N && gk < k_end;
-        }
-        rb[i] = ok ? *(const uint4*)src : make_uint4(0, 0, 0, 0);
+        const int gn = n0 + row, gk = kt + ch * 8;
+        rb[i] = (gn < g.N && gk < k_end) ? *(const uint4*)(Bb + (long)gn * g.ldb + gk) : make_uint4(0, 0, 0, 0);
       }
     } else {
-      const uint16_t* base = Bb;
-      int krel = kt;
-      if constexpr (BSEL == BSEL_KSPLIT) {
-        if (kt >= g.split) {
-          base = B2b;
-          krel = kt - g.split;
-        }
-      }
 #pragma unroll
       for (int i = 0; i < NB / 8; ++i) {
         const int q = tid + 256 * i;
@@ -211,8 +136,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const int gk = kt + kb * 8 + r;
-          const int kr = krel + kb * 8 + r;
-          rb[i * 8 + r] = (q < BN && gk < k_end && gn < g.N) ? *(const uint4*)(base + (long)kr * g.ldb + gn)
+          rb[i * 8 + r] = (q < BN && gk < k_end && gn < g.N) ? *(const uint4*)(Bb + (long)gk * g.ldb + gn)
                                                                : make_uint4(0, 0, 0, 0);
         }
       }
@@ -314,91 +238,31 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   // Lane (lrow, lgrp) owns rows m = ... + lrow and 4 consecutive columns per
   // group q: n = ... + q*8 + lgrp + {0..3}.
   const int lrow = lane & 31, lgrp = (lane >> 5) * 4;
-  if constexpr (EPI == EPI_SWIGLU_FWD) {
-    uint16_t* Gp = (uint16_t*)g.C;
-    uint16_t* Up = (uint16_t*)g.C2;
-    uint16_t* Hp = (uint16_t*)g.C3;
-    static_for<TM>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      const int m = m0 + wm * WTM + i * 32 + lrow;
-      if (m < m_end) {
-        static_for<TN / 2>([&](auto J) {
-          constexpr int j = decltype(J)::value;
-          static_for<4>([&](auto Q) {
-            constexpr int q = decltype(Q)::value;
-            const int hh = n0 / 2 + wn * (WTN / 2) + j * 32 + q * 8 + lgrp;
-            if (hh < g.split) {
-              float gv[4], uv[4], hv[4];
-              static_for<4>([&](auto Rr) {
-                constexpr int r = decltype(Rr)::value;
-                gv[r] = acc[i][j][q * 4 + r];
-                uv[r] = acc[i][j + TN / 2][q * 4 + r];
-                hv[r] = silu_f(gv[r]) * uv[r];
-              });
-              const long o = (long)m * g.ldc + hh;
-              *(uint2*)(Gp + o) = make_uint2(pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3]));
-              *(uint2*)(Up + o) = make_uint2(pack_bf2(uv[0], uv[1]), pack_bf2(uv[2], uv[3]));
-              *(uint2*)(Hp + o) = make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
+  static_for<TM>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    const int m = m0 + wm * WTM + i * 32 + lrow;
+    if (m < m_end) {
+      static_for<TN>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        static_for<4>([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          const int n = n0 + wn * WTN + j * 32 + q * 8 + lgrp;
+          if (n < g.N) {
+            const float v0 = acc[i][j][q * 4 + 0], v1 = acc[i][j][q * 4 + 1];
+            const float v2 = acc[i][j][q * 4 + 2], v3 = acc[i][j][q * 4 + 3];
+            const long o = (long)m * g.ldc + n;
+            if constexpr (EPI == EPI_F32) {
+              *(float4*)((float*)g.C + split_idx * g.c_split_stride + o) = make_float4(v0, v1, v2, v3);
+            } else {  // EPI_ADD_BF16: the bf16 output plus the product, rounded once more
+              const uint2 old = *(uint2*)((uint16_t*)g.C + o);
+              *(uint2*)((uint16_t*)g.C + o) = make_uint2(pack_bf2(bf_lo(old.x) + v0, bf_hi(old.x) + v1),
+                                                         pack_bf2(bf_lo(old.y) + v2, bf_hi(old.y) + v3));
             }
-          });
-        });
-      }
-    });
-  } else {
-    static_for<TM>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      const int m = m0 + wm * WTM + i * 32 + lrow;
-      if (m < m_end) {
-        void* Cb = g.C;
-        int mrow0 = 0;
-        if constexpr (CSEL == CSEL_MSPLIT) {
-          if (m >= g.split) {
-            Cb = g.C2;
-            mrow0 = g.split;
           }
-        }
-        static_for<TN>([&](auto J) {
-          constexpr int j = decltype(J)::value;
-          static_for<4>([&](auto Q) {
-            constexpr int q = decltype(Q)::value;
-            const int n = n0 + wn * WTN + j * 32 + q * 8 + lgrp;
-            if (n < g.N) {
-              const float v0 = acc[i][j][q * 4 + 0], v1 = acc[i][j][q * 4 + 1];
-              const float v2 = acc[i][j][q * 4 + 2], v3 = acc[i][j][q * 4 + 3];
-              const long o = (long)e * g.c_es + (long)(m - mrow0) * g.ldc + n;
-              if constexpr (EPI == EPI_BF16) {
-                *(uint2*)((uint16_t*)Cb + o) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
-              } else if constexpr (EPI == EPI_F32) {
-                *(float4*)((float*)Cb + split_idx * g.c_split_stride + o) = make_float4(v0, v1, v2, v3);
-              } else if constexpr (EPI == EPI_ADD_BF16) {
-                const uint2 old = *(uint2*)((uint16_t*)Cb + o);
-                *(uint2*)((uint16_t*)Cb + o) = make_uint2(pack_bf2(bf_lo(old.x) + v0, bf_hi(old.x) + v1),
-                                                          pack_bf2(bf_lo(old.y) + v2, bf_hi(old.y) + v3));
-              } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-                // (v0..v3) = dH[m][n..n+3]; n indexes h
-                const long gu = (long)m * g.ldgu + n;
-                const uint2 gw = *(const uint2*)(g.G + gu);
-                const uint2 uw = *(const uint2*)(g.U + gu);
-                const float vv[4] = {v0, v1, v2, v3};
-                const float gg[4] = {bf_lo(gw.x), bf_hi(gw.x), bf_lo(gw.y), bf_hi(gw.y)};
-                const float uu[4] = {bf_lo(uw.x), bf_hi(uw.x), bf_lo(uw.y), bf_hi(uw.y)};
-                float dg[4], du[4];
-                static_for<4>([&](auto Rr) {
-                  constexpr int r = decltype(Rr)::value;
-                  const float s = sigmoid_f(gg[r]);
-                  du[r] = vv[r] * gg[r] * s;
-                  dg[r] = vv[r] * uu[r] * s * (1.0f + gg[r] * (1.0f - s));
-                });
-                uint16_t* D = (uint16_t*)Cb + (long)m * g.ldc;
-                *(uint2*)(D + n) = make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
-                *(uint2*)(D + g.split + n) = make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
-              }
-            }
-          });
         });
-      }
-    });
-  }
+      });
+    }
+  });
 }
 
 // Fixed-order sum of split-K partials: out[i] = sum_s part[s][i].
@@ -416,11 +280,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const float* __
 
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int MODE, int BSEL, int CSEL, int EPI>
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int EPI>
 static void run(const char* name, const GemmArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return;
   ProfScope ps(name, s);
-  gemm_bf16_kernel<BM, BN, WM, WN, AKC, BKC, MODE, BSEL, CSEL, EPI><<<grid, 256, 0, s>>>(a);
+  gemm_bf16_kernel<BM, BN, WM, WN, AKC, BKC, EPI><<<grid, 256, 0, s>>>(a);
 }
 
 // ---------------- router GEMMs on the matrix cores (E >= 64) ----------------
@@ -433,7 +297,7 @@ hipError_t launch_dense_nt_f32out(const uint16_t* A, const uint16_t* B, float* C
   a.C = C; a.ldc = N;
   a.M = M; a.N = N; a.K = K;
   a.tiles_m = cdiv(M, 128); a.tiles_n = cdiv(N, 128);
-  run<128, 128, 2, 2, true, true, DENSE, BSEL_NONE, CSEL_NONE, EPI_F32>("router_logits_mfma", a, a.tiles_m * a.tiles_n, s);
+  run<128, 128, 2, 2, true, true, EPI_F32>("router_logits_mfma", a, a.tiles_m * a.tiles_n, s);
   return hipGetLastError();
 }
 
@@ -465,7 +329,7 @@ hipError_t launch_router_dwr_mfma(const uint16_t* dL, const uint16_t* x, uint16_
   a.M = E; a.N = d; a.K = T;
   a.tiles_m = cdiv(E, 128); a.tiles_n = cdiv(d, 128);
   a.ksplit_len = kl;
-  run<128, 128, 2, 2, false, false, DENSE, BSEL_NONE, CSEL_NONE, EPI_F32>("router_dwr_mfma", a, sp * a.tiles_m * a.tiles_n, s);
+  run<128, 128, 2, 2, false, false, EPI_F32>("router_dwr_mfma", a, sp * a.tiles_m * a.tiles_n, s);
   const long n = (long)E * d;
   splitk_reduce_bf16_kernel<<<cdiv(n / 4, 256), 256, 0, s>>>(part, sp, n, dwr);
   return hipGetLastError();
@@ -479,7 +343,7 @@ hipError_t launch_router_dx_mfma(const uint16_t* dL, const uint16_t* wr, uint16_
   a.C = dx; a.ldc = d;
   a.M = T; a.N = d; a.K = E;
   a.tiles_m = cdiv(T, 128); a.tiles_n = cdiv(d, 128);
-  run<128, 128, 2, 2, true, false, DENSE, BSEL_NONE, CSEL_NONE, EPI_ADD_BF16>("router_dx_mfma", a, a.tiles_m * a.tiles_n, s);
+  run<128, 128, 2, 2, true, false, EPI_ADD_BF16>("router_dx_mfma", a, a.tiles_m * a.tiles_n, s);
   return hipGetLastError();
 }
 
