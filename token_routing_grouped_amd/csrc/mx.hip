@@ -60,6 +60,51 @@ TRG_DEV uint32_t e4m3_x4(float a, float b, float c, float d) {
 TRG_DEV float to_f32(float v) { return v; }
 TRG_DEV float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// bf16 blocks are quantised from packed pairs (two bf16 per dword) without
+// unpacking them to fp32:
+//   amax: an unsigned 16-bit max of the magnitude bits (bf16 magnitudes order
+//   like their bit patterns), whose exponent field gives the scale byte
+//   max(ex - 8, 0): the same s as mx_scale_exp for every finite block;
+//   codes: gfx950's scaled conversion divides each value by the scale operand
+//   (2^s, a float subnormal for s = -127) and rounds to nearest even, but
+//   returns the NaN code S.1111.111 where the quotient overflows +-448 instead
+//   of saturating; nan_to_448 turns those bytes into S.1111.110 (+-448).  On
+//   every bf16 bit pattern and scales 2^-127 .. 2^119 a hardware probe gave
+//   the same bytes as the clamp + unscaled conversion path used for fp32.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+
+TRG_DEV uint32_t nan_to_448(uint32_t w) {
+  const uint32_t t = ((w & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;  // bit 7 set where a byte is S.1111.111
+  return w ^ (t >> 7);
+}
+// Codes of the four bf16 values in the pairs a, b (bytes in element order).
+TRG_DEV uint32_t e4m3_bf16x4(uint32_t a, uint32_t b, float scale) {
+  // the first conversion writes the low half over a's own bits (no zeroing
+  // move), the second the high half
+  i16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(i16x2_t, a), __builtin_bit_cast(bf16x2_t, a),
+                                                        scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, b), scale, true);
+  return nan_to_448(__builtin_bit_cast(uint32_t, r));
+}
+// Scale byte of a block of 2n bf16 values held as n pairs.
+template <int N>
+TRG_DEV int scale_byte_bf16(const uint32_t* p) {
+  u16x2_t m = __builtin_bit_cast(u16x2_t, p[0] & 0x7fff7fffu);
+#pragma unroll
+  for (int q = 1; q < N; ++q) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, p[q] & 0x7fff7fffu));
+  const int amax = max((int)m.x, (int)m.y);
+  return max(((amax >> 7) & 0xff) - 8, 0);
+}
+// The scale operand 2^(sb - 127) of scale byte sb.
+TRG_DEV float scale_of_byte(int sb) { return __uint_as_float(sb ? (uint32_t)sb << 23 : 0x00400000u); }
+// The eight code dwords of a 32-value bf16 block held as 16 pairs.
+TRG_DEV void quant_block_bf16(const uint32_t* p, int sb, uint32_t* w) {
+  const float sc = scale_of_byte(sb);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) w[q] = e4m3_bf16x4(p[2 * q], p[2 * q + 1], sc);
+}
+
 constexpr int kMxRows = 128;  // padded rows per workgroup (four 32-row blocks)
 constexpr int kMxCols = 128;  // columns per workgroup
 
@@ -67,6 +112,13 @@ constexpr int kMxCols = 128;  // columns per workgroup
 TRG_DEV uint32_t or4(uint32_t v) {
   v |= __shfl_xor(v, 1);
   return v | __shfl_xor(v, 2);
+}
+// OR of v over the N (2 or 4) neighbouring lanes of an aligned group.
+template <int N>
+TRG_DEV uint32_t or_n(uint32_t v) {
+  v |= __shfl_xor(v, 1);
+  if constexpr (N == 4) v |= __shfl_xor(v, 2);
+  return v;
 }
 
 // Segment of the 32-row block starting at padded row base32: the block's first
@@ -95,14 +147,18 @@ TRG_DEV bool mx_block_rows(int base32, int rows, const int* seg_off, const int* 
   return true;
 }
 
-// One workgroup: 128 rows of the padded row space (four 32-row blocks, each
-// inside one segment) x 128 columns; every thread takes two units per pass.
+// One workgroup: RB rows of the padded row space (NB = RB/32 blocks of 32
+// rows, each inside one segment) x 128 columns, 256 threads.
 //   rowwise pass: unit u -> row u/4, 32 columns from (u%4)*32: the four units
 //   of a row are neighbouring lanes, so each row's 128 payload bytes go out as
-//   one piece and its 4 scale bytes as one dword;
-//   columnwise pass: unit u -> column u/4, 32-row block u%4: likewise 128
-//   payload bytes and one scale dword per column.
-template <class T>
+//   one piece and its 4 scale bytes as one dword (RB/64 units per thread);
+//   columnwise pass: unit u -> column u/NB, 32-row block u%NB: NB*32 payload
+//   bytes of a column as one piece, its NB scale bytes as one dword (NB = 4)
+//   or half dword (NB = 2) (NB/2 units per thread).
+// RB = 128 makes each column's payload piece one whole 128-byte line: with RB
+// = 64 (half the LDS, twice the workgroups per CU) the half-line pieces made
+// the weights' two-layout pass 30% slower.
+template <class T, int RB>
 __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, long ld_in, int rows, int cols,
                                                       const int* __restrict__ src, int gk,
                                                       const float* __restrict__ gate,
@@ -111,38 +167,40 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
                                                       uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                                       uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
                                                       long ldc) {
-  // The tile keeps the source values in their own type (bf16: 33 KiB).  Row
-  // pitch kMxCols + PAD elements plus 64 bytes per 32-row block: the
-  // columnwise pass reads four blocks x 16 columns per wave from distinct
-  // banks.
+  // The tile keeps the source values in their own type.  Row pitch kMxCols +
+  // PAD elements plus 64 bytes per 32-row block: the columnwise pass reads
+  // its blocks x columns of a wave from distinct banks.
+  constexpr int NB = RB / 32, KU = RB / 64, KC = NB / 2;
   constexpr int PAD = sizeof(T) == 2 ? 2 : 1;
   constexpr int PITCH = kMxCols + PAD;
   constexpr int BLKSKIP = 64 / sizeof(T);
   constexpr int V = 16 / sizeof(T);  // values per 16-byte load
-  __shared__ __attribute__((aligned(16))) T tile[kMxRows * PITCH + 4 * BLKSKIP];
+  __shared__ __attribute__((aligned(16))) T tile[RB * PITCH + NB * BLKSKIP];
+  static_assert(sizeof(tile) >= 1025 * sizeof(int), "the segment starts are staged in the tile");
   auto at = [&](int r, int c) -> T& { return tile[r * PITCH + (r >> 5) * BLKSKIP + c]; };
   const int tid = threadIdx.x, q4 = tid & 3;
   // workgroups walk the column blocks of a row band first: neighbouring
   // workgroups read neighbouring pieces of the same source rows
   const int ncb = (cols + kMxCols - 1) / kMxCols;
-  const int base = (int)(blockIdx.x / ncb) * kMxRows;
+  const int base = (int)(blockIdx.x / ncb) * RB;
   const int col0 = (int)(blockIdx.x % ncb) * kMxCols;
   // whole scale dwords (a row's four blocks of a 128-chunk) where the base is
   // 4-byte aligned and all four blocks are written
   const bool row_dw = ((uintptr_t)s_row & 3) == 0;
   const bool col_dw = ((uintptr_t)s_col & 3) == 0;
 
-  // The band's four 32-row blocks -> (first source row, segment end, valid),
+  // The band's 32-row blocks -> (first source row, segment end, valid),
   // looked up once per workgroup.  Segment starts go through LDS first (one
   // coalesced load instead of a chain of dependent loads per thread: the
-  // search's latency was a large part of a band's time).
-  __shared__ int s_off[1025];
-  __shared__ int blk[4][3];
+  // search's latency was a large part of a band's time); they sit in the
+  // tile's space, which is written only after the lookup.
+  int* s_off = (int*)tile;
+  __shared__ int blk[NB][3];
   if (seg_off != nullptr && nseg <= 1024) {
     for (int e = tid; e <= nseg; e += 256) s_off[e] = seg_off128[e];
     __syncthreads();
   }
-  if (tid < 4) {
+  if (tid < NB) {
     const int b32 = base + tid * 32;
     int r0 = 0, seg_hi = 0, ok = 0;
     if (seg_off != nullptr && nseg <= 1024) {
@@ -165,12 +223,12 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
   }
   __syncthreads();
 
-  // ---- rowwise: both units' loads first
-  uint4 raw[2][32 / V];
-  int rr[2];
-  bool rok[2];
+  // ---- rowwise: all units' loads first
+  uint4 raw[KU][32 / V];
+  int rr[KU];
+  bool rok[KU];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < KU; ++k) {
     const int i = (tid >> 2) + 64 * k;
     const int r0 = blk[i >> 5][0], seg_hi = blk[i >> 5][1];
     const bool blk_ok = blk[i >> 5][2] != 0;
@@ -204,31 +262,39 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
     }
   }
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < KU; ++k) {
     const int i = (tid >> 2) + 64 * k;
     const int c = col0 + q4 * 32;
     // the source bits go to the tile as they are
 #pragma unroll
     for (int z = 0; z < 32; ++z) at(i, q4 * 32 + z) = ((const T*)raw[k])[z];
     if (q_row != nullptr) {
-      float v[32];
+      int s;
+      uint32_t w[8];
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t* pr = (const uint32_t*)raw[k];
+        const int sb = scale_byte_bf16<16>(pr);
+        s = sb - 127;
+        quant_block_bf16(pr, sb, w);
+      } else {
+        float v[32];
 #pragma unroll
-      for (int q = 0; q < 32 / V; ++q) unpack16<T>(raw[k][q], v + q * V);
-      float amax = 0.f;
+        for (int q = 0; q < 32 / V; ++q) unpack16<T>(raw[k][q], v + q * V);
+        float amax = 0.f;
 #pragma unroll
-      for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(v[z]));
-      const int s = mx_scale_exp(amax);
-      const uint32_t all = or4((rok[k] ? 1u : 0u) << q4);
-      const uint32_t sw = or4((uint32_t)(s + 127) << (8 * q4));
-      if (rok[k]) {
-        uint32_t w[8];
+        for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(v[z]));
+        s = mx_scale_exp(amax);
 #pragma unroll
         for (int q = 0; q < 8; ++q)
           w[q] = e4m3_x4(ldexpf(v[q * 4], -s), ldexpf(v[q * 4 + 1], -s), ldexpf(v[q * 4 + 2], -s),
                          ldexpf(v[q * 4 + 3], -s));
+      }
+      const uint32_t all = or4((rok[k] ? 1u : 0u) << q4);
+      const uint32_t sw = or4((uint32_t)(s + 127) << (8 * q4));
+      if (rok[k]) {
         uint4* dst = (uint4*)(q_row + (long)rr[k] * cols + c);
-        store_nt16(dst, make_uint4(w[0], w[1], w[2], w[3]));
-        store_nt16(dst + 1, make_uint4(w[4], w[5], w[6], w[7]));
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
         uint8_t* sp = s_row + ((long)(c >> 7) * rows + rr[k]) * 4 + ((c >> 5) & 3);
         if (row_dw && all == 15u) {
           if (q4 == 0) *(uint32_t*)sp = sw;
@@ -243,32 +309,50 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
 
   // ---- columnwise (rows outside a segment are zero in the tile)
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int cc = (tid >> 2) + 64 * k, sb = q4;
+  for (int k = 0; k < KC; ++k) {
+    const int cc = tid / NB + (256 / NB) * k, sb = tid % NB;
     const int c = col0 + cc;
     const bool ok = blk[sb][2] != 0 && c < cols;
-    float x[32];
+    int s;
+    uint32_t w[8];
+    if constexpr (sizeof(T) == 2) {
+      uint32_t pr[16];  // rows 2j, 2j+1 of the column as one pair
 #pragma unroll
-    for (int z = 0; z < 32; ++z) x[z] = to_f32(at(sb * 32 + z, cc));
-    float amax = 0.f;
+      for (int j = 0; j < 16; ++j) {
+        u16x2_t pj;
+        pj.x = at(sb * 32 + 2 * j, cc);
+        pj.y = at(sb * 32 + 2 * j + 1, cc);
+        pr[j] = __builtin_bit_cast(uint32_t, pj);
+      }
+      const int sbyte = scale_byte_bf16<16>(pr);
+      s = sbyte - 127;
+      quant_block_bf16(pr, sbyte, w);
+    } else {
+      float x[32];
 #pragma unroll
-    for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(x[z]));
-    const int s = mx_scale_exp(amax);
-    const uint32_t all = or4((ok ? 1u : 0u) << q4);
-    const uint32_t sw = or4((uint32_t)(s + 127) << (8 * q4));
-    if (ok) {
-      uint32_t w[8];
+      for (int z = 0; z < 32; ++z) x[z] = to_f32(at(sb * 32 + z, cc));
+      float amax = 0.f;
+#pragma unroll
+      for (int z = 0; z < 32; ++z) amax = fmaxf(amax, fabsf(x[z]));
+      s = mx_scale_exp(amax);
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         w[q] = e4m3_x4(ldexpf(x[q * 4], -s), ldexpf(x[q * 4 + 1], -s), ldexpf(x[q * 4 + 2], -s),
                        ldexpf(x[q * 4 + 3], -s));
+    }
+    const uint32_t all = or_n<NB>((ok ? 1u : 0u) << sb);
+    const uint32_t sw = or_n<NB>((uint32_t)(s + 127) << (8 * sb));
+    if (ok) {
       uint4* dst = (uint4*)(q_col + (long)c * ldc + base + sb * 32);
-      store_nt16(dst, make_uint4(w[0], w[1], w[2], w[3]));
-      store_nt16(dst + 1, make_uint4(w[4], w[5], w[6], w[7]));
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
       const int b = (base + sb * 32) >> 5;  // block along the padded rows
       uint8_t* sp = s_col + ((long)(b >> 2) * cols + c) * 4 + (b & 3);
-      if (col_dw && all == 15u) {
-        if (sb == 0) *(uint32_t*)sp = sw;
+      if (col_dw && all == (1u << NB) - 1) {  // the group's NB bytes at once (base is a multiple of RB)
+        if (sb == 0) {
+          if constexpr (NB == 4) *(uint32_t*)sp = sw;
+          else *(uint16_t*)sp = (uint16_t)sw;
+        }
       } else {
         *sp = (uint8_t)(s + 127);
       }
@@ -281,14 +365,15 @@ hipError_t launch_mx_quantize(const void* in, bool bf16, long ld_in, int rows, i
                               uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, long ldc,
                               hipStream_t s, const float* gate) {
   if (rows == 0 || max_blocks32 == 0) return hipSuccess;
-  const long nblk = (long)((max_blocks32 + 3) / 4) * ((cols + kMxCols - 1) / kMxCols);
+  constexpr int NB = kMxRows / 32;
+  const long nblk = (long)((max_blocks32 + NB - 1) / NB) * ((cols + kMxCols - 1) / kMxCols);
   if (nblk > 0x7FFFFFFFL) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)nblk;
   if (bf16)
-    mx_dual_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)in, ld_in, rows, cols, src, gk, gate, seg_off,
+    mx_dual_kernel<uint16_t, kMxRows><<<grid, 256, 0, s>>>((const uint16_t*)in, ld_in, rows, cols, src, gk, gate, seg_off,
                                                   seg_off128, nseg, seg_rows, q_row, s_row, q_col, s_col, ldc);
   else
-    mx_dual_kernel<float><<<grid, 256, 0, s>>>((const float*)in, ld_in, rows, cols, src, gk, gate, seg_off, seg_off128,
+    mx_dual_kernel<float, kMxRows><<<grid, 256, 0, s>>>((const float*)in, ld_in, rows, cols, src, gk, gate, seg_off, seg_off128,
                                                nseg, seg_rows, q_row, s_row, q_col, s_col, ldc);
   return hipGetLastError();
 }
