@@ -267,6 +267,26 @@ moe_status_t moe_router_bwd(const float* probs, const int32_t* topk_idx, const f
                             void* dx, void* dwr, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_router_bwd_unpermute: moe_unpermute_sum and moe_router_bwd (or, with a
+ * non-null aux_g, moe_router_bwd_aux) in one pass over dx, the input's whole
+ * gradient: the adjoint of the dispatch (routed rows written straight into
+ * the experts' buffers: Olmo-core 3 overview, "Routing and compute
+ * optimisation") plus the gradient through the gates into x:
+ *   dx[t] = sum_j dxp[pos[t,j]] + (dlogits wr)[t]
+ * summed in fp32 (the slots in order, then the router term) and rounded once
+ * to dt; dwr as moe_router_bwd.  dx is written, not read.
+ *   dxp [T*k, d] dt, 16-byte aligned: the expert-path input gradient in
+ *       expert order (moe_grouped_gemm_bwd's dxp); pos [T,k] from moe_route.
+ *   Other arguments, workspace (moe_router_bwd_workspace_size) and errors as
+ *   moe_router_bwd; aux_g may be null.
+ */
+moe_status_t moe_router_bwd_unpermute(const float* probs, const int32_t* topk_idx, const float* dgate,
+                                      const float* aux_g, const void* x, const void* wr,
+                                      const void* dxp, const int32_t* pos, int T, int d, int E, int k,
+                                      int dt, void* dx, void* dwr, void* ws, size_t ws_bytes,
+                                      void* stream);
+
+/*
  * Router balance step.  The pages warn that a routing balance score can
  * improve while the actual workload balance gets worse (token gerrymandering:
  * Olmo-core 3 overview, "Empirical findings beyond raw speed") but define no

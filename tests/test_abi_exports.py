@@ -75,6 +75,15 @@ def test_host_side_validation_without_gpu():
     assert st == 3 and b"g is not 16-byte aligned" in lib.moe_last_error_string()
     st = lib.moe_grouped_gemm_fwd(c, c, c, c, c, 2, 8, 64, 64, 1, None, ctypes.c_void_p(40), c, c, c, 1 << 20, None)
     assert st == 3 and b"u is not 16-byte aligned" in lib.moe_last_error_string()
+    # the fused dx pass needs dxp and pos (and 16-byte aligned dxp)
+    big = 1 << 30
+    st = lib.moe_router_bwd_unpermute(c, c, c, None, c, c, None, c, 4, 64, 8, 2, 1, c, c, c, big, None)
+    assert st == 1 and b"dxp is null" in lib.moe_last_error_string()
+    st = lib.moe_router_bwd_unpermute(c, c, c, None, c, c, ctypes.c_void_p(24), c, 4, 64, 8, 2, 1, c, c, c, big,
+                                      None)
+    assert st == 3 and b"dxp is not 16-byte aligned" in lib.moe_last_error_string()
+    st = lib.moe_router_bwd_unpermute(c, c, c, None, c, c, c, None, 4, 64, 8, 2, 1, c, c, c, big, None)
+    assert st == 1 and b"pos is null" in lib.moe_last_error_string()
 
 
 def test_mx_arg_structs_match_the_header(tmp_path):

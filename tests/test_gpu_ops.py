@@ -119,3 +119,58 @@ def test_router_backward(dt, T, d, E, k, acc):
     dL, rdwr, rdx = ref.router_backward(probs, rt["idx"], dgate, x, wr)
     assert_close("dwr", to_np(dwr), rdwr)
     assert_close("dx", to_np(dx), dx0.astype(np.float64) + rdx)
+
+
+@pytest.mark.parametrize("aux", [False, True])
+@pytest.mark.parametrize("dt,T,d,E,k", [("bf16", 1000, 2048, 8, 4), ("f32", 256, 128, 8, 2),
+                                        ("bf16", 700, 2048, 128, 4), ("bf16", 300, 6144, 384, 8),
+                                        ("bf16", 129, 512, 40, 3), ("bf16", 131, 320, 64, 1),
+                                        ("f32", 77, 96, 64, 5)])
+def test_router_backward_unpermute(dt, T, d, E, k, aux):
+    """moe_router_bwd_unpermute: dx = unpermute-sum of dXp + the router term in
+    one pass (one rounding) against the oracle; dWr identical to
+    moe_router_bwd's; dx within a rounding of the two-call path."""
+    from token_routing_grouped_amd import _abi
+
+    say(f"router bwd + unpermute {dt} T={T} d={d} E={E} k={k} aux={aux}")
+    rng = np.random.default_rng(11 * T + E + k)
+    x = inputs.bf16_round(rng.standard_normal((T, d)).astype(np.float32))
+    wr = inputs.bf16_round((rng.standard_normal((E, d)) * 0.02).astype(np.float32))
+    dxp = inputs.bf16_round((rng.standard_normal((T * k, d)) * 0.01).astype(np.float32))
+    L = ref.router_logits(x, wr).astype(np.float32)
+    rt = ref.route(L, k)
+    probs = rt["probs"].astype(np.float32)
+    dgate = rng.standard_normal((T, k)).astype(np.float32)
+    aux_g = (np.abs(rng.standard_normal(E)) * 0.1).astype(np.float32) if aux else None
+    args = dict(probs=_dev(probs, torch.float32), topk_idx=_dev(rt["idx"].astype(np.int32), torch.int32),
+                dgate=_dev(dgate, torch.float32), x=_dev(x, DT[dt]), wr=_dev(wr, DT[dt]))
+    pos = _dev(rt["pos"].astype(np.int32), torch.int32)
+    dxp_t = _dev(dxp, DT[dt])
+    ag = None if aux_g is None else _dev(aux_g, torch.float32)
+    ws = _abi.workspace(_abi.moe_router_bwd_workspace_size(T, d, E), DEV)
+    dx = torch.full((T, d), float("nan"), dtype=DT[dt], device=DEV)  # written, not read
+    dwr = torch.empty(E, d, dtype=DT[dt], device=DEV)
+    _abi.moe_router_bwd_unpermute(args["probs"], args["topk_idx"], args["dgate"], args["x"], args["wr"], dxp_t, pos,
+                                  dx, dwr, ws, aux_g=ag)
+    # the two-call path on the same inputs
+    dx2 = torch.empty(T, d, dtype=DT[dt], device=DEV)
+    dwr2 = torch.empty(E, d, dtype=DT[dt], device=DEV)
+    _abi.moe_unpermute_sum(dxp_t, pos, dx2)
+    if ag is None:
+        _abi.moe_router_bwd(args["probs"], args["topk_idx"], args["dgate"], args["x"], args["wr"], dx2, dwr2, ws)
+    else:
+        _abi.moe_router_bwd_aux(args["probs"], args["topk_idx"], args["dgate"], ag, args["x"], args["wr"], dx2, dwr2,
+                                ws)
+    torch.cuda.synchronize()
+    dL, rdwr, rdx = ref.router_backward(probs, rt["idx"], dgate, x, wr, aux_g=aux_g)
+    rdx_all = ref.unpermute_sum(dxp, rt["pos"]) + rdx
+    tol = 1e-2 if dt == "bf16" else 1e-5
+    assert_close("dx", to_np(dx), rdx_all, rel=tol, max_frac=2e-2 if dt == "bf16" else 1e-4)
+    assert_close("dwr", to_np(dwr), rdwr, rel=tol, max_frac=2e-2 if dt == "bf16" else 1e-4)
+    assert torch.equal(dwr, dwr2), "dwr differs from moe_router_bwd's"
+    # one rounding instead of two: apart by at most the two paths' rounding
+    # errors, a few units in the last place of the two terms' magnitudes
+    d1, d2 = to_np(dx).astype(np.float64), to_np(dx2).astype(np.float64)
+    ulp = 2.0 ** -7 if dt == "bf16" else 2.0 ** -22
+    mag = np.abs(ref.unpermute_sum(dxp, rt["pos"])) + np.abs(rdx)
+    assert np.all(np.abs(d1 - d2) <= 3 * ulp * mag + 1e-30)

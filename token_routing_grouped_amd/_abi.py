@@ -52,6 +52,7 @@ _SIGS = {
     "moe_router_bwd_workspace_size": ([_I, _I, _I], _Z),
     "moe_router_bwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "moe_router_bwd_aux": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "moe_router_bwd_unpermute": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "moe_balance_workspace_size": ([_I, _I], _Z),
     "moe_balance": ([_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _Z, _P], _I),
     "mx_quantize": ([_P, _I, _I, _I, _P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P], _I),
@@ -319,6 +320,22 @@ def moe_router_bwd(probs, topk_idx, dgate, x, wr, dx, dwr, ws):
     _expect(dwr, x.dtype, "dwr")
     _check(lib().moe_router_bwd(_p(probs), _p(topk_idx), _p(dgate), _p(x), _p(wr), T, d, E, k, _dt(x), _p(dx), _p(dwr),
                                 _p(ws), ws.numel(), _stream()), "moe_router_bwd")
+
+
+def moe_router_bwd_unpermute(probs, topk_idx, dgate, x, wr, dxp, pos, dx, dwr, ws, aux_g=None):
+    """dx = unpermute-sum of dxp + the router's input gradient (one pass,
+    one rounding); dwr as moe_router_bwd; aux_g adds the balance loss."""
+    T, d = x.shape
+    E = wr.shape[0]
+    k = topk_idx.shape[1]
+    _expect(dx, x.dtype, "dx")
+    _expect(dwr, x.dtype, "dwr")
+    _expect(dxp, x.dtype, "dxp")
+    if aux_g is not None:
+        _expect(aux_g, torch.float32, "aux_g")
+    _check(lib().moe_router_bwd_unpermute(_p(probs), _p(topk_idx), _p(dgate), _p(aux_g), _p(x), _p(wr), _p(dxp),
+                                          _p(pos), T, d, E, k, _dt(x), _p(dx), _p(dwr), _p(ws), ws.numel(),
+                                          _stream()), "moe_router_bwd_unpermute")
 
 
 def moe_router_bwd_aux(probs, topk_idx, dgate, aux_g, x, wr, dx, dwr, ws):

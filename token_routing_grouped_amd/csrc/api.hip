@@ -440,7 +440,8 @@ size_t moe_router_bwd_workspace_size(int T, int d, int E) {
 
 static moe_status_t router_bwd_impl(const char* fn, const float* probs, const int32_t* topk_idx, const float* dgate,
                                     const float* aux_g, const void* x, const void* wr, int T, int d, int E, int k,
-                                    int dt, void* dx, void* dwr, void* ws, size_t ws_bytes, void* stream) {
+                                    int dt, void* dx, void* dwr, void* ws, size_t ws_bytes, void* stream,
+                                    const void* dxp = nullptr, const int32_t* pos = nullptr, bool fused = false) {
   TRY(check_dt(fn, dt));
   TRY(check_tk(fn, T, k));
   if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
@@ -451,6 +452,7 @@ static moe_status_t router_bwd_impl(const char* fn, const float* probs, const in
   TRY(check_ptrs(fn, {{"wr", wr}, {"dwr", dwr}}));
   if (T > 0)
     TRY(check_ptrs(fn, {{"probs", probs}, {"topk_idx", topk_idx}, {"dgate", dgate}, {"x", x}, {"dx", dx}}));
+  if (fused && T > 0) TRY(check_ptrs(fn, {{"dxp", dxp}, {"pos", pos}}));
   const size_t need = trg::router_bwd_ws_bytes(T, d, E);
   if (ws == nullptr || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
@@ -458,7 +460,15 @@ static moe_status_t router_bwd_impl(const char* fn, const float* probs, const in
   TRY(check_device());
   trg::ProfScope ps(fn, (hipStream_t)stream);
   return hip_status(fn, trg::launch_router_bwd(probs, topk_idx, dgate, aux_g, x, wr, T, d, E, k, dt == MOE_BF16, dx,
-                                               dwr, ws, (hipStream_t)stream));
+                                               dwr, ws, (hipStream_t)stream, fused ? dxp : nullptr, pos));
+}
+
+moe_status_t moe_router_bwd_unpermute(const float* probs, const int32_t* topk_idx, const float* dgate,
+                                      const float* aux_g, const void* x, const void* wr, const void* dxp,
+                                      const int32_t* pos, int T, int d, int E, int k, int dt, void* dx, void* dwr,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  return router_bwd_impl("moe_router_bwd_unpermute", probs, topk_idx, dgate, aux_g, x, wr, T, d, E, k, dt, dx, dwr,
+                         ws, ws_bytes, stream, dxp, pos, true);
 }
 
 moe_status_t moe_router_bwd(const float* probs, const int32_t* topk_idx, const float* dgate, const void* x,

@@ -16,14 +16,19 @@
 //  * The MFMA is issued as (B fragment, A fragment): each lane then owns 4
 //    consecutive output columns of one row, stored as one 16-byte write.
 //  * One dense problem per launch, with an optional fixed-order split-K (fp32
-//    partials); epilogues: fp32 store, or read-add-write into a bf16 output.
+//    partials); epilogues: fp32 store, read-add-write into a bf16 output, or
+//    (the router's dx with the unpermute-sum folded in) the tile staged in LDS
+//    as fp32 and written as whole 16-byte row pieces of
+//    bf16(sum_j dxp[pos[m, j]] + product).  The last one reads each gathered
+//    row piece once and writes dx once, where read-add-write after a separate
+//    unpermute-sum moved dx three times.
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
 
 namespace trg {
 
-enum Epi { EPI_F32 = 1, EPI_ADD_BF16 = 4 };
+enum Epi { EPI_F32 = 1, EPI_ADD_BF16 = 4, EPI_UNPERMUTE = 8 };
 
 struct GemmArgs {
   // A[m][k]: K-contiguous -> A[m*lda + k]; MN-contiguous -> A[k*lda + m]
@@ -37,6 +42,10 @@ struct GemmArgs {
   int tiles_m, tiles_n;
   int ksplit_len;  // split-K: K elements per split (multiple of 64); 0 = none
   long c_split_stride;
+  // EPI_UNPERMUTE: C[m] = bf16(sum_j dxp[pos[m*k + j]] + product[m]), rows of ldc
+  const uint16_t* dxp;
+  const int* pos;
+  int k;
 };
 
 TRG_DEV bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -73,7 +82,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NB = BKC ? BN * 8 / 256 : ((BN + 255) / 256) * 8;
   static_assert(!AKC || (BM * 8) % 256 == 0, "A tile");
   static_assert(!BKC || (BN * 8) % 256 == 0, "B tile");
-  __shared__ uint4 smem[2 * STAGE];
+  constexpr int EP = BN + 4;  // fp32 row pitch of the staged tile (EPI_UNPERMUTE)
+  constexpr int SMEM = (EPI == EPI_UNPERMUTE && BM * EP / 4 > 2 * STAGE) ? BM * EP / 4 : 2 * STAGE;
+  __shared__ uint4 smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -238,6 +249,80 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   // Lane (lrow, lgrp) owns rows m = ... + lrow and 4 consecutive columns per
   // group q: n = ... + q*8 + lgrp + {0..3}.
   const int lrow = lane & 31, lgrp = (lane >> 5) * 4;
+  if constexpr (EPI == EPI_UNPERMUTE) {
+    // the product tile to LDS (the K loop ended with a barrier: the stages are free)
+    float* st = (float*)smem;
+    static_for<TM>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      static_for<TN>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        static_for<4>([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          const int r = wm * WTM + i * 32 + lrow, c = wn * WTN + j * 32 + q * 8 + lgrp;
+          *(float4*)(st + r * EP + c) = make_float4(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1],
+                                                    acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+        });
+      });
+    });
+    __syncthreads();
+    // 16-byte row pieces: 8 columns of one row; BN / 8 consecutive threads per
+    // row, NP pieces per thread.  The position and row piece loads of two
+    // slots of all NP pieces are issued together (one pair of round trips per
+    // two slots, not per piece and slot); the sums still take the slots in
+    // order.
+    constexpr int PPR = BN / 8, NP = BM * PPR / 256;
+    static_assert(BM * PPR % 256 == 0, "pieces per thread");
+    long mrow[NP];
+    int ncol[NP];
+    bool ok[NP];
+    float s[NP][8];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + 256 * i, r = p / PPR, c = (p % PPR) * 8;
+      mrow[i] = m0 + r;
+      ncol[i] = n0 + c;
+      ok[i] = mrow[i] < m_end && ncol[i] < g.N;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) s[i][z] = 0.f;
+    }
+    for (int j = 0; j < g.k; j += 2) {  // slots in order, fp32
+      const bool two = j + 1 < g.k;
+      int pj[2][NP];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        pj[0][i] = ok[i] ? g.pos[mrow[i] * g.k + j] : 0;
+        pj[1][i] = ok[i] && two ? g.pos[mrow[i] * g.k + j + 1] : 0;
+      }
+      uint4 v[2][NP];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+          v[q][i] = ok[i] && (q == 0 || two) ? *(const uint4*)(g.dxp + (long)pj[q][i] * g.ldc + ncol[i])
+                                             : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (q == 1 && !two) break;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const uint4 w = v[q][i];
+          s[i][0] += bf_lo(w.x); s[i][1] += bf_hi(w.x); s[i][2] += bf_lo(w.y); s[i][3] += bf_hi(w.y);
+          s[i][4] += bf_lo(w.z); s[i][5] += bf_hi(w.z); s[i][6] += bf_lo(w.w); s[i][7] += bf_hi(w.w);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (ok[i]) {
+        const int p = tid + 256 * i, r = p / PPR, c = (p % PPR) * 8;
+        const float4 a0 = *(const float4*)(st + r * EP + c), a1 = *(const float4*)(st + r * EP + c + 4);
+        *(uint4*)((uint16_t*)g.C + mrow[i] * g.ldc + ncol[i]) =
+            make_uint4(pack_bf2(s[i][0] + a0.x, s[i][1] + a0.y), pack_bf2(s[i][2] + a0.z, s[i][3] + a0.w),
+                       pack_bf2(s[i][4] + a1.x, s[i][5] + a1.y), pack_bf2(s[i][6] + a1.z, s[i][7] + a1.w));
+      }
+    }
+    return;
+  }
   static_for<TM>([&](auto I) {
     constexpr int i = decltype(I)::value;
     const int m = m0 + wm * WTM + i * 32 + lrow;
@@ -335,15 +420,20 @@ hipError_t launch_router_dwr_mfma(const uint16_t* dL, const uint16_t* x, uint16_
   return hipGetLastError();
 }
 
-hipError_t launch_router_dx_mfma(const uint16_t* dL, const uint16_t* wr, uint16_t* dx, int T, int d, int E,
-                                 hipStream_t s) {
+hipError_t launch_router_dx_mfma(const uint16_t* dL, const uint16_t* wr, uint16_t* dx, const uint16_t* dxp,
+                                 const int* pos, int k, int T, int d, int E, hipStream_t s) {
   GemmArgs a{};
   a.A = dL; a.lda = E;  // A[m=t][k=e] K-contiguous
   a.B = wr; a.ldb = d;  // B[n=c][k=e] = wr[e][c], MN-contiguous
   a.C = dx; a.ldc = d;
   a.M = T; a.N = d; a.K = E;
   a.tiles_m = cdiv(T, 128); a.tiles_n = cdiv(d, 128);
-  run<128, 128, 2, 2, true, false, EPI_ADD_BF16>("router_dx_mfma", a, a.tiles_m * a.tiles_n, s);
+  if (dxp != nullptr) {  // dx = unpermute-sum of dxp + dL wr
+    a.dxp = dxp; a.pos = pos; a.k = k;
+    run<128, 128, 2, 2, true, false, EPI_UNPERMUTE>("router_dx_mfma", a, a.tiles_m * a.tiles_n, s);
+  } else {
+    run<128, 128, 2, 2, true, false, EPI_ADD_BF16>("router_dx_mfma", a, a.tiles_m * a.tiles_n, s);
+  }
   return hipGetLastError();
 }
 

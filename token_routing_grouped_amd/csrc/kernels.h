@@ -31,9 +31,11 @@ hipError_t launch_combine_bwd(const void* dy, const void* yp, const float* w, co
 size_t router_bwd_ws_bytes(int T, int d, int E);
 hipError_t launch_router_logits(const void* x, bool bf16, const void* wr, int T, int d, int E, float* logits,
                                 hipStream_t s);
+// dxp == nullptr: dx += dlogits wr.  Otherwise dx = sum_j dxp[pos[t,j]] +
+// dlogits wr (the unpermute-sum folded in; dx is only written).
 hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dgate, const float* aux_g,
                              const void* x, const void* wr, int T, int d, int E, int k, bool bf16, void* dx, void* dwr,
-                             void* ws, hipStream_t s);
+                             void* ws, hipStream_t s, const void* dxp = nullptr, const int* pos = nullptr);
 size_t balance_ws_bytes(int T, int E);
 hipError_t launch_balance(const float* probs, const int* counts, int T, int E, int k, float alpha, float* stats,
                           float* aux_g, float* mean_probs, void* ws, hipStream_t s);
@@ -53,7 +55,8 @@ hipError_t launch_dense_nt_f32out(const uint16_t* A, const uint16_t* B, float* C
                                   hipStream_t s);
 hipError_t launch_router_dwr_mfma(const uint16_t* dL, const uint16_t* x, uint16_t* dwr, float* part, int T, int d,
                                   int E, hipStream_t s);
-hipError_t launch_router_dx_mfma(const uint16_t* dL, const uint16_t* wr, uint16_t* dx, int T, int d, int E,
+hipError_t launch_router_dx_mfma(const uint16_t* dL, const uint16_t* wr, uint16_t* dx, const uint16_t* dxp,
+                                 const int* pos, int k, int T, int d, int E,
                                  hipStream_t s);
 size_t router_dwr_mfma_part_bytes(int T, int d, int E);
 

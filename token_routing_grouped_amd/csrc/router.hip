@@ -239,27 +239,59 @@ __global__ __launch_bounds__(256) void chunk_sum_kernel(const float* __restrict_
 }
 
 // dx[t] += sum_e dL[t, e] Wr[e] for TPB = 4 tokens per workgroup: the Wr
-// row pieces a thread loads serve all TPB token rows.
+// row pieces a thread loads serve all TPB token rows.  With dxp the
+// expert-path term is summed here instead of read from dx (the unpermute-sum
+// folded in): dx[t] = sum_j dxp[pos[t, j]] + sum_e dL[t, e] Wr[e], the slots
+// summed in order in fp32 as the unpermute-sum does, then the router term,
+// one rounding.
 constexpr int kDxTokens = 4;
 template <class T, int EB>
 __global__ __launch_bounds__(256) void router_dx_valu_kernel(const float* __restrict__ dL, const T* __restrict__ wr,
-                                                             int Tn, int d, int E, T* __restrict__ dx) {
+                                                             int Tn, int d, int E, T* __restrict__ dx,
+                                                             const T* __restrict__ dxp, const int* __restrict__ pos,
+                                                             int k) {
   constexpr int V = Elt<T>::kVec;
   constexpr int TPB = kDxTokens;
   __shared__ float sdl[TPB][EB];
+  __shared__ int spos[TPB][32];  // the tokens' slot positions (k <= 32; rows past Tn: row Tn - 1's)
   const int t0 = blockIdx.x * TPB;
   for (int i = threadIdx.x; i < TPB * EB; i += 256) {
     const int u = i / EB, e = i % EB;
     sdl[u][e] = (t0 + u < Tn && e < E) ? dL[(long)(t0 + u) * E + e] : 0.f;
   }
+  if (dxp != nullptr)
+    for (int i = threadIdx.x; i < TPB * k; i += 256) {
+      const int u = i / k, j = i % k;
+      spos[u][j] = pos[(long)min(t0 + u, Tn - 1) * k + j];
+    }
   __syncthreads();
   const int nv = d / V;
   for (int v = threadIdx.x; v < nv; v += 256) {
     // the expert-path gradient rows (rows past Tn read row Tn - 1 and are
     // never written), added after the router term
-    uint4 rv[TPB];
+    float base[TPB][V];
+    if (dxp == nullptr) {
 #pragma unroll
-    for (int u = 0; u < TPB; ++u) rv[u] = ((const uint4*)(dx + (long)min(t0 + u, Tn - 1) * d))[v];
+      for (int u = 0; u < TPB; ++u) unpack16<T>(((const uint4*)(dx + (long)min(t0 + u, Tn - 1) * d))[v], base[u]);
+    } else {  // slot j's rows of all TPB tokens loaded together
+#pragma unroll
+      for (int u = 0; u < TPB; ++u)
+#pragma unroll
+        for (int i = 0; i < V; ++i) base[u][i] = 0.f;
+      for (int j = 0; j < k; ++j) {
+        uint4 rv[TPB];
+#pragma unroll
+        for (int u = 0; u < TPB; ++u)
+          rv[u] = ((const uint4*)(dxp + (long)spos[u][j] * d))[v];
+#pragma unroll
+        for (int u = 0; u < TPB; ++u) {
+          float f[V];
+          unpack16<T>(rv[u], f);
+#pragma unroll
+          for (int i = 0; i < V; ++i) base[u][i] += f[i];
+        }
+      }
+    }
     float acc[TPB][V];
 #pragma unroll
     for (int u = 0; u < TPB; ++u)
@@ -288,10 +320,8 @@ __global__ __launch_bounds__(256) void router_dx_valu_kernel(const float* __rest
 #pragma unroll
     for (int u = 0; u < TPB; ++u) {
       if (t0 + u < Tn) {
-        float g[V];
-        unpack16<T>(rv[u], g);
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[u][i] += g[i];
+        for (int i = 0; i < V; ++i) acc[u][i] += base[u][i];
         ((uint4*)(dx + (long)(t0 + u) * d))[v] = pack16<T>(acc[u]);
       }
     }
@@ -341,7 +371,7 @@ hipError_t launch_router_logits(const void* x, bool bf16, const void* wr, int T,
 
 template <class T, int EB>
 static void bwd_valu(const float* dL, const void* x, const void* wr, int Tn, int d, int E, void* dx, void* dwr,
-                     float* part, hipStream_t s) {
+                     float* part, hipStream_t s, const void* dxp, const int* pos, int k) {
   const int nch = (Tn + kDwrChunk - 1) / kDwrChunk;
   constexpr int CV = 64 / EB;
   constexpr int cols_per_block = 32 * CV;
@@ -350,21 +380,22 @@ static void bwd_valu(const float* dL, const void* x, const void* wr, int Tn, int
   else router_dwr_partial_kernel<T, EB, true><<<grid, 256, 0, s>>>(dL, (const T*)x, Tn, d, E, part);
   const long n = (long)E * d;
   chunk_sum_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, nch, n, (T*)dwr);
-  router_dx_valu_kernel<T, EB><<<(Tn + kDxTokens - 1) / kDxTokens, 256, 0, s>>>(dL, (const T*)wr, Tn, d, E, (T*)dx);
+  router_dx_valu_kernel<T, EB><<<(Tn + kDxTokens - 1) / kDxTokens, 256, 0, s>>>(dL, (const T*)wr, Tn, d, E, (T*)dx,
+                                                                                (const T*)dxp, pos, k);
 }
 
 template <class T>
 static void bwd_valu_any(const float* dL, const void* x, const void* wr, int Tn, int d, int E, void* dx, void* dwr,
-                         float* part, hipStream_t s) {
-  if (E <= 8) bwd_valu<T, 8>(dL, x, wr, Tn, d, E, dx, dwr, part, s);
-  else if (E <= 16) bwd_valu<T, 16>(dL, x, wr, Tn, d, E, dx, dwr, part, s);
-  else if (E <= 32) bwd_valu<T, 32>(dL, x, wr, Tn, d, E, dx, dwr, part, s);
-  else bwd_valu<T, 64>(dL, x, wr, Tn, d, E, dx, dwr, part, s);
+                         float* part, hipStream_t s, const void* dxp, const int* pos, int k) {
+  if (E <= 8) bwd_valu<T, 8>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k);
+  else if (E <= 16) bwd_valu<T, 16>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k);
+  else if (E <= 32) bwd_valu<T, 32>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k);
+  else bwd_valu<T, 64>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k);
 }
 
 hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dgate, const float* aux_g,
                              const void* x, const void* wr, int T, int d, int E, int k, bool bf16, void* dx, void* dwr,
-                             void* ws, hipStream_t s) {
+                             void* ws, hipStream_t s, const void* dxp, const int* pos) {
   const bool mf = router_uses_mfma(bf16, E);
   if (!mf && E > 64) return hipErrorInvalidValue;
   char* p = (char*)ws;
@@ -389,10 +420,10 @@ hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dg
   if (mf) {
     hipError_t err = launch_router_dwr_mfma(dLb, (const uint16_t*)x, (uint16_t*)dwr, part, T, d, E, s);
     if (err != hipSuccess) return err;
-    return launch_router_dx_mfma(dLb, (const uint16_t*)wr, (uint16_t*)dx, T, d, E, s);
+    return launch_router_dx_mfma(dLb, (const uint16_t*)wr, (uint16_t*)dx, (const uint16_t*)dxp, pos, k, T, d, E, s);
   }
-  if (bf16) bwd_valu_any<uint16_t>(dL, x, wr, T, d, E, dx, dwr, part, s);
-  else bwd_valu_any<float>(dL, x, wr, T, d, E, dx, dwr, part, s);
+  if (bf16) bwd_valu_any<uint16_t>(dL, x, wr, T, d, E, dx, dwr, part, s, dxp, pos, k);
+  else bwd_valu_any<float>(dL, x, wr, T, d, E, dx, dwr, part, s, dxp, pos, k);
   return hipGetLastError();
 }
 

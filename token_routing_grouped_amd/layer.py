@@ -50,6 +50,10 @@ class MoELayerGPU:
         # overlap: the weight-gradient GEMMs run on a second stream (default
         # priority) next to the dgrad chain, joined by events
         self.overlap = bool(overlap)
+        # with two streams: whether the dx pass (unpermute-sum + router
+        # backward) runs before the main stream joins the side stream's weight
+        # gradients, i.e. next to them
+        self.dx_before_join = True
         self.R = R = T * k
         self.dtype = dtype
         self.mx = mx
@@ -191,14 +195,13 @@ class MoELayerGPU:
         else:
             _abi.moe_grouped_gemm_bwd(self.dyp, self.xp, self.g, self.u, self.hb, w1, w3, w2, self.offsets, self.dgu,
                                       self.dxp, self.dw1, self.dw3, self.dw2, self.ws_gemm)
-        _abi.moe_unpermute_sum(self.dxp, self.pos, self.dx)
-        if self.overlap:
+        # dx in one pass: the unpermute-sum of dXp plus the router's term
+        if self.overlap and not self.dx_before_join:
             torch.cuda.current_stream().wait_event(self._ev_side_done)
-        if self.aux_alpha > 0.0:
-            _abi.moe_router_bwd_aux(self.probs, self.topk_idx, self.dgate, self.aux_g, x, wr, self.dx, self.dwr,
-                                    self.ws_router)
-        else:
-            _abi.moe_router_bwd(self.probs, self.topk_idx, self.dgate, x, wr, self.dx, self.dwr, self.ws_router)
+        _abi.moe_router_bwd_unpermute(self.probs, self.topk_idx, self.dgate, x, wr, self.dxp, self.pos, self.dx,
+                                      self.dwr, self.ws_router, aux_g=self.aux_g if self.aux_alpha > 0.0 else None)
+        if self.overlap and self.dx_before_join:
+            torch.cuda.current_stream().wait_event(self._ev_side_done)
         return self.dx
 
     def balance(self, alpha=None):
