@@ -381,8 +381,8 @@ hipError_t launch_dense_nt_f32out(const uint16_t* A, const uint16_t* B, float* C
   a.B = B; a.ldb = K;
   a.C = C; a.ldc = N;
   a.M = M; a.N = N; a.K = K;
-  a.tiles_m = cdiv(M, 128); a.tiles_n = cdiv(N, 128);
-  run<128, 128, 2, 2, true, true, EPI_F32>("router_logits_mfma", a, a.tiles_m * a.tiles_n, s);
+  a.tiles_m = cdiv(M, 64); a.tiles_n = cdiv(N, 128);
+  run<64, 128, 1, 4, true, true, EPI_F32>("router_logits_mfma", a, a.tiles_m * a.tiles_n, s);
   return hipGetLastError();
 }
 
