@@ -245,7 +245,10 @@ enum {
   MOE_BWD_WGRAD_DOWN = 2,
   MOE_BWD_DGRAD_UP = 4,
   MOE_BWD_WGRAD_UP = 8,
-  MOE_BWD_ALL = 15
+  MOE_BWD_ALL = 15,
+  /* MXFP8 parts only (moe_grouped_gemm_bwd_mx_parts): */
+  MOE_BWD_MX_QUANT_DY = 16, /* make dYp's MX copies (nothing else unless other bits are set) */
+  MOE_BWD_MX_DY_READY = 32  /* with MOE_BWD_DGRAD_DOWN: dYp's copies exist, do not remake them */
 };
 moe_status_t moe_grouped_gemm_bwd_parts(const void* dyp, const void* xp, const void* g, const void* u,
                                         const void* hbuf, const void* w1, const void* w3, const void* w2,
@@ -420,10 +423,12 @@ moe_status_t moe_grouped_gemm_bwd_mx(const moe_mx_bwd_args* args, void* stream);
  * moe_grouped_gemm_bwd_mx_parts: moe_grouped_gemm_bwd_mx restricted to a
  * subset (MOE_BWD_* mask) of its four GEMMs, for two streams as with
  * moe_grouped_gemm_bwd_parts.  MOE_BWD_DGRAD_DOWN also makes dYp's MX copies
- * (dyq/dys, dyqT/dysT) before its GEMM and dG|dU's (dguq/dgus, dguqT/dgusT)
- * after it, so MOE_BWD_WGRAD_DOWN and MOE_BWD_WGRAD_UP need that part done
- * and MOE_BWD_DGRAD_UP too.  Calls that may run concurrently need separate
- * workspaces.  Same arguments and checks as moe_grouped_gemm_bwd_mx.
+ * (dyq/dys, dyqT/dysT) before its GEMM, unless MOE_BWD_MX_DY_READY is set
+ * (an earlier MOE_BWD_MX_QUANT_DY call made them), and dG|dU's (dguq/dgus,
+ * dguqT/dgusT) after it.  MOE_BWD_WGRAD_DOWN needs dYp's copies (either
+ * way), MOE_BWD_WGRAD_UP and MOE_BWD_DGRAD_UP need the dgrad-down part done.
+ * Calls that may run concurrently need separate workspaces.  Same arguments
+ * and checks as moe_grouped_gemm_bwd_mx.
  */
 moe_status_t moe_grouped_gemm_bwd_mx_parts(const moe_mx_bwd_args* args, unsigned parts, void* stream);
 /*

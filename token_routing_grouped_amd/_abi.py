@@ -277,6 +277,7 @@ def moe_grouped_gemm_fwd(xp, w1, w3, w2, offsets, g, u, hbuf, yp, ws):
 
 
 BWD_DGRAD_DOWN, BWD_WGRAD_DOWN, BWD_DGRAD_UP, BWD_WGRAD_UP, BWD_ALL = 1, 2, 4, 8, 15
+BWD_MX_QUANT_DY, BWD_MX_DY_READY = 16, 32  # MXFP8 parts only
 
 
 def moe_grouped_gemm_bwd_parts(dyp, xp, g, u, hbuf, w1, w3, w2, offsets, dgu, dxp, dw1, dw3, dw2, parts, ws):

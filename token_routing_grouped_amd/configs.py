@@ -58,7 +58,7 @@ CONFIGS = {
     "mxfp8": LayerConfig("mxfp8", T=16384, d=2048, E=128, k=4, h=1024, dtype="bf16", seed=2,
                          modes=("router", "uniform"), mx=True, overlap=True),
     "mxfp8_small": LayerConfig("mxfp8_small", T=8192, d=2048, E=8, k=4, h=1024, dtype="bf16",
-                               seed=1, mx=True),
+                               seed=1, mx=True, overlap=True),
     "trillion": LayerConfig("trillion", T=4096, d=6144, E=384, k=8, h=2048, dtype="bf16", seed=4,
                             modes=("uniform",)),
 }

@@ -591,8 +591,13 @@ moe_status_t moe_grouped_gemm_recompute_gu_mx(const moe_mx_fwd_args* a, void* st
 
 static moe_status_t ggemm_bwd_mx_impl(const char* fn, const moe_mx_bwd_args* a, unsigned parts, void* stream) {
   if (!a) return fail(MOE_ERR_INVALID_ARG, "%s: args is null", fn);
-  if (parts == 0 || (parts & ~(unsigned)MOE_BWD_ALL) != 0)
-    return fail(MOE_ERR_INVALID_ARG, "%s: parts must be a non-empty subset of MOE_BWD_ALL", fn);
+  const unsigned mx_all = MOE_BWD_ALL | MOE_BWD_MX_QUANT_DY | MOE_BWD_MX_DY_READY;
+  if ((parts & ~mx_all) != 0 || (parts & (MOE_BWD_ALL | MOE_BWD_MX_QUANT_DY)) == 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: parts must be a non-empty subset of MOE_BWD_ALL | MOE_BWD_MX_QUANT_DY "
+                "(with MOE_BWD_MX_DY_READY only beside MOE_BWD_DGRAD_DOWN)", fn);
+  if ((parts & MOE_BWD_MX_DY_READY) && (!(parts & MOE_BWD_DGRAD_DOWN) || (parts & MOE_BWD_MX_QUANT_DY)))
+    return fail(MOE_ERR_INVALID_ARG, "%s: MOE_BWD_MX_DY_READY goes with MOE_BWD_DGRAD_DOWN and without "
+                "MOE_BWD_MX_QUANT_DY", fn);
   TRY(check_mx_dims(fn, a->E, a->R, a->d, a->h, a->rcap, a->ws, a->ws_bytes));
   TRY(check_ptrs(fn, {{"offsets", a->offsets}, {"off128", a->off128}, {"w1tq", a->w1tq}, {"w1ts", a->w1ts},
                       {"w3tq", a->w3tq}, {"w3ts", a->w3ts}, {"w2tq", a->w2tq}, {"w2ts", a->w2ts}, {"dw1", a->dw1},

@@ -426,11 +426,13 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, unsigned parts, hipStream_t s) {
   return hipGetLastError();
 }
 
-// parts (MOE_BWD_* mask): DGRAD_DOWN also quantises dYp before its GEMM and
-// dG|dU after it, so WGRAD_DOWN and WGRAD_UP may start once it is done.
+// parts (MOE_BWD_* mask): DGRAD_DOWN also quantises dYp before its GEMM
+// (unless MX_DY_READY) and dG|dU after it; MX_QUANT_DY quantises dYp alone,
+// so WGRAD_DOWN may start as soon as that is done, WGRAD_UP once DGRAD_DOWN is.
 hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
-  if (parts & MOE_BWD_DGRAD_DOWN) {  // dYp -> rowwise (dgrad down) and columnwise per expert (wgrad down)
+  if ((parts & MOE_BWD_MX_QUANT_DY) || ((parts & MOE_BWD_DGRAD_DOWN) && !(parts & MOE_BWD_MX_DY_READY))) {
+    // dYp -> rowwise (dgrad down) and columnwise per expert (wgrad down)
     ProfScope ps("mx_quantize_dy", s);
     // from the stored dYp, or straight from dy (row r: topk_w[src[r]] * dy[src[r] / k])
     const bool from_dy = p.dyp == nullptr;

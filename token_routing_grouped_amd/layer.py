@@ -54,6 +54,9 @@ class MoELayerGPU:
         # backward) runs before the main stream joins the side stream's weight
         # gradients, i.e. next to them
         self.dx_before_join = True
+        # MXFP8 with two streams: wgrad-down starts as soon as dYp's MX copies
+        # exist (next to dgrad-down) instead of after dgrad-down
+        self.mx_early_wgrad_down = True
         self.R = R = T * k
         self.dtype = dtype
         self.mx = mx
@@ -221,17 +224,28 @@ class MoELayerGPU:
                     dw2=self.dw2, ws=ws, ws_bytes=ws.numel())
 
     def _backward_gemms_two_streams_mx(self):
-        """MXFP8: dgrad-down (which also makes the MX copies of dYp and dG|dU)
-        on the current stream, then both weight gradients on the side stream
-        while dgrad-up runs."""
+        """MXFP8: dYp's MX copies, then wgrad-down on the side stream next to
+        dgrad-down (which also makes dG|dU's copies) on the current stream,
+        then wgrad-up on the side stream while dgrad-up runs."""
         main, side = torch.cuda.current_stream(), self.side_stream
-        _abi.moe_grouped_gemm_bwd_mx_parts(_abi.BWD_DGRAD_DOWN, **self._mx_bwd_fields(self.ws_gemm))
+        if self.mx_early_wgrad_down:
+            _abi.moe_grouped_gemm_bwd_mx_parts(_abi.BWD_MX_QUANT_DY, **self._mx_bwd_fields(self.ws_gemm))
+            ev_dy = torch.cuda.Event()
+            ev_dy.record(main)
+            with torch.cuda.stream(side):
+                side.wait_event(ev_dy)
+                _abi.moe_grouped_gemm_bwd_mx_parts(_abi.BWD_WGRAD_DOWN, **self._mx_bwd_fields(self.ws_gemm2))
+            _abi.moe_grouped_gemm_bwd_mx_parts(_abi.BWD_DGRAD_DOWN | _abi.BWD_MX_DY_READY,
+                                               **self._mx_bwd_fields(self.ws_gemm))
+            side_parts = _abi.BWD_WGRAD_UP
+        else:
+            _abi.moe_grouped_gemm_bwd_mx_parts(_abi.BWD_DGRAD_DOWN, **self._mx_bwd_fields(self.ws_gemm))
+            side_parts = _abi.BWD_WGRAD_DOWN | _abi.BWD_WGRAD_UP
         ev = torch.cuda.Event()
         ev.record(main)
         with torch.cuda.stream(side):
             side.wait_event(ev)
-            _abi.moe_grouped_gemm_bwd_mx_parts(_abi.BWD_WGRAD_DOWN | _abi.BWD_WGRAD_UP,
-                                               **self._mx_bwd_fields(self.ws_gemm2))
+            _abi.moe_grouped_gemm_bwd_mx_parts(side_parts, **self._mx_bwd_fields(self.ws_gemm2))
             self._ev_side_done = torch.cuda.Event()
             self._ev_side_done.record(side)
         _abi.moe_grouped_gemm_bwd_mx_parts(_abi.BWD_DGRAD_UP, **self._mx_bwd_fields(self.ws_gemm))
