@@ -340,17 +340,21 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
         w[q] = e4m3_x4(ldexpf(x[q * 4], -s), ldexpf(x[q * 4 + 1], -s), ldexpf(x[q * 4 + 2], -s),
                        ldexpf(x[q * 4 + 3], -s));
     }
-    const uint32_t all = or_n<NB>((ok ? 1u : 0u) << sb);
-    const uint32_t sw = or_n<NB>((uint32_t)(s + 127) << (8 * sb));
+    // scale bytes in groups of G neighbouring lanes (blocks): one dword (G =
+    // 4) or half dword (G = 2) from the group's first lane
+    constexpr int G = NB < 4 ? NB : 4;
+    const int sg = sb % G;
+    const uint32_t all = or_n<G>((ok ? 1u : 0u) << sg);
+    const uint32_t sw = or_n<G>((uint32_t)(s + 127) << (8 * sg));
     if (ok) {
       uint4* dst = (uint4*)(q_col + (long)c * ldc + base + sb * 32);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
       const int b = (base + sb * 32) >> 5;  // block along the padded rows
       uint8_t* sp = s_col + ((long)(b >> 2) * cols + c) * 4 + (b & 3);
-      if (col_dw && all == (1u << NB) - 1) {  // the group's NB bytes at once (base is a multiple of RB)
-        if (sb == 0) {
-          if constexpr (NB == 4) *(uint32_t*)sp = sw;
+      if (col_dw && all == (1u << G) - 1) {  // the group's G bytes at once (base is a multiple of RB)
+        if (sg == 0) {
+          if constexpr (G == 4) *(uint32_t*)sp = sw;
           else *(uint16_t*)sp = (uint16_t)sw;
         }
       } else {
