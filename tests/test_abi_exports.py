@@ -168,5 +168,13 @@ def test_host_validation_of_the_next_rows():
     # MXFP8 backward parts: empty and out-of-range masks are refused before anything else
     a = _abi.MxBwdArgs(E=2, R=8, d=128, h=128, rcap=512)
     assert lib.moe_grouped_gemm_bwd_mx_parts(ctypes.byref(a), 0, None) == 1
-    assert lib.moe_grouped_gemm_bwd_mx_parts(ctypes.byref(a), 16, None) == 1
+    assert lib.moe_grouped_gemm_bwd_mx_parts(ctypes.byref(a), 64, None) == 1
     assert b"parts" in lib.moe_last_error_string()
+    # MOE_BWD_MX_DY_READY only beside MOE_BWD_DGRAD_DOWN, never with MOE_BWD_MX_QUANT_DY
+    for bad in (_abi.BWD_MX_DY_READY, _abi.BWD_MX_DY_READY | _abi.BWD_WGRAD_DOWN,
+                _abi.BWD_MX_DY_READY | _abi.BWD_DGRAD_DOWN | _abi.BWD_MX_QUANT_DY):
+        assert lib.moe_grouped_gemm_bwd_mx_parts(ctypes.byref(a), bad, None) == 1
+        assert b"MOE_BWD_MX_DY_READY" in lib.moe_last_error_string()
+    # a valid mask gets past the mask check (and then stops at the null buffers)
+    assert lib.moe_grouped_gemm_bwd_mx_parts(ctypes.byref(a), _abi.BWD_MX_QUANT_DY, None) != 0
+    assert b"is null" in lib.moe_last_error_string()
