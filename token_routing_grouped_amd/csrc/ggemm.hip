@@ -253,14 +253,23 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_kernel(Args g) {
       // Scheduling fences keep the next slice's reads ahead of this slice's
       // MFMAs (two fragment sets stay live instead of one re-used per MFMA).
       __builtin_amdgcn_sched_barrier(0);
+      // Ragged K: an expert's last step may hold fewer than BK rows; its rows
+      // past k_end read as zero, so when it holds at most half a step the
+      // upper half's slices add nothing and are skipped (short segments: 85
+      // rows per expert take two steps, the second a third full).  One
+      // uniform test per step: per-slice tests slowed the full steps.
+      const bool upper = MODE != RAGGED_K || cur.k_end - cur.k0 - it * BK > BK / 2;
       static_for<BK / 16>([&](auto KK) {
         constexpr int kk = decltype(KK)::value;
         constexpr int fb = kk & 1;  // fragment set of this slice
+        if (kk >= BK / 32 && !upper) return;
         if constexpr (kk + 1 < BK / 16) {
+          if (kk + 1 < BK / 32 || upper) {
 #pragma unroll
-          for (int i = 0; i < TM; ++i) af[fb ^ 1][i] = frag<BM, AKC>(sA, wm * WTM + i * 32, kk + 1, lane);
+            for (int i = 0; i < TM; ++i) af[fb ^ 1][i] = frag<BM, AKC>(sA, wm * WTM + i * 32, kk + 1, lane);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) bfr[fb ^ 1][j] = frag<BN, BKC>(sB, wn * WTN + j * 32, kk + 1, lane);
+            for (int j = 0; j < TN; ++j) bfr[fb ^ 1][j] = frag<BN, BKC>(sB, wn * WTN + j * 32, kk + 1, lane);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
