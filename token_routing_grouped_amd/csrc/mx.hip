@@ -153,11 +153,12 @@ TRG_DEV bool mx_block_rows(int base32, int rows, const int* seg_off, const int* 
 //   of a row are neighbouring lanes, so each row's 128 payload bytes go out as
 //   one piece and its 4 scale bytes as one dword (RB/64 units per thread);
 //   columnwise pass: unit u -> column u/NB, 32-row block u%NB: NB*32 payload
-//   bytes of a column as one piece, its NB scale bytes as one dword (NB = 4)
-//   or half dword (NB = 2) (NB/2 units per thread).
+//   bytes of a column as one piece, its scale bytes as dwords (four blocks
+//   each) or, for NB = 2, a half dword (NB/2 units per thread).
 // RB = 128 makes each column's payload piece one whole 128-byte line: with RB
 // = 64 (half the LDS, twice the workgroups per CU) the half-line pieces made
-// the weights' two-layout pass 30% slower.
+// the weights' two-layout pass 30% slower, and RB = 256 (two-line pieces, two
+// workgroups per CU) 5% slower.
 template <class T, int RB>
 __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, long ld_in, int rows, int cols,
                                                       const int* __restrict__ src, int gk,
