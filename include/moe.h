@@ -288,6 +288,22 @@ moe_status_t moe_router_bwd_unpermute(const float* probs, const int32_t* topk_id
                                       const void* dxp, const int32_t* pos, int T, int d, int E, int k,
                                       int dt, void* dx, void* dwr, void* ws, size_t ws_bytes,
                                       void* stream);
+/*
+ * moe_router_bwd_unpermute_parts: moe_router_bwd_unpermute restricted to its
+ * dwr part (MOE_ROUTER_DWR: needs dgate, not dxp) or its dx part
+ * (MOE_ROUTER_DX: needs dxp), so that dwr can run on a second stream as soon
+ * as the combine backward has written dgate.  Each part recomputes dlogits in
+ * its own workspace: calls that may run concurrently need separate
+ * workspaces.  A part's unused pointers may be null (dwr and x without
+ * MOE_ROUTER_DWR; dx, wr, dxp and pos without MOE_ROUTER_DX).  Both parts
+ * together equal moe_router_bwd_unpermute bit for bit.
+ */
+enum { MOE_ROUTER_DWR = 1, MOE_ROUTER_DX = 2 };
+moe_status_t moe_router_bwd_unpermute_parts(const float* probs, const int32_t* topk_idx,
+                                            const float* dgate, const float* aux_g, const void* x,
+                                            const void* wr, const void* dxp, const int32_t* pos, int T,
+                                            int d, int E, int k, int dt, void* dx, void* dwr, void* ws,
+                                            size_t ws_bytes, unsigned parts, void* stream);
 
 /*
  * Router balance step.  The pages warn that a routing balance score can

@@ -113,7 +113,7 @@ def test_step_writes_only_its_buffers(case):
     layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, **flags)
     names = ROUTING + FLOAT_OUT + WORKSPACES + (["xp"] if not flags.get("mx") else MX_BUFS)
     if flags.get("overlap"):
-        names.append("ws_gemm2")
+        names += ["ws_gemm2", "ws_router2"]
     guards = _install_guards(layer, names)
     layer.step(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"], forced_idx=fi)
     torch.cuda.synchronize()

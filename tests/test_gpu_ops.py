@@ -174,3 +174,31 @@ def test_router_backward_unpermute(dt, T, d, E, k, aux):
     ulp = 2.0 ** -7 if dt == "bf16" else 2.0 ** -22
     mag = np.abs(ref.unpermute_sum(dxp, rt["pos"])) + np.abs(rdx)
     assert np.all(np.abs(d1 - d2) <= 3 * ulp * mag + 1e-30)
+
+
+@pytest.mark.parametrize("dt,T,d,E,k", [("bf16", 1000, 2048, 8, 4), ("bf16", 700, 2048, 128, 4), ("f32", 77, 96, 64, 5)])
+def test_router_backward_parts_equal_the_whole_call(dt, T, d, E, k):
+    """moe_router_bwd_unpermute_parts: the dWr part and the dx part, each with
+    its own workspace, give the one-call result bit for bit."""
+    from token_routing_grouped_amd import _abi
+
+    say(f"router bwd parts {dt} T={T} d={d} E={E} k={k}")
+    rng = np.random.default_rng(17 * T + E)
+    x = _dev(inputs.bf16_round(rng.standard_normal((T, d)).astype(np.float32)), DT[dt])
+    wr = _dev(inputs.bf16_round((rng.standard_normal((E, d)) * 0.02).astype(np.float32)), DT[dt])
+    dxp = _dev(inputs.bf16_round((rng.standard_normal((T * k, d)) * 0.01).astype(np.float32)), DT[dt])
+    rt = ref.route(ref.router_logits(to_np(x), to_np(wr)).astype(np.float32), k)
+    probs = _dev(rt["probs"].astype(np.float32), torch.float32)
+    idx = _dev(rt["idx"].astype(np.int32), torch.int32)
+    pos = _dev(rt["pos"].astype(np.int32), torch.int32)
+    dgate = _dev(rng.standard_normal((T, k)).astype(np.float32), torch.float32)
+    ws1 = _abi.workspace(_abi.moe_router_bwd_workspace_size(T, d, E), DEV)
+    ws2 = _abi.workspace(_abi.moe_router_bwd_workspace_size(T, d, E), DEV)
+    dx, dwr = torch.empty(T, d, dtype=DT[dt], device=DEV), torch.empty(E, d, dtype=DT[dt], device=DEV)
+    _abi.moe_router_bwd_unpermute(probs, idx, dgate, x, wr, dxp, pos, dx, dwr, ws1)
+    dx2 = torch.full((T, d), float("nan"), dtype=DT[dt], device=DEV)
+    dwr2 = torch.full((E, d), float("nan"), dtype=DT[dt], device=DEV)
+    _abi.moe_router_bwd_unpermute_parts(_abi.ROUTER_DWR, probs, idx, dgate, x, wr, None, None, None, dwr2, ws2)
+    _abi.moe_router_bwd_unpermute_parts(_abi.ROUTER_DX, probs, idx, dgate, x, wr, dxp, pos, dx2, None, ws1)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx2) and torch.equal(dwr, dwr2)

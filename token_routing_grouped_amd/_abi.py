@@ -53,6 +53,8 @@ _SIGS = {
     "moe_router_bwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "moe_router_bwd_aux": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "moe_router_bwd_unpermute": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "moe_router_bwd_unpermute_parts": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z,
+                                        ctypes.c_uint, _P], _I),
     "moe_balance_workspace_size": ([_I, _I], _Z),
     "moe_balance": ([_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _Z, _P], _I),
     "mx_quantize": ([_P, _I, _I, _I, _P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P], _I),
@@ -337,6 +339,26 @@ def moe_router_bwd_unpermute(probs, topk_idx, dgate, x, wr, dxp, pos, dx, dwr, w
     _check(lib().moe_router_bwd_unpermute(_p(probs), _p(topk_idx), _p(dgate), _p(aux_g), _p(x), _p(wr), _p(dxp),
                                           _p(pos), T, d, E, k, _dt(x), _p(dx), _p(dwr), _p(ws), ws.numel(),
                                           _stream()), "moe_router_bwd_unpermute")
+
+
+ROUTER_DWR, ROUTER_DX = 1, 2
+
+
+def moe_router_bwd_unpermute_parts(parts, probs, topk_idx, dgate, x, wr, dxp, pos, dx, dwr, ws, aux_g=None):
+    """moe_router_bwd_unpermute restricted to ROUTER_DWR and / or ROUTER_DX."""
+    T, d = x.shape
+    E = wr.shape[0]
+    k = topk_idx.shape[1]
+    if parts & ROUTER_DX:
+        _expect(dx, x.dtype, "dx")
+        _expect(dxp, x.dtype, "dxp")
+    if parts & ROUTER_DWR:
+        _expect(dwr, x.dtype, "dwr")
+    if aux_g is not None:
+        _expect(aux_g, torch.float32, "aux_g")
+    _check(lib().moe_router_bwd_unpermute_parts(_p(probs), _p(topk_idx), _p(dgate), _p(aux_g), _p(x), _p(wr), _p(dxp),
+                                                _p(pos), T, d, E, k, _dt(x), _p(dx), _p(dwr), _p(ws), ws.numel(),
+                                                parts, _stream()), "moe_router_bwd_unpermute_parts")
 
 
 def moe_router_bwd_aux(probs, topk_idx, dgate, aux_g, x, wr, dx, dwr, ws):

@@ -441,7 +441,8 @@ size_t moe_router_bwd_workspace_size(int T, int d, int E) {
 static moe_status_t router_bwd_impl(const char* fn, const float* probs, const int32_t* topk_idx, const float* dgate,
                                     const float* aux_g, const void* x, const void* wr, int T, int d, int E, int k,
                                     int dt, void* dx, void* dwr, void* ws, size_t ws_bytes, void* stream,
-                                    const void* dxp = nullptr, const int32_t* pos = nullptr, bool fused = false) {
+                                    const void* dxp = nullptr, const int32_t* pos = nullptr, bool fused = false,
+                                    unsigned parts = MOE_ROUTER_DWR | MOE_ROUTER_DX) {
   TRY(check_dt(fn, dt));
   TRY(check_tk(fn, T, k));
   if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "%s: E must be in [1, 1024]", fn);
@@ -449,10 +450,16 @@ static moe_status_t router_bwd_impl(const char* fn, const float* probs, const in
   TRY(check_row(fn, "d", d, dt));
   if (!(dt == MOE_BF16 && E >= 64 && E % 8 == 0) && E > 64)
     return fail(MOE_ERR_UNSUPPORTED, "%s: E > 64 needs bf16 storage and E %% 8 == 0", fn);
-  TRY(check_ptrs(fn, {{"wr", wr}, {"dwr", dwr}}));
-  if (T > 0)
-    TRY(check_ptrs(fn, {{"probs", probs}, {"topk_idx", topk_idx}, {"dgate", dgate}, {"x", x}, {"dx", dx}}));
-  if (fused && T > 0) TRY(check_ptrs(fn, {{"dxp", dxp}, {"pos", pos}}));
+  if (parts == 0 || (parts & ~(unsigned)(MOE_ROUTER_DWR | MOE_ROUTER_DX)) != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: parts must be a non-empty subset of MOE_ROUTER_DWR | MOE_ROUTER_DX", fn);
+  const bool p_dwr = parts & MOE_ROUTER_DWR, p_dx = parts & MOE_ROUTER_DX;
+  if (p_dwr) TRY(check_ptrs(fn, {{"dwr", dwr}}));
+  if (T > 0) {
+    TRY(check_ptrs(fn, {{"probs", probs}, {"topk_idx", topk_idx}, {"dgate", dgate}}));
+    if (p_dwr) TRY(check_ptrs(fn, {{"x", x}}));
+    if (p_dx) TRY(check_ptrs(fn, {{"wr", wr}, {"dx", dx}}));
+    if (fused && p_dx) TRY(check_ptrs(fn, {{"dxp", dxp}, {"pos", pos}}));
+  }
   const size_t need = trg::router_bwd_ws_bytes(T, d, E);
   if (ws == nullptr || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws_bytes);
@@ -460,7 +467,7 @@ static moe_status_t router_bwd_impl(const char* fn, const float* probs, const in
   TRY(check_device());
   trg::ProfScope ps(fn, (hipStream_t)stream);
   return hip_status(fn, trg::launch_router_bwd(probs, topk_idx, dgate, aux_g, x, wr, T, d, E, k, dt == MOE_BF16, dx,
-                                               dwr, ws, (hipStream_t)stream, fused ? dxp : nullptr, pos));
+                                               dwr, ws, (hipStream_t)stream, fused ? dxp : nullptr, pos, parts));
 }
 
 moe_status_t moe_router_bwd_unpermute(const float* probs, const int32_t* topk_idx, const float* dgate,
@@ -469,6 +476,14 @@ moe_status_t moe_router_bwd_unpermute(const float* probs, const int32_t* topk_id
                                       void* ws, size_t ws_bytes, void* stream) {
   return router_bwd_impl("moe_router_bwd_unpermute", probs, topk_idx, dgate, aux_g, x, wr, T, d, E, k, dt, dx, dwr,
                          ws, ws_bytes, stream, dxp, pos, true);
+}
+
+moe_status_t moe_router_bwd_unpermute_parts(const float* probs, const int32_t* topk_idx, const float* dgate,
+                                            const float* aux_g, const void* x, const void* wr, const void* dxp,
+                                            const int32_t* pos, int T, int d, int E, int k, int dt, void* dx,
+                                            void* dwr, void* ws, size_t ws_bytes, unsigned parts, void* stream) {
+  return router_bwd_impl("moe_router_bwd_unpermute_parts", probs, topk_idx, dgate, aux_g, x, wr, T, d, E, k, dt, dx,
+                         dwr, ws, ws_bytes, stream, dxp, pos, true, parts);
 }
 
 moe_status_t moe_router_bwd(const float* probs, const int32_t* topk_idx, const float* dgate, const void* x,

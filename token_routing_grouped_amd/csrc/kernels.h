@@ -32,10 +32,13 @@ size_t router_bwd_ws_bytes(int T, int d, int E);
 hipError_t launch_router_logits(const void* x, bool bf16, const void* wr, int T, int d, int E, float* logits,
                                 hipStream_t s);
 // dxp == nullptr: dx += dlogits wr.  Otherwise dx = sum_j dxp[pos[t,j]] +
-// dlogits wr (the unpermute-sum folded in; dx is only written).
+// dlogits wr (the unpermute-sum folded in; dx is only written).  parts:
+// kRouterDwr and / or kRouterDx (dlogits is computed for either).
+constexpr unsigned kRouterDwr = 1, kRouterDx = 2;
 hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dgate, const float* aux_g,
                              const void* x, const void* wr, int T, int d, int E, int k, bool bf16, void* dx, void* dwr,
-                             void* ws, hipStream_t s, const void* dxp = nullptr, const int* pos = nullptr);
+                             void* ws, hipStream_t s, const void* dxp = nullptr, const int* pos = nullptr,
+                             unsigned parts = kRouterDwr | kRouterDx);
 size_t balance_ws_bytes(int T, int E);
 hipError_t launch_balance(const float* probs, const int* counts, int T, int E, int k, float alpha, float* stats,
                           float* aux_g, float* mean_probs, void* ws, hipStream_t s);

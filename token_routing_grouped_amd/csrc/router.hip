@@ -371,31 +371,34 @@ hipError_t launch_router_logits(const void* x, bool bf16, const void* wr, int T,
 
 template <class T, int EB>
 static void bwd_valu(const float* dL, const void* x, const void* wr, int Tn, int d, int E, void* dx, void* dwr,
-                     float* part, hipStream_t s, const void* dxp, const int* pos, int k) {
-  const int nch = (Tn + kDwrChunk - 1) / kDwrChunk;
-  constexpr int CV = 64 / EB;
-  constexpr int cols_per_block = 32 * CV;
-  dim3 grid((d + cols_per_block - 1) / cols_per_block, nch);
-  if (d % CV == 0) router_dwr_partial_kernel<T, EB, false><<<grid, 256, 0, s>>>(dL, (const T*)x, Tn, d, E, part);
-  else router_dwr_partial_kernel<T, EB, true><<<grid, 256, 0, s>>>(dL, (const T*)x, Tn, d, E, part);
-  const long n = (long)E * d;
-  chunk_sum_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, nch, n, (T*)dwr);
-  router_dx_valu_kernel<T, EB><<<(Tn + kDxTokens - 1) / kDxTokens, 256, 0, s>>>(dL, (const T*)wr, Tn, d, E, (T*)dx,
-                                                                                (const T*)dxp, pos, k);
+                     float* part, hipStream_t s, const void* dxp, const int* pos, int k, unsigned parts) {
+  if (parts & kRouterDwr) {
+    const int nch = (Tn + kDwrChunk - 1) / kDwrChunk;
+    constexpr int CV = 64 / EB;
+    constexpr int cols_per_block = 32 * CV;
+    dim3 grid((d + cols_per_block - 1) / cols_per_block, nch);
+    if (d % CV == 0) router_dwr_partial_kernel<T, EB, false><<<grid, 256, 0, s>>>(dL, (const T*)x, Tn, d, E, part);
+    else router_dwr_partial_kernel<T, EB, true><<<grid, 256, 0, s>>>(dL, (const T*)x, Tn, d, E, part);
+    const long n = (long)E * d;
+    chunk_sum_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, nch, n, (T*)dwr);
+  }
+  if (parts & kRouterDx)
+    router_dx_valu_kernel<T, EB><<<(Tn + kDxTokens - 1) / kDxTokens, 256, 0, s>>>(dL, (const T*)wr, Tn, d, E, (T*)dx,
+                                                                                  (const T*)dxp, pos, k);
 }
 
 template <class T>
 static void bwd_valu_any(const float* dL, const void* x, const void* wr, int Tn, int d, int E, void* dx, void* dwr,
-                         float* part, hipStream_t s, const void* dxp, const int* pos, int k) {
-  if (E <= 8) bwd_valu<T, 8>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k);
-  else if (E <= 16) bwd_valu<T, 16>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k);
-  else if (E <= 32) bwd_valu<T, 32>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k);
-  else bwd_valu<T, 64>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k);
+                         float* part, hipStream_t s, const void* dxp, const int* pos, int k, unsigned parts) {
+  if (E <= 8) bwd_valu<T, 8>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k, parts);
+  else if (E <= 16) bwd_valu<T, 16>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k, parts);
+  else if (E <= 32) bwd_valu<T, 32>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k, parts);
+  else bwd_valu<T, 64>(dL, x, wr, Tn, d, E, dx, dwr, part, s, dxp, pos, k, parts);
 }
 
 hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dgate, const float* aux_g,
                              const void* x, const void* wr, int T, int d, int E, int k, bool bf16, void* dx, void* dwr,
-                             void* ws, hipStream_t s, const void* dxp, const int* pos) {
+                             void* ws, hipStream_t s, const void* dxp, const int* pos, unsigned parts) {
   const bool mf = router_uses_mfma(bf16, E);
   if (!mf && E > 64) return hipErrorInvalidValue;
   char* p = (char*)ws;
@@ -405,6 +408,7 @@ hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dg
   p += align256((size_t)T * E * sizeof(uint16_t));
   float* part = (float*)p;
   if (T == 0) {  // no tokens: dWr is zero (a fill kernel, not a memset node)
+    if (!(parts & kRouterDwr)) return hipSuccess;
     const long n = (long)E * d;
     if (bf16) zero_fill_kernel<uint16_t><<<(unsigned)((n + 255) / 256), 256, 0, s>>>((uint16_t*)dwr, n);
     else zero_fill_kernel<float><<<(unsigned)((n + 255) / 256), 256, 0, s>>>((float*)dwr, n);
@@ -418,12 +422,16 @@ hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dg
   else if (E <= 512) router_dl_kernel<8><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
   else router_dl_kernel<16><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
   if (mf) {
-    hipError_t err = launch_router_dwr_mfma(dLb, (const uint16_t*)x, (uint16_t*)dwr, part, T, d, E, s);
-    if (err != hipSuccess) return err;
-    return launch_router_dx_mfma(dLb, (const uint16_t*)wr, (uint16_t*)dx, (const uint16_t*)dxp, pos, k, T, d, E, s);
+    if (parts & kRouterDwr) {
+      hipError_t err = launch_router_dwr_mfma(dLb, (const uint16_t*)x, (uint16_t*)dwr, part, T, d, E, s);
+      if (err != hipSuccess) return err;
+    }
+    if (parts & kRouterDx)
+      return launch_router_dx_mfma(dLb, (const uint16_t*)wr, (uint16_t*)dx, (const uint16_t*)dxp, pos, k, T, d, E, s);
+    return hipGetLastError();
   }
-  if (bf16) bwd_valu_any<uint16_t>(dL, x, wr, T, d, E, dx, dwr, part, s, dxp, pos, k);
-  else bwd_valu_any<float>(dL, x, wr, T, d, E, dx, dwr, part, s, dxp, pos, k);
+  if (bf16) bwd_valu_any<uint16_t>(dL, x, wr, T, d, E, dx, dwr, part, s, dxp, pos, k, parts);
+  else bwd_valu_any<float>(dL, x, wr, T, d, E, dx, dwr, part, s, dxp, pos, k, parts);
   return hipGetLastError();
 }
 

@@ -57,6 +57,12 @@ class MoELayerGPU:
         # MXFP8 with two streams: wgrad-down starts as soon as dYp's MX copies
         # exist (next to dgrad-down) instead of after dgrad-down
         self.mx_early_wgrad_down = True
+        # with two streams: the router's dWr part runs on the side stream
+        # right after the combine backward (the dx part stays on the main one).
+        # MXFP8 only: there the side stream idles while dYp's MX copies are
+        # made (wide 3.44 -> 3.42 ms/step); in bf16 it would delay wgrad-down,
+        # which starts right after the combine backward (small +1%).
+        self.router_dwr_on_side = bool(mx)
         self.R = R = T * k
         self.dtype = dtype
         self.mx = mx
@@ -94,6 +100,7 @@ class MoELayerGPU:
         if self.overlap:
             self.side_stream = torch.cuda.Stream(device=dev)
             self.ws_gemm2 = _abi.workspace(_abi.moe_grouped_gemm_workspace_size(E, R, d, h), dev)
+            self.ws_router2 = _abi.workspace(_abi.moe_router_bwd_workspace_size(T, d, E), dev)
         # router balance step: {score, aux loss, max/mean load, min/mean load},
         # the aux loss's per-expert probability gradient and mean probabilities
         self.balance_stats = e(4, dt=f32)
@@ -187,6 +194,17 @@ class MoELayerGPU:
         # MXFP8: dYp is not stored; its MX copies come straight from dy (gate-scaled gather)
         self._dy = dy
         _abi.moe_combine_bwd(dy, self.yp, self.topk_w, self.pos, None if self.mx else self.dyp, self.dgate)
+        aux_g = self.aux_g if self.aux_alpha > 0.0 else None
+        split_router = self.overlap and self.router_dwr_on_side
+        if split_router:
+            # the router's dWr needs only dgate: it runs on the side stream
+            # ahead of the weight gradients, the dx part stays on this one
+            ev_dgate = torch.cuda.Event()
+            ev_dgate.record(torch.cuda.current_stream())
+            with torch.cuda.stream(self.side_stream):
+                self.side_stream.wait_event(ev_dgate)
+                _abi.moe_router_bwd_unpermute_parts(_abi.ROUTER_DWR, self.probs, self.topk_idx, self.dgate, x, wr,
+                                                    None, None, None, self.dwr, self.ws_router2, aux_g=aux_g)
         if self.lean:
             self.recompute_gu(w1, w3)
         if self.mx and self.overlap:
@@ -201,8 +219,12 @@ class MoELayerGPU:
         # dx in one pass: the unpermute-sum of dXp plus the router's term
         if self.overlap and not self.dx_before_join:
             torch.cuda.current_stream().wait_event(self._ev_side_done)
-        _abi.moe_router_bwd_unpermute(self.probs, self.topk_idx, self.dgate, x, wr, self.dxp, self.pos, self.dx,
-                                      self.dwr, self.ws_router, aux_g=self.aux_g if self.aux_alpha > 0.0 else None)
+        if split_router:
+            _abi.moe_router_bwd_unpermute_parts(_abi.ROUTER_DX, self.probs, self.topk_idx, self.dgate, x, wr, self.dxp,
+                                                self.pos, self.dx, None, self.ws_router, aux_g=aux_g)
+        else:
+            _abi.moe_router_bwd_unpermute(self.probs, self.topk_idx, self.dgate, x, wr, self.dxp, self.pos, self.dx,
+                                          self.dwr, self.ws_router, aux_g=aux_g)
         if self.overlap and self.dx_before_join:
             torch.cuda.current_stream().wait_event(self._ev_side_done)
         return self.dx
