@@ -36,10 +36,15 @@ bool prof_selected(const char* name) {
 
 bool prof_on() { return g_prof.load(std::memory_order_relaxed); }
 
+// Timing-only events: without the default system-scope fence, recording one
+// does not write back and invalidate the caches between the launches it
+// brackets (timestamps are read after a device synchronisation).
+hipError_t prof_event(hipEvent_t* ev) { return hipEventCreateWithFlags(ev, hipEventDisableSystemFence); }
+
 void prof_begin(const char* name, hipStream_t s) {
   if (!prof_selected(name)) return;
   hipEvent_t ev;
-  if (hipEventCreate(&ev) != hipSuccess) return;
+  if (prof_event(&ev) != hipSuccess) return;
   (void)hipEventRecord(ev, s);
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_open.emplace_back(name, ev);
@@ -48,7 +53,7 @@ void prof_begin(const char* name, hipStream_t s) {
 void prof_end(const char* name, hipStream_t s) {
   if (!prof_selected(name)) return;
   hipEvent_t ev;
-  if (hipEventCreate(&ev) != hipSuccess) return;
+  if (prof_event(&ev) != hipSuccess) return;
   (void)hipEventRecord(ev, s);
   std::lock_guard<std::mutex> lk(g_prof_mu);
   for (size_t i = g_prof_open.size(); i-- > 0;) {
