@@ -8,10 +8,14 @@ arithmetic of its own.  Forward:
 
 Backward:
 
-  moe_combine_bwd -> moe_grouped_gemm_bwd -> moe_unpermute_sum -> moe_router_bwd
+  moe_combine_bwd -> moe_grouped_gemm_bwd -> moe_router_bwd_unpermute
 
-With aux_alpha > 0 the router balance step runs after routing (moe_balance)
-and its loss's gradient enters the router backward (moe_router_bwd_aux).
+(the last one writes dx once: the unpermute-sum of dXp plus the router's term,
+and dWr).  With overlap=True the weight-gradient GEMMs run on a second stream
+(moe_grouped_gemm_bwd_parts / _mx_parts), and in MXFP8 also the router's dWr
+part (moe_router_bwd_unpermute_parts).  With aux_alpha > 0 the router balance
+step runs after routing (moe_balance) and its loss's gradient enters the
+router backward (aux_g).
 With lean=True the forward does not store G and U and the backward recomputes
 them (moe_grouped_gemm_recompute_gu[_mx]) before moe_grouped_gemm_bwd[_mx].
 
