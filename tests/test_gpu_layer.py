@@ -39,6 +39,10 @@ CASES = [
     # experts of >= 2048 rows on average: light tails (50 and 2 rows past whole
     # 256-row tiles) are scheduled apart from the full-cost tiles
     ("tail_split_E4", "small", dict(T=4096, E=4, k=2, d=256, h=128), "tails", {}),
+    # the same tails over longer K loops (16 steps in the up projection and
+    # dgrad down, 8 in dgrad up, 4 in down): the light tails' three-stage
+    # pipeline in its steady state
+    ("tail_split_E4_K1024", "small", dict(T=4096, E=4, k=2, d=1024, h=256), "tails", {}),
     # d not a multiple of the 256-wide tiles: partial N tiles of the down and
     # dgrad-up GEMMs, partial M tiles of wgrad-down and partial N tiles of
     # wgrad-up (256-row tiles at d = 320, 128-row tiles at d = 192)
