@@ -215,6 +215,43 @@ def gate_runs(small_tensors, small_ms, steps, warmup, dev):
     }
 
 
+# Dense equivalent (M, N, K) of each grouped GEMM: same flop count as one
+# launch, as one plain GEMM over all R routed rows.
+def dense_shape(kernel, cfg):
+    R, d, h = cfg.R, cfg.d, cfg.h
+    shapes = {"ggemm_up_swiglu": (R, 2 * h, d), "ggemm_down": (R, d, h), "ggemm_dgrad_down_swiglu": (R, h, d),
+              "ggemm_dgrad_up": (R, d, 2 * h), "ggemm_wgrad_down": (d, h, R), "ggemm_wgrad_up": (2 * h, d, R)}
+    return shapes.get(kernel)
+
+
+def dense_gemm_ref(M, N, K, dev, reps=20):
+    """torch.mm (the vendor GEMM library) on one dense bf16 GEMM of the given
+    size, contiguous operands, timed with events: what the library reaches on
+    the same work without grouping or an epilogue, as a reference for the
+    grouped kernel's fraction of peak."""
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    a = (torch.randn(M, K, device=dev, generator=g) * 0.02).to(torch.bfloat16).contiguous()
+    b = (torch.randn(K, N, device=dev, generator=g) * 0.02).to(torch.bfloat16).contiguous()
+    c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    tflops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    del a, b, c
+    return {"M": M, "N": N, "K": K, "dtype": "bf16", "avg_us": us, "tflops": tflops,
+            "frac": tflops / BF16_PEAK_TFLOPS, "launches": reps}
+
+
 def copy_probe(nbytes=1 << 30, reps=5):
     """A plain copy kernel of known size: each launch reads and writes exactly
     nbytes.  Profiled with the FETCH_SIZE / WRITE_SIZE counters it gives the
@@ -428,6 +465,13 @@ def main():
                    "note": "bytes the layer keeps from the forward to the backward (routing metadata, inputs and "
                            "weights excluded)"},
     }
+    shape = dense_shape(dom, cfg)
+    if shape is not None and not cfg.mx:
+        log("bench: dense GEMM reference")
+        out["dense_gemm_ref"] = dict(dense_gemm_ref(*shape, dev), kernel=dom,
+                                     note="torch.mm on one dense bf16 GEMM with the dominant kernel's flop "
+                                          "count (one expert-free M x N x K; the grouped weight gradients write "
+                                          "E times its output), outside the timed region")
     if cfg.slug == "small" and mode == "router" and not (a.no_gates or a.lean or a.aux_alpha or a.serial or a.overlap):
         out["gates"] = gate_runs(t, out["ms_per_step_no_events"], a.steps, a.warmup, dev)
     if not a.no_cpu_baseline:

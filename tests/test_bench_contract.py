@@ -59,5 +59,9 @@ def test_bench_line_fields(monkeypatch, capsys):
         assert key in rf, key
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
+    # the vendor library's dense GEMM of the dominant kernel's size, for reference
+    ref = d["dense_gemm_ref"]
+    assert ref["kernel"] == rf["kernel"] and ref["M"] == d["config"]["T"] * d["config"]["k"]
+    assert ref["avg_us"] > 0 and 0 < ref["frac"] < 1
     # tokens/s is the timed loop's: T tokens per ms_per_step
     assert abs(d["value"] - d["config"]["T"] / (d["ms_per_step"] * 1e-3)) <= 1e-6 * d["value"]
