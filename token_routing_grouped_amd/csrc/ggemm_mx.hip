@@ -258,7 +258,6 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
       }
       const char* sA = smem + (it & 1) * STAGE;
       const char* sB = sA + SA;
-      const int kt = it * BK;
       // Slice 0's fragments are read here; slice 1's are read under slice 0's
       // MFMAs, A fragment i as soon as row i's MFMAs are issued, B fragment j
       // after the last row's MFMA j (the registers of one slice, renamed a
