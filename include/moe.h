@@ -347,7 +347,11 @@ moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, con
  *   columnwise   q [cols, ldc] u8: blocks of 32 consecutive rows inside each
  *                row segment, the last block of a segment zero-padded;
  *                segment e starts at column off128[e] (the transpose of the
- *                rowwise form of each padded segment)
+ *                rowwise form of each padded segment).  With fixed segments
+ *                (the weights: nseg segments of seg_rows rows) the copy is
+ *                expert-major instead: q [nseg*cols, ldc], row e*cols + c
+ *                holding column c of segment e, so one expert's copy is a
+ *                contiguous [cols, ldc] block
  *   scales       K-chunk major: for an MX matrix of n rows (rowwise: rows;
  *                columnwise: cols) with K values per row (rowwise: cols;
  *                columnwise: ldc), the scale of block b (K values 32b ..
@@ -369,9 +373,10 @@ moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, con
  *     (rows a multiple of seg_rows, or seg_rows = rows), each padded to 32.
  *   q_row/s_row (nullable): rowwise output; s_row holds ceil(cols/128) * rows
  *     * 4 bytes.  q_col/s_col (nullable): columnwise output with row stride ldc
- *     (a multiple of 32, at least the padded row count: rows + 127*nseg with
- *     seg_off, else segments x round32(seg_rows)); s_col holds ceil(ldc/128) *
- *     cols * 4 bytes.
+ *     (a multiple of 32; with seg_off at least rows + 127*nseg, and s_col holds
+ *     ceil(ldc/128) * cols * 4 bytes; with fixed segments at least
+ *     round32(seg_rows), q_col holds rows/seg_rows * cols rows and s_col
+ *     ceil(ldc/128) * rows/seg_rows * cols * 4 bytes).
  * cols must be a multiple of 32.  Bit-exact and deterministic.
  */
 moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32_t* gather_src, int gather_k,
@@ -416,9 +421,11 @@ typedef struct {
   const void* g; const void* u;             /* [R,h] bf16 from the forward          */
   const uint8_t* hqT; const uint8_t* hsT;   /* columnwise H from the forward        */
   const uint8_t* xqT; const uint8_t* xsT;   /* [d,rcap] columnwise routed x       */
-  const uint8_t* w1tq; const uint8_t* w1ts; /* [d,E*h], [d,E*h/32]: W1 blocked on h */
+  const uint8_t* w1tq; const uint8_t* w1ts; /* [E*d,h], [E*d,h/32]: W1 blocked on h,
+                                               expert-major (mx_quantize, seg_rows h) */
   const uint8_t* w3tq; const uint8_t* w3ts; /* same for W3                          */
-  const uint8_t* w2tq; const uint8_t* w2ts; /* [h,E*d], [h,E*d/32]: W2 blocked on d */
+  const uint8_t* w2tq; const uint8_t* w2ts; /* [E*h,d], [E*h,d/32]: W2 blocked on d,
+                                               expert-major (seg_rows d)            */
   void* dgu;                                /* out: [R,2h] bf16 (dG | dU)           */
   uint8_t* dguq; uint8_t* dgus;             /* out: [R,2h], [R,2h/32]               */
   uint8_t* dguqT; uint8_t* dgusT;           /* out: [2h,rcap], [2h,rcap/32]     */

@@ -128,20 +128,26 @@ def test_mx_quantize_gather_both_layouts(T, E, k, cols, mode):
     assert (mx_scales_to_rows(sT.cpu().numpy(), cols, rc)[:, :R32 // 32] == cs).all()
 
 
-def test_mx_quantize_fixed_segments():
-    """Weights: E segments of h rows each, both layouts in one pass."""
+@pytest.mark.parametrize("E,h,d", [(3, 96, 160), (4, 256, 128)], ids=["h96", "h256"])
+def test_mx_quantize_fixed_segments(E, h, d):
+    """Weights: E segments of h rows each, both layouts in one pass.  The
+    columnwise copy is expert-major: row e*d + c holds column c of segment e
+    (h96: segments not a multiple of 128 rows, scale bytes written one by
+    one; h256: whole scale dwords)."""
     from token_routing_grouped_amd import _abi
 
-    E, h, d = 3, 96, 160
     w = _special_matrix(E * h, d, 5)
-    q, s, qT, sT = _u8(E * h, d), _u8(mx_scale_bytes(E * h, d)), _u8(d, E * h), _u8(mx_scale_bytes(d, E * h))
+    q, s, qT, sT = _u8(E * h, d), _u8(mx_scale_bytes(E * h, d)), _u8(E * d, h), _u8(mx_scale_bytes(E * d, h))
     _abi.mx_quantize(_dev(w, torch.bfloat16), E * h, q, s, qT, sT, seg_rows=h)
     torch.cuda.synchronize()
     rq, rs = mx.quantize_rows(w)
     assert (q.cpu().numpy() == rq).all() and (mx_scales_to_rows(s.cpu().numpy(), E * h, d) == rs).all()
     off = np.arange(E + 1) * h
-    cq, cs = mx.quantize_cols_segmented(w, off, off)
-    assert (qT.cpu().numpy() == cq).all() and (mx_scales_to_rows(sT.cpu().numpy(), d, E * h) == cs).all()
+    cq, cs = mx.quantize_cols_segmented(w, off, off)  # [d, E*h] and [d, E*h/32]: segments side by side
+    want_q = np.concatenate([cq[:, e * h:(e + 1) * h] for e in range(E)], axis=0)
+    want_s = np.concatenate([cs[:, e * h // 32:(e + 1) * h // 32] for e in range(E)], axis=0)
+    assert (qT.cpu().numpy() == want_q).all()
+    assert (mx_scales_to_rows(sT.cpu().numpy(), E * d, h) == want_s).all()
 
 
 def test_mx_quantize_deterministic():

@@ -540,18 +540,20 @@ moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32
   if ((q_row == nullptr) != (s_row == nullptr)) return fail(MOE_ERR_INVALID_ARG, "%s: q_row and s_row go together", fn);
   if ((q_col == nullptr) != (s_col == nullptr)) return fail(MOE_ERR_INVALID_ARG, "%s: q_col and s_col go together", fn);
   if (gather_src && gather_k < 1) return fail(MOE_ERR_INVALID_ARG, "%s: gather_k must be >= 1", fn);
-  long padded;
+  long padded, col_rows;  // padded rows in all; rows one columnwise row holds
   if (seg_off) {
     if (!seg_off128) return fail(MOE_ERR_INVALID_ARG, "%s: seg_off128 is required with seg_off", fn);
     if (nseg < 1 || nseg > 65536) return fail(MOE_ERR_INVALID_ARG, "%s: nseg must be in [1, 65536]", fn);
     padded = ((long)rows + 127L * nseg + 31) / 32 * 32;
+    col_rows = (long)rows + 127L * nseg;
   } else {
     if (seg_rows < 1 || (seg_rows != rows && (seg_rows % 32 != 0 || rows % seg_rows != 0)))
       return fail(MOE_ERR_INVALID_ARG, "%s: seg_rows must equal rows, or be a multiple of 32 dividing rows", fn);
     const long seg32 = ((long)seg_rows + 31) / 32 * 32;
     padded = rows == 0 ? 0 : ((long)rows + seg_rows - 1) / seg_rows * seg32;
+    col_rows = seg32;  // expert-major: one segment per columnwise row
   }
-  if (q_col && (ldc % 32 != 0 || ldc < (seg_off ? (long)rows + 127L * nseg : padded)))
+  if (q_col && (ldc % 32 != 0 || ldc < col_rows))
     return fail(MOE_ERR_INVALID_ARG, "%s: ldc must be a multiple of 32 and cover the padded rows", fn);
   if (padded >= (1L << 31) || (long)rows * cols >= (1L << 31) * 16L)
     return fail(MOE_ERR_UNSUPPORTED, "%s: problem too large", fn);

@@ -44,8 +44,7 @@ struct MxArgs {
   const uint8_t* sB;   // B scales (GLU: W1; KSPLIT: the first K half)
   const uint8_t* sB2;  // GLU: W3; KSPLIT: the second K half
   long sb_step;        // bytes per K chunk of B
-  int sb_row_es;       // B scale rows per expert (forward weights: N rows each)
-  int sb_k_es;         // B K values per expert (dgrad weights: experts side by side along K)
+  int sb_row_es;       // B scale rows per expert (weights: N rows each, expert-major)
   long sA_bytes, sB_bytes;  // extents (bounds for the scale loads)
 };
 
@@ -198,7 +197,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
         second = kt >= g.split;
         if (second) ktb -= g.split;
       }
-      const long off = ((long)(c.e * x.sb_k_es + ktb) >> 7) * x.sb_step + ((long)c.e * x.sb_row_es + row0) * 4;
+      const long off = (long)(ktb >> 7) * x.sb_step + ((long)c.e * x.sb_row_es + row0) * 4;
       lds_load16(second ? rsSB2 : rsSB, dst, (int)off + lane * 16);
     }
   };
@@ -388,10 +387,10 @@ template <int BM>
 static hipError_t mx_dgrad_bm(const MxBwd& p, unsigned parts, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
   const int mt_max = cdiv(R, BM) + E;
-  if (parts & MOE_BWD_DGRAD_DOWN) {  // dgrad down + SwiGLU backward: dyq [R,d] x W2 blocked along d ([h, E*d])
+  if (parts & MOE_BWD_DGRAD_DOWN) {  // dgrad down + SwiGLU backward: dyq [R,d] x W2 blocked along d ([E*h, d])
     Args a{};
     a.A = (const uint16_t*)p.dyq; a.lda = d;
-    a.B = (const uint16_t*)p.w2tq; a.ldb = (long)E * d; a.b_es = d;
+    a.B = (const uint16_t*)p.w2tq; a.ldb = d; a.b_es = (long)h * d;
     a.C = p.dgu; a.ldc = 2L * h;
     a.G = (const uint16_t*)p.g; a.U = (const uint16_t*)p.u; a.ldgu = h;
     a.N = h; a.K = d; a.split = h;
@@ -399,7 +398,7 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, unsigned parts, hipStream_t s) {
     a.tiles_n = cdiv(h, 256);
     MxArgs x{};
     x.sA = p.dys; x.sa_step = 4L * R; x.sA_bytes = (long)R * (d / 32);
-    x.sB = p.w2ts; x.sb_step = 4L * h; x.sb_k_es = d; x.sB_bytes = (long)h * E * d / 32;
+    x.sB = p.w2ts; x.sb_step = 4L * E * h; x.sb_row_es = h; x.sB_bytes = (long)h * E * d / 32;
     run_mx<BM, 256, RAGGED_M, BSEL_NONE, CSEL_NONE, EPI_SWIGLU_BWD>("ggemm_mx_dgrad_down_swiglu", a, x,
                                                                     mt_max * a.tiles_n, s);
   }
@@ -409,17 +408,17 @@ static hipError_t mx_dgrad_bm(const MxBwd& p, unsigned parts, hipStream_t s) {
                                               (R + 127 * E + 31) / 32, p.dguq, p.dgus, p.dguqT, p.dgusT, p.rcap, s);
     if (err != hipSuccess) return err;
   }
-  if (parts & MOE_BWD_DGRAD_UP) {  // dgrad up: dguq [R,2h] x (W1 | W3) blocked along h ([d, E*h] each)
+  if (parts & MOE_BWD_DGRAD_UP) {  // dgrad up: dguq [R,2h] x (W1 | W3) blocked along h ([E*d, h] each)
     Args a{};
     a.A = (const uint16_t*)p.dguq; a.lda = 2L * h;
-    a.B = (const uint16_t*)p.w1tq; a.B2 = (const uint16_t*)p.w3tq; a.ldb = (long)E * h; a.b_es = h;
+    a.B = (const uint16_t*)p.w1tq; a.B2 = (const uint16_t*)p.w3tq; a.ldb = h; a.b_es = (long)d * h;
     a.C = p.dxp; a.ldc = d;
     a.N = d; a.K = 2 * h; a.split = h;
     a.offsets = p.offsets; a.split_tails = split_tails(E, R); a.E = E; a.R = R;
     a.tiles_n = cdiv(d, 256);
     MxArgs x{};
     x.sA = p.dgus; x.sa_step = 4L * R; x.sA_bytes = (long)R * (2 * h / 32);
-    x.sB = p.w1ts; x.sB2 = p.w3ts; x.sb_step = 4L * d; x.sb_k_es = h; x.sB_bytes = (long)d * E * h / 32;
+    x.sB = p.w1ts; x.sB2 = p.w3ts; x.sb_step = 4L * E * d; x.sb_row_es = d; x.sB_bytes = (long)d * E * h / 32;
     run_mx<BM, 256, RAGGED_M, BSEL_KSPLIT, CSEL_NONE, EPI_BF16>("ggemm_mx_dgrad_up", a, x, mt_max * a.tiles_n, s);
   }
   return hipGetLastError();

@@ -188,7 +188,15 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
   // whole scale dwords (a row's four blocks of a 128-chunk) where the base is
   // 4-byte aligned and all four blocks are written
   const bool row_dw = ((uintptr_t)s_row & 3) == 0;
-  const bool col_dw = ((uintptr_t)s_col & 3) == 0;
+  // Fixed segments (weights: experts of seg_rows rows) go out expert-major:
+  // the columnwise copy is an MX matrix of nsegf * cols rows, row e * cols + c
+  // holding column c of segment e (its padded rows, row stride ldc), so a GEMM
+  // that reads one expert's copy reads rows ldc bytes apart.  A single
+  // segment (seg_rows = rows) is the plain transpose either way.
+  const bool emaj = seg_off == nullptr && seg_rows < rows;
+  const int seg32 = (seg_rows + 31) / 32 * 32;
+  const int nsegf = emaj ? rows / seg_rows : 1;
+  const bool col_dw = ((uintptr_t)s_col & 3) == 0 && (!emaj || seg32 % 128 == 0);
 
   // The band's 32-row blocks -> (first source row, segment end, valid),
   // looked up once per workgroup.  Segment starts go through LDS first (one
@@ -348,11 +356,21 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
     const uint32_t all = or_n<G>((ok ? 1u : 0u) << sg);
     const uint32_t sw = or_n<G>((uint32_t)(s + 127) << (8 * sg));
     if (ok) {
-      uint4* dst = (uint4*)(q_col + (long)c * ldc + base + sb * 32);
+      // (matrix row, padded row inside it, rows of the MX matrix)
+      long mrow = c;
+      int pr = base + sb * 32;
+      long nrow = cols;
+      if (emaj) {
+        const int e = pr / seg32;
+        mrow = (long)e * cols + c;
+        pr -= e * seg32;
+        nrow = (long)nsegf * cols;
+      }
+      uint4* dst = (uint4*)(q_col + mrow * ldc + pr);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      const int b = (base + sb * 32) >> 5;  // block along the padded rows
-      uint8_t* sp = s_col + ((long)(b >> 2) * cols + c) * 4 + (b & 3);
+      const int b = pr >> 5;  // block along the (segment's) padded rows
+      uint8_t* sp = s_col + ((long)(b >> 2) * nrow + mrow) * 4 + (b & 3);
       if (col_dw && all == (1u << G) - 1) {  // the group's G bytes at once (base is a multiple of RB)
         if (sg == 0) {
           if constexpr (G == 4) *(uint32_t*)sp = sw;
