@@ -143,7 +143,7 @@ def test_mx_quantize_fixed_segments(E, h, d):
     rq, rs = mx.quantize_rows(w)
     assert (q.cpu().numpy() == rq).all() and (mx_scales_to_rows(s.cpu().numpy(), E * h, d) == rs).all()
     off = np.arange(E + 1) * h
-    cq, cs = mx.quantize_cols_segmented(w, off, off)  # [d, E*h] and [d, E*h/32]: segments side by side
+    cq, cs = mx.quantize_cols_segmented(w, off, off)  # the oracle's [d, E*h], [d, E*h/32]; restacked per segment
     want_q = np.concatenate([cq[:, e * h:(e + 1) * h] for e in range(E)], axis=0)
     want_s = np.concatenate([cs[:, e * h // 32:(e + 1) * h // 32] for e in range(E)], axis=0)
     assert (qT.cpu().numpy() == want_q).all()

@@ -16,7 +16,8 @@
 //   column layout   q_col [cols, ldc]                              (blocks of
 //                   32 consecutive rows inside each segment, zero-padded at
 //                   the segment's end; segment e starts at column off128[e]:
-//                   the weight-gradient K).
+//                   the weight-gradient K), or, for fixed segments (the
+//                   weights' dgrad copies), expert-major [nseg * cols, ldc].
 // Scale bytes are stored K-chunk major: the scale of block b (of 32 values
 // along K) of row r of an n-row MX matrix is byte (b / 4 * n + r) * 4 + b % 4,
 // so the four scales of one 128-wide K chunk of a row form one dword and the
