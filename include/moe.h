@@ -348,10 +348,10 @@ moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, con
  *                row segment, the last block of a segment zero-padded;
  *                segment e starts at column off128[e] (the transpose of the
  *                rowwise form of each padded segment).  With fixed segments
- *                (the weights: nseg segments of seg_rows rows) the copy is
- *                expert-major instead: q [nseg*cols, ldc], row e*cols + c
- *                holding column c of segment e, so one expert's copy is a
- *                contiguous [cols, ldc] block
+ *                (the weights: S = rows/seg_rows segments of seg_rows rows)
+ *                the copy is expert-major instead: q [S*cols, ldc], row
+ *                e*cols + c holding column c of segment e, so one expert's
+ *                copy is a contiguous [cols, ldc] block
  *   scales       K-chunk major: for an MX matrix of n rows (rowwise: rows;
  *                columnwise: cols) with K values per row (rowwise: cols;
  *                columnwise: ldc), the scale of block b (K values 32b ..
