@@ -344,14 +344,16 @@ moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, con
  * elements E4M3FN(v / 2^s) rounded to nearest even and saturated to +-448,
  * sign of zero kept.  Layouts:
  *   rowwise      q [rows, cols] u8 (blocks along cols)
- *   columnwise   q [cols, ldc] u8: blocks of 32 consecutive rows inside each
- *                row segment, the last block of a segment zero-padded;
- *                segment e starts at column off128[e] (the transpose of the
- *                rowwise form of each padded segment).  With fixed segments
- *                (the weights: S = rows/seg_rows segments of seg_rows rows)
- *                the copy is expert-major instead: q [S*cols, ldc], row
- *                e*cols + c holding column c of segment e, so one expert's
- *                copy is a contiguous [cols, ldc] block
+ *   columnwise   blocks of 32 consecutive rows inside each row segment, the
+ *                last block of a segment zero-padded, stored expert-major:
+ *                each segment's copy is the transpose of its padded rows, a
+ *                contiguous [cols, len] block (row c = column c of the
+ *                segment), so a GEMM over one expert reads rows len bytes
+ *                apart.  With seg_off the copy of segment e starts at byte
+ *                off128[e] * cols and len = off128[e+1] - off128[e] (a buffer
+ *                of cols * ldc bytes); with fixed segments (the weights: S =
+ *                rows/seg_rows segments) q is [S*cols, ldc], row e*cols + c
+ *                holding column c of segment e
  *   scales       K-chunk major: for an MX matrix of n rows (rowwise: rows;
  *                columnwise: cols) with K values per row (rowwise: cols;
  *                columnwise: ldc), the scale of block b (K values 32b ..
@@ -372,11 +374,12 @@ moe_status_t moe_router_bwd_aux(const float* probs, const int32_t* topk_idx, con
  *     segment and at most 127 rows longer (moe_route's offsets / off128); if null, segments of seg_rows rows
  *     (rows a multiple of seg_rows, or seg_rows = rows), each padded to 32.
  *   q_row/s_row (nullable): rowwise output; s_row holds ceil(cols/128) * rows
- *     * 4 bytes.  q_col/s_col (nullable): columnwise output with row stride ldc
- *     (a multiple of 32; with seg_off at least rows + 127*nseg, and s_col holds
- *     ceil(ldc/128) * cols * 4 bytes; with fixed segments at least
- *     round32(seg_rows), q_col holds rows/seg_rows * cols rows and s_col
- *     ceil(ldc/128) * rows/seg_rows * cols * 4 bytes).
+ *     * 4 bytes.  q_col/s_col (nullable): columnwise output; ldc a multiple of
+ *     32.  With seg_off, ldc >= rows + 127*nseg is the padded row capacity:
+ *     q_col holds cols * ldc bytes, s_col ceil(ldc/128) * cols * 4.  With
+ *     fixed segments, ldc >= round32(seg_rows) is the row stride: q_col holds
+ *     rows/seg_rows * cols rows of ldc, s_col ceil(ldc/128) * rows/seg_rows *
+ *     cols * 4 bytes.
  * cols must be a multiple of 32.  Bit-exact and deterministic.
  */
 moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32_t* gather_src, int gather_k,
@@ -388,7 +391,9 @@ moe_status_t mx_quantize(const void* in, int dt, int rows, int cols, const int32
  * as moe_grouped_gemm_fwd / _bwd, with every GEMM operand quantised along its
  * own reduction dimension and multiplied on gfx950's scaled matrix cores
  * (fp32 accumulation, bf16 outputs).  d and h must be multiples of 128; rcap
- * (row stride of every columnwise copy) a multiple of 128 and >= R + 127*E;
+ * (padded row capacity of every columnwise copy: a copy of n columns holds
+ * n * rcap bytes, expert-major as mx_quantize writes it) a multiple of 128 and
+ * >= R + 127*E;
  * off128 as moe_route writes it (segment starts on multiples of 128).  Scale
  * arrays are in the K-chunk-major layout above; with d, h and rcap multiples
  * of 128 each holds exactly (values)/32 bytes, e.g. xs = R*d/32.
@@ -406,7 +411,7 @@ typedef struct {
   const uint8_t* w2q; const uint8_t* w2s; /* [E,d,h], [E,d,h/32] rowwise       */
   void* g; void* u; void* hbuf;           /* out: [R,h] bf16                   */
   uint8_t* hq; uint8_t* hs;               /* out: [R,h], [R,h/32] rowwise H    */
-  uint8_t* hqT; uint8_t* hsT;             /* out: [h,rcap], [h,rcap/32]    */
+  uint8_t* hqT; uint8_t* hsT;             /* out: h*rcap (expert-major), [h,rcap/32] */
   void* yp;                               /* out: [R,d] bf16                   */
   void* ws; size_t ws_bytes;
 } moe_mx_fwd_args;
@@ -417,10 +422,10 @@ typedef struct {
   const int32_t* off128;
   const void* dyp;                          /* [R,d] bf16 (moe_combine_bwd)         */
   uint8_t* dyq; uint8_t* dys;               /* out: [R,d], [R,d/32] rowwise dYp     */
-  uint8_t* dyqT; uint8_t* dysT;             /* out: [d,rcap], [d,rcap/32]       */
+  uint8_t* dyqT; uint8_t* dysT;             /* out: d*rcap (expert-major), [d,rcap/32] */
   const void* g; const void* u;             /* [R,h] bf16 from the forward          */
   const uint8_t* hqT; const uint8_t* hsT;   /* columnwise H from the forward        */
-  const uint8_t* xqT; const uint8_t* xsT;   /* [d,rcap] columnwise routed x       */
+  const uint8_t* xqT; const uint8_t* xsT;   /* d*rcap columnwise routed x (expert-major) */
   const uint8_t* w1tq; const uint8_t* w1ts; /* [E*d,h], [E*d,h/32]: W1 blocked on h,
                                                expert-major (mx_quantize, seg_rows h) */
   const uint8_t* w3tq; const uint8_t* w3ts; /* same for W3                          */
@@ -428,7 +433,7 @@ typedef struct {
                                                expert-major (seg_rows d)            */
   void* dgu;                                /* out: [R,2h] bf16 (dG | dU)           */
   uint8_t* dguq; uint8_t* dgus;             /* out: [R,2h], [R,2h/32]               */
-  uint8_t* dguqT; uint8_t* dgusT;           /* out: [2h,rcap], [2h,rcap/32]     */
+  uint8_t* dguqT; uint8_t* dgusT;           /* out: 2h*rcap (expert-major), [2h,rcap/32] */
   void* dxp;                                /* out: [R,d] bf16                      */
   void* dw1; void* dw3; void* dw2;          /* out: weight gradients, bf16          */
   void* ws; size_t ws_bytes;

@@ -53,6 +53,21 @@ def mx_scale_bytes(rows, K):
     return -(-K // 128) * rows * 4
 
 
+def mx_cols_side_by_side(buf, cols, off128):
+    """The library's columnwise MX copy of segmented rows (segment e's copy a
+    [cols, len_e] block at byte off128[e] * cols, len_e = off128[e+1] -
+    off128[e]) as the [cols, off128[-1]] array with the segments side by side,
+    the layout the oracle uses.  A pure re-indexing."""
+    flat = np.asarray(buf).reshape(-1)
+    off = np.asarray(off128).astype(np.int64)
+    out = np.zeros((cols, int(off[-1])), dtype=flat.dtype)
+    for e in range(len(off) - 1):
+        ps, pe = int(off[e]), int(off[e + 1])
+        if pe > ps:
+            out[:, ps:pe] = flat[ps * cols:pe * cols].reshape(cols, pe - ps)
+    return out
+
+
 def mx_scales_to_rows(buf, rows, K):
     """The library's K-chunk-major scale bytes (block b of row r at byte
     (b // 4 * rows + r) * 4 + b % 4) as a [rows, K/32] array, the layout the

@@ -129,8 +129,10 @@ def test_step_writes_only_its_buffers(case):
         assert (getattr(layer, n) >= 0).all(), f"{n}: entries left unwritten"
     if flags.get("mx"):
         end = int(layer.off128[-1].item())
-        for n in ("xqT", "hqT", "dyqT", "dguqT"):  # payload [cols, rcap]
-            assert (getattr(layer, n)[:, end:] == 0xEE).all(), f"{n}: written past the last padded segment"
+        for n in ("xqT", "hqT", "dyqT", "dguqT"):  # payload: segment e at byte off128[e] * cols, flat
+            buf = getattr(layer, n)
+            cols = buf.numel() // layer.rcap
+            assert (buf.reshape(-1)[end * cols:] == 0xEE).all(), f"{n}: written past the last padded segment"
         for n in ("xsT", "hsT", "dysT", "dgusT"):  # scales, K-chunk major: [rcap/128][cols][4]
             buf = getattr(layer, n)
             cols = buf.shape[0]

@@ -18,7 +18,7 @@ from oracle import moe_ref as ref
 from oracle import mx_ref as mx
 from token_routing_grouped_amd import configs, inputs
 
-from helpers import mx_scale_bytes, mx_scales_to_rows, rel_l2, say, tail_routing, to_np
+from helpers import mx_scale_bytes, mx_cols_side_by_side, mx_scales_to_rows, rel_l2, say, tail_routing, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -124,7 +124,7 @@ def test_mx_quantize_gather_both_layouts(T, E, k, cols, mode):
     assert (q.cpu().numpy() == rq).all() and (mx_scales_to_rows(s.cpu().numpy(), R, cols) == rs).all()
     cq, cs = mx.quantize_cols_segmented(xp, rt["offsets"], rt["off128"])
     R32 = int(rt["off128"][-1])
-    assert (qT.cpu().numpy()[:, :R32] == cq).all()
+    assert (mx_cols_side_by_side(qT.cpu().numpy(), cols, rt["off128"]) == cq).all()  # segment e at byte off128[e]*cols
     assert (mx_scales_to_rows(sT.cpu().numpy(), cols, rc)[:, :R32 // 32] == cs).all()
 
 
@@ -203,7 +203,7 @@ def test_mx_layer_parity(case):
     off, off128 = f["offsets"], f["off128"]
     R32 = int(off128[-1])
     dyq = mx.dequantize_rows(to_np(layer.dyq), mx_scales_to_rows(to_np(layer.dys), R, d))
-    dyqT = mx.dequantize_cols_segmented(to_np(layer.dyqT)[:, :R32],
+    dyqT = mx.dequantize_cols_segmented(mx_cols_side_by_side(to_np(layer.dyqT), d, off128),
                                         mx_scales_to_rows(to_np(layer.dysT), d, layer.rcap)[:, :R32 // 32], off, off128)
     checks = [("G", layer.g, f["G"]), ("U", layer.u, f["U"]), ("H", layer.hb, f["H"]), ("Yp", layer.yp, f["yp"]),
               ("y", layer.y, f["y"]), ("dYp (MX rows)", dyq, mx.qdq_rows(b["dyp"])),
@@ -232,9 +232,9 @@ def test_mx_layer_deterministic():
         layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, mx=True)
         layer.step(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])
         torch.cuda.synchronize()
-        R32 = int(layer.off128[-1].item())  # columnwise copies are written up to the last padded segment
-        outs.append([a.clone() for a in (layer.y, layer.dx, layer.dw1, layer.dw2, layer.xq, layer.hqT[:, :R32],
-                                         layer.dguqT[:, :R32])])
+        R32 = int(layer.off128[-1].item())  # columnwise copies: off128[-1] * cols bytes written
+        outs.append([a.clone() for a in (layer.y, layer.dx, layer.dw1, layer.dw2, layer.xq, layer.hqT[:R32 * cfg.h],
+                                         layer.dguqT[:R32 * 2 * cfg.h])])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
 
@@ -266,6 +266,6 @@ def test_mx_dy_copies_from_dy_equal_the_quantised_stored_dyp(T, E, mode):
     end = int(layer.off128[-1].item())
     assert torch.equal(dgate, layer.dgate)
     assert torch.equal(q, layer.dyq) and torch.equal(s.view(-1), layer.dys.view(-1))
-    assert torch.equal(qT[:, :end], layer.dyqT[:, :end])
+    assert torch.equal(qT.reshape(-1)[:end * d], layer.dyqT[:end * d])
     nb = end // 128 * d * 4  # scale chunks up to the last padded segment
     assert torch.equal(sT.view(-1)[:nb], layer.dysT.view(-1)[:nb])

@@ -401,7 +401,8 @@ def mx_quantize(x, rows, q_row=None, s_row=None, q_col=None, s_col=None, gather_
         _expect(t, torch.uint8, n)
     for t, n in ((gather_src, "gather_src"), (seg_off, "seg_off"), (seg_off128, "seg_off128")):
         _expect(t, torch.int32, n)
-    ldc = 0 if q_col is None else q_col.shape[1]
+    # columnwise row capacity: [rows, ldc] (fixed segments), or a flat buffer of cols * ldc bytes
+    ldc = 0 if q_col is None else (q_col.shape[1] if q_col.dim() == 2 else q_col.numel() // cols)
     _check(lib().mx_quantize(_p(x), _dt(x), rows, cols, _p(gather_src), gather_k, _p(seg_off), _p(seg_off128), nseg,
                              seg_rows, _p(q_row), _p(s_row), _p(q_col), _p(s_col), ldc, _stream()), "mx_quantize")
 

@@ -113,6 +113,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
 
   struct Tile {
     int e, m0, m_end, n0, k0, klen;
+    int ld;  // weight gradients: the operands' row stride (the segment's padded length)
     __amdgpu_buffer_rsrc_t rsA, rsB, rsB2;
   };
   auto decode = [&](int t) {
@@ -135,7 +136,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
                                        : c.rsB;
       }
     } else {
-      // weight gradients: K = the expert's 128-padded column segment
+      // weight gradients: K = the expert's 128-padded column segment; each
+      // operand's copy of segment e is one [rows, klen] block at byte
+      // off128[e] * rows (expert-major, mx_quantize)
       const int per_e = g.tiles_m * g.tiles_n;
       c.e = t / per_e;
       const int r = t - c.e * per_e;
@@ -145,8 +148,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
       c.n0 = nt * BN;
       c.k0 = g.offsets[c.e];
       c.klen = g.offsets[c.e + 1] - c.k0;
-      c.rsA = make_rsrc(A + (long)c.m0 * g.lda + c.k0, (long)(g.M - c.m0) * g.lda - c.k0);
-      c.rsB = make_rsrc(B + (long)c.n0 * g.ldb + c.k0, (long)(g.N - c.n0) * g.ldb - c.k0);
+      c.ld = c.klen;
+      c.rsA = make_rsrc(A + (long)c.k0 * g.M + (long)c.m0 * c.klen, (long)(g.M - c.m0) * c.klen);
+      c.rsB = make_rsrc(B + (long)c.k0 * g.N + (long)c.n0 * c.klen, (long)(g.N - c.n0) * c.klen);
       c.rsB2 = c.rsB;
     }
     return c;
@@ -156,6 +160,18 @@ __global__ __launch_bounds__(64 * WM * WN) void ggemm_mx_kernel(Args g, MxArgs x
   auto issue = [&](const Tile& c, int kt, int stage) {  // kt: K offset relative to c.k0
     char* sA = smem + stage * STAGE;
     char* sB = sA + SA;
+    if constexpr (MODE == RAGGED_K) {  // both operands: rows of the segment's length
+      const int ll[2] = {kc_lane_off(lane, 0, c.ld), kc_lane_off(lane, 1, c.ld)};
+      load_kc<BM, NW>(sA, wave, ll, kt, c.ld, [&](int r8, int& r0) {
+        r0 = r8;
+        return c.rsA;
+      });
+      load_kc<BN, NW>(sB, wave, ll, kt, c.ld, [&](int r8, int& r0) {
+        r0 = r8;
+        return c.rsB;
+      });
+      return;
+    }
     load_kc<BM, NW>(sA, wave, a_lane, kt, (int)g.lda, [&](int r8, int& r0) {
       r0 = r8;
       return c.rsA;
@@ -448,8 +464,8 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s) {
   const long sc = p.rcap / 32;
   if (parts & MOE_BWD_WGRAD_DOWN) {  // wgrad down: dW2[e] = dYp_e^T H_e over the expert's padded segment
     Args a{};
-    a.A = (const uint16_t*)p.dyqT; a.lda = p.rcap;
-    a.B = (const uint16_t*)p.hqT; a.ldb = p.rcap;
+    a.A = (const uint16_t*)p.dyqT;  // expert-major columnwise copies: rows of each segment's length
+    a.B = (const uint16_t*)p.hqT;
     a.C = p.dw2; a.ldc = h; a.c_es = (long)d * h;
     a.M = d; a.N = h;
     a.offsets = p.off128; a.kstep = 128; a.E = E; a.R = R;
@@ -462,8 +478,8 @@ hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s) {
   }
   if (parts & MOE_BWD_WGRAD_UP) {  // wgrad up: [dW1; dW3][e] = [dG | dU]_e^T Xp_e
     Args a{};
-    a.A = (const uint16_t*)p.dguqT; a.lda = p.rcap;
-    a.B = (const uint16_t*)p.xqT; a.ldb = p.rcap;
+    a.A = (const uint16_t*)p.dguqT;  // expert-major columnwise copies: rows of each segment's length
+    a.B = (const uint16_t*)p.xqT;
     a.C = p.dw1; a.C2 = p.dw3; a.ldc = d; a.c_es = (long)h * d;
     a.M = 2 * h; a.N = d; a.split = h;
     a.offsets = p.off128; a.kstep = 128; a.E = E; a.R = R;

@@ -125,7 +125,7 @@ TRG_DEV uint32_t or_n(uint32_t v) {
 // Segment of the 32-row block starting at padded row base32: the block's first
 // source row, the segment's end row; false past the padded row space.
 TRG_DEV bool mx_block_rows(int base32, int rows, const int* seg_off, const int* seg_off128, int nseg, int seg_rows,
-                           int& r0, int& seg_hi) {
+                           int& r0, int& seg_hi, int& pstart, int& plen) {
   if (seg_off != nullptr) {
     if (base32 >= seg_off128[nseg]) return false;
     int lo = 0, hi = nseg;  // last e with seg_off128[e] <= base32
@@ -135,6 +135,8 @@ TRG_DEV bool mx_block_rows(int base32, int rows, const int* seg_off, const int* 
     }
     r0 = seg_off[lo] + (base32 - seg_off128[lo]);
     seg_hi = seg_off[lo + 1];
+    pstart = seg_off128[lo];
+    plen = seg_off128[lo + 1] - seg_off128[lo];
   } else {
     // fixed-size segments of seg_rows rows (rows a multiple of seg_rows, or a
     // single segment), each padded to a multiple of 32 rows
@@ -205,14 +207,14 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
   // search's latency was a large part of a band's time); they sit in the
   // tile's space, which is written only after the lookup.
   int* s_off = (int*)tile;
-  __shared__ int blk[NB][3];
+  __shared__ int blk[NB][5];  // first source row, segment end, valid, padded segment start and length
   if (seg_off != nullptr && nseg <= 1024) {
     for (int e = tid; e <= nseg; e += 256) s_off[e] = seg_off128[e];
     __syncthreads();
   }
   if (tid < NB) {
     const int b32 = base + tid * 32;
-    int r0 = 0, seg_hi = 0, ok = 0;
+    int r0 = 0, seg_hi = 0, ok = 0, pstart = 0, plen = 0;
     if (seg_off != nullptr && nseg <= 1024) {
       if (b32 < s_off[nseg]) {
         int lo = 0, hi = nseg;  // last e with seg_off128[e] <= b32
@@ -222,14 +224,18 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
         }
         r0 = seg_off[lo] + (b32 - s_off[lo]);
         seg_hi = seg_off[lo + 1];
+        pstart = s_off[lo];
+        plen = s_off[lo + 1] - s_off[lo];
         ok = 1;
       }
     } else {
-      ok = mx_block_rows(b32, rows, seg_off, seg_off128, nseg, seg_rows, r0, seg_hi) ? 1 : 0;
+      ok = mx_block_rows(b32, rows, seg_off, seg_off128, nseg, seg_rows, r0, seg_hi, pstart, plen) ? 1 : 0;
     }
     blk[tid][0] = r0;
     blk[tid][1] = seg_hi;
     blk[tid][2] = ok;
+    blk[tid][3] = pstart;
+    blk[tid][4] = plen;
   }
   __syncthreads();
 
@@ -361,13 +367,21 @@ __global__ __launch_bounds__(256) void mx_dual_kernel(const T* __restrict__ in, 
       long mrow = c;
       int pr = base + sb * 32;
       long nrow = cols;
+      uint8_t* qdst;
       if (emaj) {
         const int e = pr / seg32;
         mrow = (long)e * cols + c;
         pr -= e * seg32;
         nrow = (long)nsegf * cols;
+        qdst = q_col + mrow * ldc + pr;
+      } else if (seg_off != nullptr) {
+        // segment e's copy is one [cols, len_e] block at byte off128[e] * cols
+        const int ps = blk[sb][3], pl = blk[sb][4];
+        qdst = q_col + (long)ps * cols + (long)c * pl + (pr - ps);
+      } else {
+        qdst = q_col + (long)c * ldc + pr;
       }
-      uint4* dst = (uint4*)(q_col + mrow * ldc + pr);
+      uint4* dst = (uint4*)qdst;
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
       const int b = pr >> 5;  // block along the (segment's) padded rows

@@ -122,16 +122,16 @@ class MoELayerGPU:
         u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device=dev)
         self.rcap = rc = (R + 127 * E + 127) // 128 * 128  # columnwise row stride
         # routed x: rowwise (up) and columnwise per expert (wgrad up)
-        self.xq, self.xs, self.xqT, self.xsT = u8(R, d), u8(R, d // 32), u8(d, rc), u8(d, rc // 32)
+        self.xq, self.xs, self.xqT, self.xsT = u8(R, d), u8(R, d // 32), u8(d * rc), u8(d, rc // 32)
         # weights: rowwise (forward) and blocked along the other dim (dgrad)
         # columnwise (dgrad) copies expert-major: [E*d, h] for W1/W3 (blocked on h), [E*h, d] for W2
         self.w1q, self.w1s, self.w1tq, self.w1ts = u8(E, h, d), u8(E, h, d // 32), u8(E * d, h), u8(E * d, h // 32)
         self.w3q, self.w3s, self.w3tq, self.w3ts = u8(E, h, d), u8(E, h, d // 32), u8(E * d, h), u8(E * d, h // 32)
         self.w2q, self.w2s, self.w2tq, self.w2ts = u8(E, d, h), u8(E, d, h // 32), u8(E * h, d), u8(E * h, d // 32)
-        self.hq, self.hs, self.hqT, self.hsT = u8(R, h), u8(R, h // 32), u8(h, rc), u8(h, rc // 32)
-        self.dyq, self.dys, self.dyqT, self.dysT = u8(R, d), u8(R, d // 32), u8(d, rc), u8(d, rc // 32)
+        self.hq, self.hs, self.hqT, self.hsT = u8(R, h), u8(R, h // 32), u8(h * rc), u8(h, rc // 32)
+        self.dyq, self.dys, self.dyqT, self.dysT = u8(R, d), u8(R, d // 32), u8(d * rc), u8(d, rc // 32)
         self.dguq, self.dgus = u8(R, 2 * h), u8(R, 2 * h // 32)
-        self.dguqT, self.dgusT = u8(2 * h, rc), u8(2 * h, rc // 32)
+        self.dguqT, self.dgusT = u8(2 * h * rc), u8(2 * h, rc // 32)
 
     def quantize_weights(self, w1, w3, w2):
         """Both MX layouts of every expert weight (one pass per matrix)."""
