@@ -13,11 +13,15 @@
 // source:
 //   row layout      q_row [rows, cols]                             (blocks
 //                   along the columns: the forward and dgrad K);
-//   column layout   q_col [cols, ldc]                              (blocks of
-//                   32 consecutive rows inside each segment, zero-padded at
-//                   the segment's end; segment e starts at column off128[e]:
-//                   the weight-gradient K), or, for fixed segments (the
-//                   weights' dgrad copies), expert-major [nseg * cols, ldc].
+//   column layout   blocks of 32 consecutive rows inside each segment,
+//                   zero-padded at the segment's end (the weight-gradient K),
+//                   stored expert-major.  Gathered segments (padded rows
+//                   off128[e] .. off128[e+1], len_e of them): segment e is the
+//                   block [cols, len_e] at byte off128[e] * cols, so column c
+//                   of the segment is one row of len_e bytes.  Fixed segments
+//                   (the weights' dgrad copies): [nseg * cols, ldc], row
+//                   e * cols + c holding column c of segment e.  One segment:
+//                   the plain transpose [cols, ldc].
 // Scale bytes are stored K-chunk major: the scale of block b (of 32 values
 // along K) of row r of an n-row MX matrix is byte (b / 4 * n + r) * 4 + b % 4,
 // so the four scales of one 128-wide K chunk of a row form one dword and the
