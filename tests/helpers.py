@@ -40,6 +40,17 @@ def tail_routing(T, counts):
     return np.stack([lst[:T], lst[T:]], axis=1).astype(np.int32)
 
 
+def holes_routing(T, E, k, seed, empty=(3, 7, 15)):
+    """Forced uniform routing over the experts not in `empty`, which get no
+    rows (zero-length segments in the middle and, with E = 16, at the end of
+    the expert list)."""
+    from token_routing_grouped_amd import inputs
+
+    keep = np.array([e for e in range(E) if e not in empty])
+    idx = inputs.forced_routing("uniform", T, len(keep), k, seed)
+    return keep[idx].astype(np.int32)
+
+
 def to_np(t):
     return t.detach().float().cpu().numpy() if t.dtype.is_floating_point else t.detach().cpu().numpy()
 

@@ -17,7 +17,7 @@ import torch
 from oracle import moe_ref as ref
 from token_routing_grouped_amd import configs, inputs
 
-from helpers import assert_close, say, tail_routing, to_np
+from helpers import assert_close, holes_routing, say, tail_routing, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,9 @@ CASES = [
     # experts of >= 2048 rows on average: light tails (50 and 2 rows past whole
     # 256-row tiles) are scheduled apart from the full-cost tiles
     ("tail_split_E4", "small", dict(T=4096, E=4, k=2, d=256, h=128), "tails", {}),
+    # experts 3, 7 and 15 of 16 get no rows: empty segments inside and at the
+    # end of the expert list
+    ("holes_E16", "wide", dict(T=400, E=16, d=256, h=128), "holes", {}),
     # the same tails over longer K loops (16 steps in the up projection and
     # dgrad down, 8 in dgrad up, 4 in down): the light tails' three-stage
     # pipeline in its steady state
@@ -90,6 +93,8 @@ def test_layer_parity(case):
         assert not (differ & ~ties).any(), f"routing differs on {int((differ & ~ties).sum())} non-tied tokens"
     elif mode == "tails":
         forced = tail_routing(cfg.T, [2098, 1998, 2050, 2046])
+    elif mode == "holes":
+        forced = holes_routing(cfg.T, cfg.E, cfg.k, cfg.seed)
     else:
         forced = inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)
 

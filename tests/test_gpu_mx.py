@@ -18,7 +18,7 @@ from oracle import moe_ref as ref
 from oracle import mx_ref as mx
 from token_routing_grouped_amd import configs, inputs
 
-from helpers import mx_scale_bytes, mx_cols_side_by_side, mx_scales_to_rows, rel_l2, say, tail_routing, to_np
+from helpers import holes_routing, mx_scale_bytes, mx_cols_side_by_side, mx_scales_to_rows, rel_l2, say, tail_routing, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -167,6 +167,9 @@ LAYER_CASES = [
     ("one_expert", "small", dict(T=200, E=1, k=1, d=128, h=256), "router", {}),
     ("T1", "small", dict(T=1, d=128, h=128), "router", {}),
     ("tail_split_E4", "small", dict(T=4096, E=4, k=2, d=256, h=128), "tails", {}),
+    # experts 3, 7 and 15 of 16 get no rows: zero-length column segments inside
+    # and at the end of the expert-major copies
+    ("holes_E16", "wide", dict(T=400, E=16, d=256, h=128), "holes", {}),
     # d not a multiple of the 256-wide tiles (partial N / M tiles)
     ("d384_router", "small", dict(T=600, d=384, h=256), "router", {}),
     # memory-lean backward (G and U recomputed from the fp8 copies)
@@ -189,6 +192,8 @@ def test_mx_layer_parity(case):
         forced = ref.topk_experts(ref.router_logits(x, wr).astype(np.float32), cfg.k).astype(np.int32)
     elif mode == "tails":
         forced = tail_routing(cfg.T, [2098, 1998, 2050, 2046])
+    elif mode == "holes":
+        forced = holes_routing(cfg.T, cfg.E, cfg.k, cfg.seed)
     else:
         forced = inputs.forced_routing(mode, cfg.T, cfg.E, cfg.k, cfg.seed)
     layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, mx=True, **flags)
