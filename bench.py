@@ -293,8 +293,8 @@ def main():
     a = ap.parse_args()
 
     if a.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported by this build "
-              f"(the layer is measured on one GPU's share).", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
+              f"(the layer is measured on one GPU's share; there is no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
