@@ -95,21 +95,33 @@ TRG_DEV float wave_max(float v) {
   return v;
 }
 
-// Exclusive scan of one value per thread over a block of 1024 threads.
-TRG_DEV int block_excl_scan_1024(int v, int* tmp /* 1024 */, int* total) {
-  const int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int add = tid >= o ? tmp[tid - o] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+// Exclusive scan of one value per thread over a block of 1024 threads: a
+// shuffle scan inside each wave, then the 16 wave totals scanned by wave 0
+// (three barriers; integer sums, so the result does not depend on the order).
+TRG_DEV int block_excl_scan_1024(int v, int* tmp /* >= 32 */, int* total) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  int x = v;  // inclusive scan over the wave
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
   }
-  int incl = tmp[tid];
-  *total = tmp[1023];
+  if (lane == kWave - 1) tmp[wv] = x;
   __syncthreads();
-  return incl - v;
+  if (wv == 0) {
+    int w = lane < 16 ? tmp[lane] : 0;  // inclusive scan of the wave totals
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int y = __shfl_up(w, o, kWave);
+      if (lane >= o) w += y;
+    }
+    if (lane < 16) tmp[16 + lane] = w;
+  }
+  __syncthreads();
+  const int before = wv > 0 ? tmp[16 + wv - 1] : 0;
+  *total = tmp[31];
+  __syncthreads();  // tmp is reused by the next call
+  return before + x - v;
 }
 
 // The epilogues' activation functions with the hardware reciprocal (1 ulp;
