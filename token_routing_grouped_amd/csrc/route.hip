@@ -123,6 +123,84 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   }
 }
 
+// The same for E <= LPT <= 32: a wave takes 64 / LPT tokens, LPT lanes each
+// (lane sl of a token's group holds expert sl), so few experts do not leave
+// most of a wave idle.  The shuffles stay inside a token's group.  The results
+// are those of the one-token-per-wave kernel bit for bit: there the butterfly
+// steps wider than LPT only combine with lanes holding no expert (max with
+// -inf, sum with +0), and the remaining steps are these, in the same order;
+// the arg-max is exact in any order.  A group past T runs on token T - 1's
+// logits and writes nothing.
+template <int LPT>
+__global__ __launch_bounds__(256) void route_topk_packed_kernel(const float* __restrict__ logits, int T, int E,
+                                                                int k, const int* __restrict__ forced,
+                                                                float* __restrict__ probs, int* __restrict__ idx_out,
+                                                                float* __restrict__ w_out, int* __restrict__ err_flag) {
+  constexpr int TPW = 64 / LPT;  // tokens per wave
+  const int lane = threadIdx.x & 63, sl = lane & (LPT - 1);
+  const int t0 = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6) * TPW + lane / LPT;
+  const bool valid = t0 < T;
+  const int t = valid ? t0 : T - 1;
+  const bool has_e = sl < E;
+  float v = has_e ? logits[(long)t * E + sl] : -INFINITY;
+  if (v != v) v = -INFINITY;  // NaN never wins a slot
+  float m = v;
+#pragma unroll
+  for (int o = LPT / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, LPT));
+  const float ex = has_e ? expf(v - m) : 0.f;
+  float s = ex;
+#pragma unroll
+  for (int o = LPT / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, LPT);
+  const float p = ex / s;
+  if (valid && has_e) probs[(long)t * E + sl] = p;
+
+  if (forced != nullptr) {
+    int fe = sl < k ? forced[(long)t * k + sl] : 0;
+    int flags = 0;
+    if (sl < k && (fe < 0 || fe >= E)) {
+      flags |= 1;
+      fe = fe < 0 ? 0 : E - 1;
+    }
+    for (int j = 0; j < k; ++j) {
+      const int other = __shfl(fe, j, LPT);
+      if (sl < k && j < sl && other == fe) flags |= 2;
+    }
+    const float w = __shfl(p, fe, LPT);
+    if (valid && sl < k) {
+      idx_out[(long)t * k + sl] = fe;
+      w_out[(long)t * k + sl] = w;
+      if (flags && err_flag) atomicOr(err_flag, flags);
+    }
+    return;
+  }
+
+  bool chosen = false;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+    if (has_e && !chosen) {
+      bv = v;
+      be = sl;
+    }
+#pragma unroll
+    for (int o = LPT / 2; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, LPT);
+      const int oe = __shfl_xor(be, o, LPT);
+      if (better(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    // be is now uniform across the token's group
+    if (be == sl) chosen = true;
+    const float w = __shfl(p, be & (LPT - 1), LPT);
+    if (valid && sl == 0) {
+      idx_out[(long)t * k + j] = be;
+      w_out[(long)t * k + j] = w;
+    }
+  }
+}
+
 // Per-chunk expert histogram.  4 waves per block, one chunk per wave.
 __global__ __launch_bounds__(256) void route_count_kernel(const int* __restrict__ idx, int R, int E, int nchunks,
                                                           int* __restrict__ chunk_cnt) {
@@ -318,7 +396,13 @@ hipError_t launch_route(const float* logits, int T, int E, int k, const int* for
     return hipGetLastError();
   }
   dim3 g1((T + 3) / 4);
-  if (E <= 64)
+  if (E <= 8)
+    route_topk_packed_kernel<8><<<(T + 31) / 32, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
+  else if (E <= 16)
+    route_topk_packed_kernel<16><<<(T + 15) / 16, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
+  else if (E <= 32)
+    route_topk_packed_kernel<32><<<(T + 7) / 8, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
+  else if (E <= 64)
     route_topk_kernel<1><<<g1, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
   else if (E <= 128)
     route_topk_kernel<2><<<g1, 256, 0, s>>>(logits, T, E, k, forced, probs, idx, w, err_flag);
