@@ -49,6 +49,9 @@ CASES = [  # T, E, k, logit scale, tie grid
     (1, 8, 2, 1.0, 0), (256, 8, 2, 1.0, 0), (257, 8, 4, 1.0, 0), (1000, 8, 4, 0.9, 2), (513, 128, 4, 0.9, 0),
     (777, 128, 4, 0.9, 4), (300, 384, 8, 0.9, 0), (129, 384, 8, 0.9, 8), (64, 1024, 32, 1.0, 0), (50, 5, 5, 1.0, 1),
     (40, 1, 1, 1.0, 0), (2048, 64, 6, 3.0, 0), (96, 100, 7, 1.0, 2),
+    # few experts: 8, 16 and 32 lanes per token, several tokens per wave, T not
+    # a multiple of the tokens per workgroup
+    (65, 9, 2, 1.0, 0), (97, 12, 3, 1.0, 1), (333, 24, 5, 1.0, 2), (200, 32, 8, 0.9, 0),
 ]
 
 
@@ -74,7 +77,8 @@ def test_route_all_ties_closed_form():
     assert g["counts"].tolist() == [T] * k + [0] * (E - k)
 
 
-@pytest.mark.parametrize("mode,T,E,k", [("uniform", 4096, 384, 8), ("zipf", 3000, 128, 4), ("uniform", 999, 128, 4)])
+@pytest.mark.parametrize("mode,T,E,k", [("uniform", 4096, 384, 8), ("zipf", 3000, 128, 4), ("uniform", 999, 128, 4),
+                                        ("uniform", 501, 24, 4), ("zipf", 130, 12, 3)])
 def test_route_forced(mode, T, E, k):
     say(f"route forced {mode} T={T} E={E} k={k}")
     idx = inputs.forced_routing(mode, T, E, k, seed=11)
