@@ -372,6 +372,13 @@ hipError_t launch_router_logits(const void* x, bool bf16, const void* wr, int T,
 template <class T, int EB>
 static void bwd_valu(const float* dL, const void* x, const void* wr, int Tn, int d, int E, void* dx, void* dwr,
                      float* part, hipStream_t s, const void* dxp, const int* pos, int k, unsigned parts) {
+  // dx first: in a step whose weight gradients run on a second stream this
+  // pass (the larger one) fills the CUs those GEMMs free as they finish, and
+  // the dWr sum, which no later kernel of the step reads, comes last.  The
+  // two outputs are independent.
+  if (parts & kRouterDx)
+    router_dx_valu_kernel<T, EB><<<(Tn + kDxTokens - 1) / kDxTokens, 256, 0, s>>>(dL, (const T*)wr, Tn, d, E, (T*)dx,
+                                                                                  (const T*)dxp, pos, k);
   if (parts & kRouterDwr) {
     const int nch = (Tn + kDwrChunk - 1) / kDwrChunk;
     constexpr int CV = 64 / EB;
@@ -382,9 +389,6 @@ static void bwd_valu(const float* dL, const void* x, const void* wr, int Tn, int
     const long n = (long)E * d;
     chunk_sum_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, nch, n, (T*)dwr);
   }
-  if (parts & kRouterDx)
-    router_dx_valu_kernel<T, EB><<<(Tn + kDxTokens - 1) / kDxTokens, 256, 0, s>>>(dL, (const T*)wr, Tn, d, E, (T*)dx,
-                                                                                  (const T*)dxp, pos, k);
 }
 
 template <class T>
