@@ -54,7 +54,7 @@ CONFIGS = {
     "tiny": LayerConfig("tiny", T=256, d=128, E=8, k=2, h=256, dtype="f32", seed=0),
     "small": LayerConfig("small", T=8192, d=2048, E=8, k=4, h=1024, dtype="bf16", seed=1, overlap=True),
     "wide": LayerConfig("wide", T=16384, d=2048, E=128, k=4, h=1024, dtype="bf16", seed=2,
-                        modes=("router", "uniform", "zipf")),
+                        modes=("router", "uniform", "zipf"), overlap=True),
     "mxfp8": LayerConfig("mxfp8", T=16384, d=2048, E=128, k=4, h=1024, dtype="bf16", seed=2,
                          modes=("router", "uniform"), mx=True, overlap=True),
     "mxfp8_small": LayerConfig("mxfp8_small", T=8192, d=2048, E=8, k=4, h=1024, dtype="bf16",

@@ -426,12 +426,15 @@ hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dg
   else if (E <= 512) router_dl_kernel<8><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
   else router_dl_kernel<16><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
   if (mf) {
-    if (parts & kRouterDwr) {
-      hipError_t err = launch_router_dwr_mfma(dLb, (const uint16_t*)x, (uint16_t*)dwr, part, T, d, E, s);
+    // dx first, as on the vector path below: with the weight gradients on a
+    // second stream the fused dx GEMM fills the CUs they free
+    if (parts & kRouterDx) {
+      hipError_t err =
+          launch_router_dx_mfma(dLb, (const uint16_t*)wr, (uint16_t*)dx, (const uint16_t*)dxp, pos, k, T, d, E, s);
       if (err != hipSuccess) return err;
     }
-    if (parts & kRouterDx)
-      return launch_router_dx_mfma(dLb, (const uint16_t*)wr, (uint16_t*)dx, (const uint16_t*)dxp, pos, k, T, d, E, s);
+    if (parts & kRouterDwr)
+      return launch_router_dwr_mfma(dLb, (const uint16_t*)x, (uint16_t*)dwr, part, T, d, E, s);
     return hipGetLastError();
   }
   if (bf16) bwd_valu_any<uint16_t>(dL, x, wr, T, d, E, dx, dwr, part, s, dxp, pos, k, parts);
