@@ -448,6 +448,23 @@ typedef struct {
 moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* args, void* stream);
 moe_status_t moe_grouped_gemm_bwd_mx(const moe_mx_bwd_args* args, void* stream);
 /*
+ * moe_grouped_gemm_fwd_mx_parts: moe_grouped_gemm_fwd_mx in two halves, so
+ * that a caller making the weights' MX copies on another stream can start the
+ * up projection once W1's and W3's copies exist and wait for W2's only before
+ * the down projection.  MOE_FWD_UP: the up projection with its SwiGLU
+ * epilogue (g, u, hbuf) and H's MX copies (hq/hs, hqT/hsT); reads xq/xs,
+ * w1q/w1s, w3q/w3s.  MOE_FWD_DOWN: the down projection (yp) from H's rowwise
+ * copy and w2q/w2s; needs the up part done.  Both bits: moe_grouped_gemm_fwd_mx.
+ * Same arguments and checks as moe_grouped_gemm_fwd_mx; parts must be a
+ * non-empty subset of MOE_FWD_ALL (else MOE_ERR_INVALID_ARG).
+ */
+enum {
+  MOE_FWD_UP = 1,
+  MOE_FWD_DOWN = 2,
+  MOE_FWD_ALL = 3
+};
+moe_status_t moe_grouped_gemm_fwd_mx_parts(const moe_mx_fwd_args* args, unsigned parts, void* stream);
+/*
  * moe_grouped_gemm_bwd_mx_parts: moe_grouped_gemm_bwd_mx restricted to a
  * subset (MOE_BWD_* mask) of its four GEMMs, for two streams as with
  * moe_grouped_gemm_bwd_parts.  MOE_BWD_DGRAD_DOWN also makes dYp's MX copies

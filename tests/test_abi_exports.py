@@ -178,3 +178,11 @@ def test_host_validation_of_the_next_rows():
     # a valid mask gets past the mask check (and then stops at the null buffers)
     assert lib.moe_grouped_gemm_bwd_mx_parts(ctypes.byref(a), _abi.BWD_MX_QUANT_DY, None) != 0
     assert b"is null" in lib.moe_last_error_string()
+    # MXFP8 forward halves: empty and out-of-range masks refused, valid ones reach the buffer checks
+    f = _abi.MxFwdArgs(E=2, R=8, d=128, h=128, rcap=512)
+    for bad in (0, 4, _abi.FWD_ALL | 8):
+        assert lib.moe_grouped_gemm_fwd_mx_parts(ctypes.byref(f), bad, None) == 1
+        assert b"parts" in lib.moe_last_error_string()
+    for ok in (_abi.FWD_UP, _abi.FWD_DOWN, _abi.FWD_ALL):
+        assert lib.moe_grouped_gemm_fwd_mx_parts(ctypes.byref(f), ok, None) != 0
+        assert b"is null" in lib.moe_last_error_string()

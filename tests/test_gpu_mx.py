@@ -226,6 +226,30 @@ def test_mx_layer_parity(case):
     assert not bad, bad
 
 
+@pytest.mark.parametrize("base,over", [("small", dict(T=384, d=512, h=256)), ("wide", dict(T=512, d=256, h=128))])
+def test_mx_forward_halves_equal_the_single_call(base, over):
+    """Weights quantised on a second stream with the forward in two halves
+    (moe_grouped_gemm_fwd_mx_parts: up, then down after W2's copies) give the
+    same step, bit for bit, as the weights quantised in line and one
+    moe_grouped_gemm_fwd_mx call."""
+    from token_routing_grouped_amd.layer import MoELayerGPU
+
+    cfg = configs.get(base).with_(**over)
+    say(f"mx forward halves {base}: T={cfg.T} d={cfg.d} E={cfg.E} h={cfg.h}")
+    inp = inputs.layer_inputs(cfg)
+    t = {n: torch.from_numpy(v).to(DEV).to(torch.bfloat16) for n, v in inp.items()}
+    outs = []
+    for wq in (False, True):
+        layer = MoELayerGPU(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, torch.bfloat16, DEV, mx=True, wq_overlap=wq)
+        assert (layer.wq_stream is not None) == wq
+        for _ in range(2):
+            layer.step(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])
+        torch.cuda.synchronize()
+        outs.append([a.clone() for a in (layer.y, layer.yp, layer.hb, layer.dx, layer.dw1, layer.dw3, layer.dw2)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_mx_layer_deterministic():
     from token_routing_grouped_amd.layer import MoELayerGPU
 

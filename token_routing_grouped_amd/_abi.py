@@ -61,6 +61,7 @@ _SIGS = {
     "moe_grouped_gemm_fwd_mx": ([_P, _P], _I),
     "moe_grouped_gemm_bwd_mx": ([_P, _P], _I),
     "moe_grouped_gemm_bwd_mx_parts": ([_P, ctypes.c_uint, _P], _I),
+    "moe_grouped_gemm_fwd_mx_parts": ([_P, ctypes.c_uint, _P], _I),
 }
 
 
@@ -421,6 +422,15 @@ def moe_grouped_gemm_fwd_mx(**kw):
     """Keyword arguments are the fields of moe_mx_fwd_args (tensors or ints)."""
     a = _fill(MxFwdArgs(), **kw)
     _check(lib().moe_grouped_gemm_fwd_mx(ctypes.byref(a), _stream()), "moe_grouped_gemm_fwd_mx")
+
+
+FWD_UP, FWD_DOWN, FWD_ALL = 1, 2, 3
+
+
+def moe_grouped_gemm_fwd_mx_parts(parts, **kw):
+    """moe_grouped_gemm_fwd_mx's up half (MOE_FWD_UP) and/or down half (MOE_FWD_DOWN)."""
+    a = _fill(MxFwdArgs(), **kw)
+    _check(lib().moe_grouped_gemm_fwd_mx_parts(ctypes.byref(a), parts, _stream()), "moe_grouped_gemm_fwd_mx_parts")
 
 
 def moe_grouped_gemm_recompute_gu_mx(**kw):

@@ -586,9 +586,10 @@ static moe_status_t check_mx_dims(const char* fn, int E, int R, int d, int h, in
   return MOE_OK;
 }
 
-moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* a, void* stream) {
-  const char* fn = "moe_grouped_gemm_fwd_mx";
+static moe_status_t ggemm_fwd_mx_impl(const char* fn, const moe_mx_fwd_args* a, unsigned parts, void* stream) {
   if (!a) return fail(MOE_ERR_INVALID_ARG, "%s: args is null", fn);
+  if (parts == 0 || (parts & ~(unsigned)MOE_FWD_ALL) != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: parts must be a non-empty subset of MOE_FWD_ALL", fn);
   TRY(check_mx_dims(fn, a->E, a->R, a->d, a->h, a->rcap, a->ws, a->ws_bytes));
   TRY(check_ptrs(fn, {{"offsets", a->offsets}, {"off128", a->off128}, {"w1q", a->w1q}, {"w1s", a->w1s},
                       {"w3q", a->w3q}, {"w3s", a->w3s}, {"w2q", a->w2q}, {"w2s", a->w2s}}));
@@ -597,7 +598,15 @@ moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* a, void* stream) {
                       {"hqT", a->hqT}, {"hsT", a->hsT}, {"yp", a->yp}}));
   TRY(check_optional_aligned(fn, {{"g", a->g}, {"u", a->u}}));
   TRY(check_device());
-  return hip_status(fn, trg::launch_ggemm_fwd_mx(*a, (hipStream_t)stream));
+  return hip_status(fn, trg::launch_ggemm_fwd_mx(*a, parts, (hipStream_t)stream));
+}
+
+moe_status_t moe_grouped_gemm_fwd_mx(const moe_mx_fwd_args* a, void* stream) {
+  return ggemm_fwd_mx_impl("moe_grouped_gemm_fwd_mx", a, MOE_FWD_ALL, stream);
+}
+
+moe_status_t moe_grouped_gemm_fwd_mx_parts(const moe_mx_fwd_args* a, unsigned parts, void* stream) {
+  return ggemm_fwd_mx_impl("moe_grouped_gemm_fwd_mx_parts", a, parts, stream);
 }
 
 moe_status_t moe_grouped_gemm_recompute_gu_mx(const moe_mx_fwd_args* a, void* stream) {

@@ -363,18 +363,18 @@ hipError_t launch_ggemm_recompute_gu_mx(const MxFwd& p, hipStream_t s) {
 }
 
 template <int BM>
-static hipError_t mx_fwd_bm(const MxFwd& p, hipStream_t s) {
+static hipError_t mx_fwd_bm(const MxFwd& p, unsigned parts, hipStream_t s) {
   const int E = p.E, R = p.R, d = p.d, h = p.h;
   const int mt_max = cdiv(R, BM) + E;
-  mx_up_bm<BM>("ggemm_mx_up_swiglu", p, p.g, p.u, p.hbuf, s);
-  // H -> rowwise MX (down GEMM) and columnwise per expert (wgrad down)
-  {
+  if (parts & MOE_FWD_UP) {
+    mx_up_bm<BM>("ggemm_mx_up_swiglu", p, p.g, p.u, p.hbuf, s);
+    // H -> rowwise MX (down GEMM) and columnwise per expert (wgrad down)
     ProfScope ps("mx_quantize_h", s);
     const hipError_t err = launch_mx_quantize(p.hbuf, true, h, R, h, nullptr, 1, p.offsets, p.off128, E, 0,
                                               (R + 127 * E + 31) / 32, p.hq, p.hs, p.hqT, p.hsT, p.rcap, s);
     if (err != hipSuccess) return err;
   }
-  {  // down projection: hq [R,h] x W2q [E,d,h]
+  if (parts & MOE_FWD_DOWN) {  // down projection: hq [R,h] x W2q [E,d,h]
     Args a{};
     a.A = (const uint16_t*)p.hq; a.lda = h;
     a.B = (const uint16_t*)p.w2q; a.ldb = h; a.b_es = (long)d * h;
@@ -394,9 +394,9 @@ static hipError_t mx_fwd_bm(const MxFwd& p, hipStream_t s) {
 // fewer than 192 rows): an fp8 K step does half a bf16 step's MFMA time per
 // byte loaded, so the per-step costs need the larger tile.  The weight
 // gradients (K-tail masking, more registers) use 128 x 256.
-hipError_t launch_ggemm_fwd_mx(const MxFwd& p, hipStream_t s) {
-  if (small_rows(p.E, p.R)) return mx_fwd_bm<128>(p, s);
-  return mx_fwd_bm<256>(p, s);
+hipError_t launch_ggemm_fwd_mx(const MxFwd& p, unsigned parts, hipStream_t s) {
+  if (small_rows(p.E, p.R)) return mx_fwd_bm<128>(p, parts, s);
+  return mx_fwd_bm<256>(p, parts, s);
 }
 
 template <int BM>

@@ -82,7 +82,7 @@ typedef moe_mx_bwd_args MxBwd;
 hipError_t launch_ggemm_recompute_gu(const void* xp, const void* w1, const void* w3, const int* offsets, int E, int R,
                                      int d, int h, void* g, void* u, void* ws, hipStream_t s);
 hipError_t launch_ggemm_recompute_gu_mx(const MxFwd& p, hipStream_t s);
-hipError_t launch_ggemm_fwd_mx(const MxFwd& p, hipStream_t s);
+hipError_t launch_ggemm_fwd_mx(const MxFwd& p, unsigned parts, hipStream_t s);  // parts: MOE_FWD_* mask
 hipError_t launch_ggemm_bwd_mx(const MxBwd& p, unsigned parts, hipStream_t s);
 
 }  // namespace trg

@@ -133,15 +133,24 @@ class MoELayerGPU:
         self.dguq, self.dgus = u8(R, 2 * h), u8(R, 2 * h // 32)
         self.dguqT, self.dgusT = u8(2 * h * rc), u8(2 * h, rc // 32)
 
-    def quantize_weights(self, w1, w3, w2):
-        """Both MX layouts of every expert weight (one pass per matrix)."""
+    def quantize_w13(self, w1, w3):
+        """Both MX layouts of W1 and W3 (one pass per matrix)."""
         E, d, h = self.E, self.d, self.h
         _abi.mx_quantize(w1.view(E * h, d), E * h, self.w1q.view(E * h, d), self.w1s.view(E * h, d // 32), self.w1tq,
                          self.w1ts, seg_rows=h)
         _abi.mx_quantize(w3.view(E * h, d), E * h, self.w3q.view(E * h, d), self.w3s.view(E * h, d // 32), self.w3tq,
                          self.w3ts, seg_rows=h)
+
+    def quantize_w2(self, w2):
+        """Both MX layouts of W2."""
+        E, d, h = self.E, self.d, self.h
         _abi.mx_quantize(w2.view(E * d, h), E * d, self.w2q.view(E * d, h), self.w2s.view(E * d, h // 32), self.w2tq,
                          self.w2ts, seg_rows=d)
+
+    def quantize_weights(self, w1, w3, w2):
+        """Both MX layouts of every expert weight."""
+        self.quantize_w13(w1, w3)
+        self.quantize_w2(w2)
 
     # ------------------------------------------------------------------
     def forward(self, x, wr, w1, w3, w2, forced_idx=None):
@@ -154,9 +163,12 @@ class MoELayerGPU:
             ev.record(main)
             with torch.cuda.stream(self.wq_stream):
                 self.wq_stream.wait_event(ev)
-                self.quantize_weights(w1, w3, w2)
-                self._ev_wq = torch.cuda.Event()
-                self._ev_wq.record(self.wq_stream)
+                self.quantize_w13(w1, w3)  # the up projection waits for these
+                self._ev_w13 = torch.cuda.Event()
+                self._ev_w13.record(self.wq_stream)
+                self.quantize_w2(w2)  # the down projection waits for this one
+                self._ev_w2 = torch.cuda.Event()
+                self._ev_w2.record(self.wq_stream)
         _abi.moe_router_logits(x, wr, self.logits)
         _abi.moe_route(self.logits, self.k, self.probs, self.topk_idx, self.topk_w, self.counts, self.offsets,
                        self.pos, self.src, self.ws_route, off128=self.off128, forced_idx=forced_idx,
@@ -167,16 +179,22 @@ class MoELayerGPU:
             # routed rows of x straight into their experts' MX buffers
             _abi.mx_quantize(x, self.R, self.xq, self.xs, self.xqT, self.xsT, gather_src=self.src, gather_k=self.k,
                              seg_off=self.offsets, seg_off128=self.off128)
+            fields = dict(E=self.E, R=self.R, d=self.d, h=self.h, rcap=self.rcap, offsets=self.offsets,
+                          off128=self.off128, xq=self.xq, xs=self.xs, w1q=self.w1q, w1s=self.w1s, w3q=self.w3q,
+                          w3s=self.w3s, w2q=self.w2q, w2s=self.w2s, g=None if self.lean else self.g,
+                          u=None if self.lean else self.u, hbuf=self.hb, hq=self.hq, hs=self.hs, hqT=self.hqT,
+                          hsT=self.hsT, yp=self.yp, ws=self.ws_gemm, ws_bytes=self.ws_gemm.numel())
             if self.wq_stream is not None:
-                torch.cuda.current_stream().wait_event(self._ev_wq)
+                # the up projection starts once W1's and W3's copies exist;
+                # W2's are made meanwhile and waited for before the down one
+                main = torch.cuda.current_stream()
+                main.wait_event(self._ev_w13)
+                _abi.moe_grouped_gemm_fwd_mx_parts(_abi.FWD_UP, **fields)
+                main.wait_event(self._ev_w2)
+                _abi.moe_grouped_gemm_fwd_mx_parts(_abi.FWD_DOWN, **fields)
             else:
                 self.quantize_weights(w1, w3, w2)
-            _abi.moe_grouped_gemm_fwd_mx(E=self.E, R=self.R, d=self.d, h=self.h, rcap=self.rcap,
-                                         offsets=self.offsets, off128=self.off128, xq=self.xq, xs=self.xs, w1q=self.w1q,
-                                         w1s=self.w1s, w3q=self.w3q, w3s=self.w3s, w2q=self.w2q, w2s=self.w2s,
-                                         g=None if self.lean else self.g, u=None if self.lean else self.u,
-                                         hbuf=self.hb, hq=self.hq, hs=self.hs, hqT=self.hqT,
-                                         hsT=self.hsT, yp=self.yp, ws=self.ws_gemm, ws_bytes=self.ws_gemm.numel())
+                _abi.moe_grouped_gemm_fwd_mx(**fields)
         else:
             _abi.moe_permute(x, self.pos, self.xp)
             _abi.moe_grouped_gemm_fwd(self.xp, w1, w3, w2, self.offsets, None if self.lean else self.g,
