@@ -349,7 +349,14 @@ def main():
     # with the dgrad chain, so no backward GEMM's event duration is its own;
     # the dominant kernel is then chosen among the forward GEMMs, which run
     # alone (and the grouped-GEMM sum below counts the overlapped ones in full).
-    solo = [n for n in timed_gemms if not (layer.overlap and ("wgrad" in n or "dgrad" in n))]
+    # With the MXFP8 weights quantised on a second stream, W2's copies are made
+    # while the up projection runs, so there only the down projection is alone.
+    def alone(n):
+        if layer.overlap and ("wgrad" in n or "dgrad" in n):
+            return False
+        return not (layer.mx and layer.wq_stream is not None and "up_swiglu" in n)
+
+    solo = [n for n in timed_gemms if alone(n)]
     dom = max(solo, key=lambda n: kern[n]["avg_us"])
     log("bench: per-kernel pass done")
 
