@@ -426,7 +426,7 @@ hipError_t launch_router_bwd(const float* probs, const int* idx, const float* dg
   else if (E <= 512) router_dl_kernel<8><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
   else router_dl_kernel<16><<<gw, 256, 0, s>>>(probs, idx, dgate, aux_g, T, E, k, dL, dlb_out);
   if (mf) {
-    // dx first, as on the vector path below: with the weight gradients on a
+    // dx first, as on the vector path (bwd_valu): with the weight gradients on a
     // second stream the fused dx GEMM fills the CUs they free
     if (parts & kRouterDx) {
       hipError_t err =
